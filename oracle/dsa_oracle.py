@@ -1,0 +1,250 @@
+"""CPU oracle for the DSA hot path: Lightning Indexer + Top-K + Sparse Flash Attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+module; only the test-suite, the package smoke check and the benchmark's
+``cpu_baseline`` leg do.  It is plain NumPy in float64, deliberately slow and
+written so that each step can be read against the pages:
+
+  Pages (each cited by its title and section):
+    [P1] "Day0 Inference Optimization on Ascend CANN: A Deep Dive into Hybrid
+         Architecture Acceleration"
+    [P2] "Adapting and Optimizing Inference for a New Model Architecture on Ascend"
+    [P3] "Day0 Inference Optimization for New LLM Architectures on Heterogeneous
+         Computing Platforms"
+    [P4] "Inference Acceleration for Next-Gen Attention Architectures: From
+         Operator Reuse to Parallel Orchestration"
+
+What is computed (the method as the pages state it):
+  * the indexer scores every visible historical position with per-head relevance
+    scores q_h . k_s, weights the heads and keeps the Top-K positions
+    ([P1] sec. 1 "DSA mechanism" and sec. 2 "Deep Fusion of LI and SFA";
+    [P2] sec. 2.2 and 3.1; [P4] sec. 1 and 3.1);
+  * causal index computation: a query at position t only sees positions <= t
+    ([P1] sec. 4 "Zigzag Layout"; [P2] sec. 5.2);
+  * Sparse Flash Attention reads the latent KV rows at the selected positions and
+    runs softmax attention over only those rows ([P2] sec. 3.1; [P4] sec. 3.2),
+    on top of multi-head latent attention ([P1] sec. 1; [P3] sec. 1);
+  * paged caches are read through a block table ([P4] sec. 3.2 "efficient paged
+    addressing"; [P1] sec. 2 "directly reads paged KV cache");
+  * MXFP8: every 32 elements share one scale ([P1] sec. 3; [P2] sec. 4.2).
+
+Readings where the pages are silent (each is listed in the design notes):
+  * no activation on per-head scores; the weighted combination is a sum over
+    heads giving one score per (query, position);
+  * Top-K keeps n = min(k, t + 1) positions, larger score first, ties broken
+    toward the smaller position; the boundary is inclusive (s <= t);
+  * query i of a sequence with T_b new tokens and L_b cached keys sits at
+    t = L_b - T_b + i;
+  * SFA uses the absorbed (MQA) MLA form: one latent row per position shared by
+    every head; logits over all qk dims, V = the first d_v dims of the row.
+
+Every function here is pinned by tests that do not retype its formula
+(brute-force loops, library routines, closed forms and invariants).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ------------------------------------------------------------- O1: decoding ---
+
+def decode_bf16_bits(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16 / int16) -> float64, exactly: a bf16 value is
+    the upper half of the float32 with the same bits."""
+    b = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_table() -> np.ndarray:
+    """Value of every OCP FP8 E4M3 ('fn') byte: 1 sign bit, 4 exponent bits with
+    bias 7, 3 mantissa bits; exponent field 0 is subnormal (m * 2^-9); the
+    pattern S.1111.111 is NaN; there are no infinities (max 448)."""
+    t = np.empty(256, np.float64)
+    for byte in range(256):
+        sign = -1.0 if byte & 0x80 else 1.0
+        e = (byte >> 3) & 0xF
+        m = byte & 0x7
+        if e == 0xF and m == 0x7:
+            t[byte] = np.nan
+        elif e == 0:
+            t[byte] = sign * m * 2.0 ** -9
+        else:
+            t[byte] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
+_E4M3 = e4m3fn_table()
+
+
+def decode_e4m3(bits) -> np.ndarray:
+    return _E4M3[np.asarray(bits, dtype=np.uint8)]
+
+
+def decode_e8m0(bits) -> np.ndarray:
+    """OCP E8M0 scale byte -> 2^(E - 127); 0xFF is NaN."""
+    e = np.asarray(bits, dtype=np.uint8).astype(np.float64)
+    v = np.ldexp(1.0, (e - 127).astype(np.int64))
+    return np.where(e == 255, np.nan, v)
+
+
+def decode_values(raw, dtype: str, scale=None, group: int = 32) -> np.ndarray:
+    """Storage -> float64 for one tensor slice whose last axis is the element axis.
+
+    dtype 'f32'  : raw float32
+    dtype 'bf16' : raw bf16 bit patterns
+    dtype 'fp8'  : raw e4m3 bytes; ``scale`` has the shape of raw[..., 0]
+                   (one fp32 scale per row: per token for keys, per token and
+                   head for queries)
+    dtype 'mxfp8': raw e4m3 bytes; ``scale`` holds one e8m0 byte per group of
+                   ``group`` consecutive elements ([P1] sec. 3, [P2] sec. 4.2)
+    """
+    if dtype == "f32":
+        return np.asarray(raw, np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return decode_bf16_bits(raw)
+    if dtype == "fp8":
+        v = decode_e4m3(raw)
+        return v * np.asarray(scale, np.float64)[..., None]
+    if dtype == "mxfp8":
+        v = decode_e4m3(raw)
+        sc = decode_e8m0(scale)
+        shp = v.shape
+        v = v.reshape(*shp[:-1], shp[-1] // group, group) * sc[..., None]
+        return v.reshape(shp)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------- O2: locate/read ---
+
+def query_position(seq_len: int, q_len: int, i: int) -> int:
+    """Position of query i among the T_b newest tokens of a context of L_b keys."""
+    return int(seq_len) - int(q_len) + int(i)
+
+
+def paged_rows(pool_raw, block_table_row, page_size: int, positions) -> np.ndarray:
+    """Rows of a paged pool [num_pages][P][...] for logical ``positions``: logical
+    page s // P is looked up in the block table, the row is s % P of that page."""
+    positions = np.asarray(positions, np.int64)
+    pages = np.asarray(block_table_row, np.int64)[positions // page_size]
+    return np.asarray(pool_raw)[pages, positions % page_size]
+
+
+# ------------------------------------------------- O3: indexer (a3 and a4) ---
+
+def indexer_scores(q: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """One score per key: for every head h the relevance q_h . k_s, then the
+    head-weighted sum over heads.  q [H][D], w [H], keys [n][D] -> I [n]."""
+    per_head = keys @ q.T          # [n][H]: per-head relevance scores
+    return per_head @ w            # weighted sum over the heads
+
+
+# ---------------------------------------------------------- O4: Top-K (a6) ---
+
+def topk_select(scores: np.ndarray, k: int) -> np.ndarray:
+    """Positions of the n = min(k, len(scores)) largest scores; a tie goes to the
+    smaller position.  Returned in ascending position order."""
+    n = min(int(k), len(scores))
+    pos = np.arange(len(scores))
+    order = np.lexsort((pos, -np.asarray(scores, np.float64)))  # primary: -score
+    return np.sort(order[:n])
+
+
+# ------------------------------------------------------ O5: SFA (a8 - a11) ---
+
+def sparse_attention(q: np.ndarray, rows: np.ndarray, d_v: int, scale: float):
+    """Softmax attention of every head over the gathered latent rows only.
+    q [H][Dqk], rows [n][Dqk] -> (O [H][d_v], lse [H]); V = rows[:, :d_v]."""
+    z = scale * (q @ rows.T)                      # [H][n] logits
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=1, keepdims=True)
+    o = (e @ rows[:, :d_v]) / l
+    return o, (m + np.log(l))[:, 0]
+
+
+# ------------------------------------------------------ zigzag (a13) ---
+
+def zigzag_units(n_blocks: int):
+    """Pair query blocks from the two ends of the sequence: unit u holds blocks
+    u and n_blocks-1-u (an odd count leaves the middle block alone), so that a
+    short-history block shares a unit with a long-history one ([P1] sec. 4;
+    [P2] sec. 5.2; [P3] sec. 4.2; [P4] sec. 5.2)."""
+    units = [[u, n_blocks - 1 - u] for u in range(n_blocks // 2)]
+    if n_blocks % 2:
+        units.append([n_blocks // 2])
+    return units
+
+
+# ------------------------------------------------ per-query driver (O6) ---
+
+class QueryResult(dict):
+    """idx (ascending), scores I[0..t], kth (the n-th largest score), out, lse."""
+
+
+def indexer_query(case, b: int, i: int):
+    """Indexer + Top-K for query i of sequence b of a case (see the input module
+    for layouts).  Reads every key through the block table."""
+    P = case.page_size
+    L, T = int(case.seq_lens_host[b]), int(case.q_lens_host[b])
+    t = query_position(L, T, i)
+    tok = case.token(b, i)
+    bt = _np(case.block_table[b])
+    pos = np.arange(t + 1)
+    q = decode_values(_np(case.q_i[tok]), case.idx_dtype,
+                      None if case.q_i_scale is None else _np(case.q_i_scale[tok]))
+    k_raw = paged_rows(_np(case.k_pool), bt, P, pos)
+    k_sc = None if case.k_scale is None else paged_rows(_np(case.k_scale), bt, P, pos)
+    keys = decode_values(k_raw, case.idx_dtype, k_sc)
+    w = _np(case.w[tok]).astype(np.float64)
+    scores = indexer_scores(q, w, keys)
+    idx = topk_select(scores, case.topk)
+    kth = np.sort(scores)[::-1][len(idx) - 1]
+    return t, scores, idx, kth
+
+
+def sfa_query(case, b: int, i: int, idx) -> tuple:
+    """SFA for query i of sequence b over logical positions ``idx``."""
+    tok = case.token(b, i)
+    bt = _np(case.block_table[b])
+    rows = decode_values(paged_rows(_np(case.kv_pool), bt, case.page_size, np.asarray(idx)),
+                         case.sfa_dtype)
+    q = decode_values(_np(case.q_s[tok]), case.sfa_dtype)
+    return sparse_attention(q, rows, case.d_v, case.softmax_scale)
+
+
+def run_query(case, b: int, i: int) -> QueryResult:
+    t, scores, idx, kth = indexer_query(case, b, i)
+    out, lse = sfa_query(case, b, i, idx)
+    return QueryResult(t=t, scores=scores, idx=idx, kth=kth, out=out, lse=lse)
+
+
+# Host copies of large device/CPU tensors, kept (with a reference to the tensor,
+# so that its storage cannot be reused while cached) for repeated per-query calls.
+_HOST_CACHE: dict = {}
+_HOST_CACHE_MAX = 6
+
+
+def _np(x) -> np.ndarray:
+    """Accept numpy arrays or torch tensors (CPU or device); bf16 tensors come
+    back as their uint16 bit patterns, fp8 bytes as uint8."""
+    if isinstance(x, np.ndarray):
+        return x
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        return np.asarray(x)
+    if not isinstance(x, torch.Tensor):
+        return np.asarray(x)
+    big = x.numel() > (1 << 20)
+    if big and id(x) in _HOST_CACHE and _HOST_CACHE[id(x)][0] is x:
+        return _HOST_CACHE[id(x)][1]
+    t = x.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    a = t.cpu().numpy()
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    if big:
+        if len(_HOST_CACHE) >= _HOST_CACHE_MAX:
+            _HOST_CACHE.pop(next(iter(_HOST_CACHE)))
+        _HOST_CACHE[id(x)] = (x, a)
+    return a

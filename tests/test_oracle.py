@@ -1,0 +1,264 @@
+"""The oracle against its pins (CPU only).
+
+Each oracle function is checked against something other than itself: brute
+force on tiny inputs, library routines (torch's FP8 / E8M0 / bf16 casts,
+scaled_dot_product_attention), closed forms, invariants and the one worked
+example the pages give (the two-device zigzag split).  The mutation tests at the
+end plant plausible mistakes in copies of the oracle's functions and check that
+the pins catch them."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+from sparse_attention_04_amd.inputs import make_case, quant_fp8_rows, quant_mx_rows
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------- decoding ---
+
+def test_e4m3_table_matches_library_and_spec():
+    pins.pin_e4m3_table(oracle.e4m3fn_table())
+
+
+def test_e8m0_matches_library():
+    pins.pin_e8m0(oracle.decode_e8m0)
+
+
+def test_bf16_decode_matches_library():
+    pins.pin_bf16(oracle.decode_bf16_bits)
+
+
+def test_fp8_per_row_scale_factors_out():
+    """sum_d (a_d s_a)(b_d s_b) = s_a s_b sum_d a_d b_d: the oracle's decoded
+    FP8 rows score the same as unscaled rows times the two scales."""
+    r = np.random.default_rng(5)
+    qb = r.integers(0, 256, (4, 32)).astype(np.uint8); qb[(qb & 0x7F) == 0x7F] = 0x38
+    kb = r.integers(0, 256, (6, 32)).astype(np.uint8); kb[(kb & 0x7F) == 0x7F] = 0x38
+    sq = r.uniform(0.1, 2.0, 4); sk = r.uniform(0.1, 2.0, 6)
+    w = r.standard_normal(4)
+    q = oracle.decode_values(qb, "fp8", sq)
+    k = oracle.decode_values(kb, "fp8", sk)
+    got = oracle.indexer_scores(q, w, k)
+    raw = oracle.indexer_scores(oracle.decode_e4m3(qb), w * sq, oracle.decode_e4m3(kb)) * sk
+    assert np.allclose(got, raw, rtol=1e-13)
+
+
+def test_mx_groups_scale_independently():
+    """Each group of 32 elements carries its own power-of-two scale."""
+    bits = np.full((1, 64), 0x38, np.uint8)            # every element 1.0
+    sc = np.array([[127 + 3, 127 - 2]], np.uint8)       # 2^3 and 2^-2
+    v = oracle.decode_values(bits, "mxfp8", sc)
+    assert np.all(v[0, :32] == 8.0) and np.all(v[0, 32:] == 0.25)
+
+
+def test_input_quantisers_within_e4m3_error():
+    """The input module's encoders (not the oracle) round within half an e4m3
+    ulp of the scaled value; the oracle decodes them back."""
+    r = np.random.default_rng(9)
+    x = torch.from_numpy(r.standard_normal((50, 128)).astype(np.float32))
+    x[3, 5] = 20.0
+    bits, sc = quant_fp8_rows(x)
+    back = oracle.decode_values(bits.numpy(), "fp8", sc.numpy())
+    rel = np.abs(back - x.numpy()) / np.maximum(np.abs(x.numpy()), sc.numpy()[:, None] * 2 ** -6)
+    assert rel.max() <= 2 ** -4 + 1e-9
+    bits, e = quant_mx_rows(x)
+    back = oracle.decode_values(bits.numpy(), "mxfp8", e.numpy())
+    scale = np.repeat(2.0 ** (e.numpy().astype(np.int64) - 127), 32, axis=1)
+    err = np.abs(back - x.numpy())
+    inside = np.abs(x.numpy()) <= 448.0 * scale
+    assert np.all(err[inside] <= np.maximum(np.abs(x.numpy()) * 2 ** -4, scale * 2 ** -9)[inside] + 1e-12)
+    # beyond the element range the OCP rule saturates to the largest normal
+    assert np.all(np.abs(back[~inside]) == 448.0 * scale[~inside])
+    # group amax lands in [256, 512) before saturation at 448 (OCP MX rule)
+    g = np.abs(x.numpy()).reshape(50, 4, 32).max(-1) / 2.0 ** (e.numpy().astype(np.int64) - 127)
+    assert np.all((g >= 256) & (g < 512))
+
+
+# -------------------------------------------------------------- scores ---
+
+def test_indexer_scores_brute_force():
+    pins.pin_indexer_scores(oracle.indexer_scores)
+
+
+def test_indexer_scores_collapse_identity():
+    """With no activation, sum_h w_h (q_h . k) == (sum_h w_h q_h) . k."""
+    r = np.random.default_rng(1)
+    q, w, k = r.standard_normal((64, 128)), r.random(64) / 64, r.standard_normal((300, 128))
+    collapsed = k @ (w @ q)
+    assert np.allclose(oracle.indexer_scores(q, w, k), collapsed, rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------- top-k ---
+
+def test_topk_brute_force_rank_definition():
+    pins.pin_topk(oracle.topk_select)
+
+
+def test_topk_matches_argpartition_on_distinct_scores():
+    r = np.random.default_rng(2)
+    s = r.standard_normal(5000)
+    got = oracle.topk_select(s, 2048)
+    ref = np.sort(np.argpartition(-s, 2047)[:2048])
+    assert np.array_equal(got, ref)
+
+
+# ----------------------------------------------------------- attention ---
+
+def test_sparse_attention_pins():
+    pins.pin_sparse_attention(oracle.sparse_attention)
+
+
+# -------------------------------------------------------------- paging ---
+
+def test_paged_rows_identity_and_permutation_invariance():
+    r = np.random.default_rng(4)
+    P, npg, D = 4, 6, 3
+    logical = r.standard_normal((npg * P, D))
+    table = r.permutation(npg)
+    pool = np.empty((npg, P, D))
+    for lp in range(npg):
+        pool[table[lp]] = logical[lp * P:(lp + 1) * P]
+    pos = r.integers(0, npg * P, 40)
+    assert np.array_equal(oracle.paged_rows(pool, table, P, pos), logical[pos])
+    # move every physical page elsewhere and update the table: same rows
+    perm = r.permutation(npg)
+    pool2 = np.empty_like(pool); pool2[perm] = pool
+    assert np.array_equal(oracle.paged_rows(pool2, perm[table], P, pos), logical[pos])
+
+
+def test_query_position_reading():
+    # decode: the single new token is the last one
+    assert oracle.query_position(256, 1, 0) == 255
+    # 4-token decode after 131072 cached keys: 131068..131071
+    assert [oracle.query_position(131072, 4, i) for i in range(4)] == [131068, 131069, 131070, 131071]
+    # 8192-token chunk after 122880 cached tokens
+    assert oracle.query_position(131072, 8192, 0) == 122880
+    # full causal prefill: t = i
+    assert oracle.query_position(32768, 32768, 17) == 17
+
+
+def test_case_poison_never_reached():
+    c = make_case("c1_tiny_f32", 3, seq_len_range=(250, 250))   # ragged last page
+    r = oracle.run_query(c, 0, 0)
+    assert np.isfinite(r["scores"]).all() and np.isfinite(r["out"]).all()
+    # the poisoned tail exists
+    last = c.block_table[0, (250 - 1) // 16]
+    assert torch.isnan(c.k_pool[last, 250 % 16:]).all()
+
+
+# -------------------------------------------------------------- zigzag ---
+
+def _read_golden_zigzag():
+    units, n = [], None
+    with open(os.path.join(GOLDEN, "zigzag_two_devices.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("n_blocks"):
+                n = int(line.split()[1])
+            else:
+                units.append([int(x) for x in line.split(":")[1].split()])
+    return n, units
+
+
+def test_zigzag_two_device_example():
+    n, units = _read_golden_zigzag()
+    assert [sorted(u) for u in oracle.zigzag_units(n)] == units
+
+
+@pytest.mark.parametrize("nb", [1, 2, 3, 7, 8, 512])
+def test_zigzag_bijection_and_balance(nb):
+    units = oracle.zigzag_units(nb)
+    flat = sorted(b for u in units for b in u)
+    assert flat == list(range(nb))                     # every block once
+    # a cost linear in the block index is equal over the paired units
+    costs = [sum(2 * b + 1 for b in u) for u in units if len(u) == 2]
+    assert len(set(costs)) <= 1
+
+
+# ---------------------------------------------------- whole-path brute force ---
+
+def test_run_query_brute_force_tiny():
+    """Full path on a tiny case by explicit loops: paged reads, scores, rank
+    selection and dense masked attention."""
+    c = make_case("c1_tiny_f32", 8, seq_len_range=(45, 45), q_len=3, page_size=4,
+                  h_i=2, d_i=4, topk=16, h_s=3, d_qk=6, d_v=4, scale_dim=6)
+    for i in range(3):
+        r = oracle.run_query(c, 0, i)
+        t = 45 - 3 + i
+        assert r["t"] == t
+        tok = c.token(0, i)
+        kpool = c.k_pool.numpy().astype(np.float64)
+        bt = c.block_table[0].numpy()
+        keys = [kpool[bt[s // 4], s % 4] for s in range(t + 1)]
+        sc = pins.brute_scores(c.q_i[tok].double().tolist(), c.w[tok].double().tolist(), keys)
+        assert np.allclose(r["scores"], sc, rtol=1e-12)
+        assert list(r["idx"]) == pins.brute_topk(list(sc), 16)
+        kvpool = c.kv_pool.numpy().astype(np.float64)
+        rows = np.array([kvpool[bt[s // 4], s % 4] for s in range(t + 1)])
+        o = pins.dense_masked_attention(c.q_s[tok].double().numpy(), rows, r["idx"], 4, 1 / math.sqrt(6))
+        assert np.allclose(r["out"], o, atol=1e-12)
+
+
+# -------------------------------------------------------------- mutations ---
+
+def _mutant_scores_no_weights(q, w, keys):
+    return (keys @ q.T).sum(1)
+
+
+def _mutant_scores_transposed(q, w, keys):
+    return (keys @ q.T) @ w[::-1]
+
+
+def _mutant_topk_tie_larger(scores, k):
+    n = min(k, len(scores))
+    pos = np.arange(len(scores))
+    return np.sort(np.lexsort((-pos, -np.asarray(scores)))[:n])
+
+
+def _mutant_topk_off_by_one(scores, k):
+    return oracle.topk_select(scores, k + 1)
+
+
+def _mutant_attn_no_scale(q, rows, d_v, scale):
+    return oracle.sparse_attention(q, rows, d_v, 1.0)
+
+
+def _mutant_attn_v_from_tail(q, rows, d_v, scale):
+    o, lse = oracle.sparse_attention(q, rows, rows.shape[1], scale)
+    return o[:, -d_v:], lse
+
+
+def _mutant_attn_sign(q, rows, d_v, scale):
+    return oracle.sparse_attention(q, rows, d_v, -scale)
+
+
+def _mutant_e4m3_bias(t=None):
+    t = oracle.e4m3fn_table().copy()
+    return t * 2.0
+
+
+@pytest.mark.parametrize("pin,mutant", [
+    (pins.pin_indexer_scores, _mutant_scores_no_weights),
+    (pins.pin_indexer_scores, _mutant_scores_transposed),
+    (pins.pin_topk, _mutant_topk_tie_larger),
+    (pins.pin_topk, _mutant_topk_off_by_one),
+    (pins.pin_sparse_attention, _mutant_attn_no_scale),
+    (pins.pin_sparse_attention, _mutant_attn_v_from_tail),
+    (pins.pin_sparse_attention, _mutant_attn_sign),
+])
+def test_pins_catch_planted_mistakes(pin, mutant):
+    with pytest.raises(AssertionError):
+        pin(mutant)
+
+
+def test_codec_pin_catches_wrong_bias():
+    with pytest.raises(AssertionError):
+        pins.pin_e4m3_table(_mutant_e4m3_bias())

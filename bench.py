@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the DSA hot path on one MI355X.
+
+A step is one call of dsa_fused_decode: the fused Lightning Indexer (per-head
+scores from the paged bf16 K cache, head-weighted sum, causal mask, Top-K) and
+Sparse Flash Attention over the selected latent rows, for a batch of 32
+sequences with contexts drawn uniformly from [4096, 32768] (one new token each),
+indexer 64 heads x 128, k = 2048, SFA 128 heads over 512 + 64 latent columns.
+Inputs are synthetic, seeded and resident in HBM; several value sets with the
+same layout are rotated so that the ~236 MB step does not sit in the 256 MB
+last-level cache between steps.
+
+Prints one JSON line (see the fields below).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode tokens/s + µs/step (indexer+TopK+SFA) at 32k ctx; % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "f32": 157.3}
+
+WORKLOADS = {
+    "c2_decode_bf16": "decode, 32 sequences, contexts U[4096, 32768], bf16",
+    "c2_decode_bf16_32k": "decode, 32 sequences, every context 32768, bf16",
+    "c4_decode_fp8": "decode, 64 sequences, contexts U[16384, 65536], FP8 indexer",
+    "c4_decode_mxfp8": "decode, 64 sequences, contexts U[16384, 65536], MXFP8 indexer",
+    "c5_decode4": "4-token decode, 8 sequences at 131072 tokens, bf16",
+}
+
+
+def _el(dtype):
+    return {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[dtype]
+
+
+def algorithmic(case):
+    """Bytes each step must move and flops it must do (per-head indexer)."""
+    import numpy as np
+    L = case.seq_lens_host.astype(np.int64)
+    T = case.q_lens_host.astype(np.int64)
+    ei, es = _el(case.idx_dtype), _el(case.sfa_dtype)
+    keys = int(L.sum())
+    k_scale = {"fp8": 4, "mxfp8": case.d_i // 32}.get(case.idx_dtype, 0)
+    q_scale = {"fp8": 4, "mxfp8": case.d_i // 32}.get(case.idx_dtype, 0)
+    tq = int(T.sum())
+    idx_b = tq * case.topk * 4
+    indexer_bytes = keys * (case.d_i * ei + k_scale) + tq * case.h_i * (case.d_i * ei + q_scale + 4) + idx_b
+    rows = 0
+    pairs = 0
+    for b in range(case.batch):
+        for i in range(int(T[b])):
+            t = int(L[b] - T[b] + i)
+            rows += min(case.topk, t + 1)
+            pairs += t + 1
+    # rows gathered once per sequence and step: the union over its queries is
+    # bounded by the per-query count; for one query per sequence they coincide
+    gather = rows * case.d_qk * es
+    sfa_bytes = gather + tq * case.h_s * (case.d_qk + case.d_v) * es + tq * case.h_s * 4 + idx_b
+    indexer_flops = 2 * case.h_i * case.d_i * pairs
+    sfa_flops = 2 * case.h_s * (case.d_qk + case.d_v) * rows
+    return dict(indexer_bytes=indexer_bytes, sfa_bytes=sfa_bytes,
+                fused_bytes=indexer_bytes + sfa_bytes - idx_b,
+                indexer_flops=indexer_flops, sfa_flops=sfa_flops, keys=keys, rows=rows)
+
+
+def time_calls(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(steps):
+        fn(s)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per call
+
+
+def cpu_baseline(case, budget_s):
+    """The oracle as it stands, timed on this host on a bounded sample."""
+    import numpy as np
+    import oracle
+    from oracle import dsa_oracle as od
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    qs = [(b, i) for b in range(case.batch) for i in range(int(case.q_lens_host[b]))]
+    # host copies of the pools are input staging, done before the clock starts
+    for t in (case.k_pool, case.kv_pool, case.k_scale, case.block_table):
+        if t is not None:
+            od._np(t)
+    done, t0 = 0, time.perf_counter()
+    order = np.random.default_rng(0).permutation(len(qs))
+    for j in order:
+        oracle.run_query(case, *qs[j])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(qs)} query tokens of the same workload (first seed), "
+                      f"{el:.1f} s, float64 NumPy, host cores available {len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2_decode_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--sets", type=int, default=4, help="value sets rotated between steps")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_04_amd import binding as B
+    from sparse_attention_04_amd.inputs import make_case
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    B.lib()
+    seed = 2
+    cases = [make_case(args.workload, seed, device="cuda", value_seed=seed + 100 * r) for r in range(args.sets)]
+    calls = [B.Call(c) for c in cases]
+    for c in calls:  # allocate every workspace before timing
+        c.workspace(B.DSA_OP_FUSED_DECODE)
+        c.workspace(B.DSA_OP_INDEXER_TOPK)
+        c.workspace(B.DSA_OP_SPARSE_ATTN)
+    case = cases[0]
+    R = len(calls)
+
+    ms_step = time_calls(lambda s: calls[s % R].fused_decode(), args.steps, args.warmup, torch)
+    # per-stage times on the same stream (indexer incl. its workspace clear; SFA incl. combine)
+    idx_sets = [c.indexer_topk().clone() for c in calls]
+    ms_idx = time_calls(lambda s: calls[s % R].indexer_topk(), args.steps, args.warmup, torch)
+    ms_sfa = time_calls(lambda s: calls[s % R].sparse_attn(idx_sets[s % R]), args.steps, args.warmup, torch)
+    if args.calib_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    a = algorithmic(case)
+    tokens = case.total_q
+    kern = {"indexer": (ms_idx, a["indexer_bytes"]), "sfa": (ms_sfa, a["sfa_bytes"])}
+    dom = max(kern, key=lambda k: kern[k][0])
+    dms, dbytes = kern[dom]
+    achieved = dbytes / (dms * 1e-3) / 1e9
+    prof = os.path.join(ROOT, "profiles", "traffic.json")
+    traffic = None
+    if os.path.exists(prof):
+        try:
+            tr = json.load(open(prof))
+            ent = tr.get(args.workload, {}).get(dom)
+            if ent and ent.get("kernel_source_sha") == _kernel_sha():
+                traffic = ent["bytes_per_launch"]
+        except Exception:
+            traffic = None
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "us_per_step": ms_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.idx_dtype if case.idx_dtype != "f32" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {WORKLOADS[args.workload]}",
+            "batch": case.batch, "query_tokens": tokens, "total_context_tokens": a["keys"],
+            "indexer": f"{case.h_i} heads x {case.d_i}, {case.idx_dtype}, k={case.topk}",
+            "sfa": f"{case.h_s} heads, latent {case.d_v} + rope {case.d_qk - case.d_v}, {case.sfa_dtype}",
+            "page_size": case.page_size, "value_sets_rotated": R,
+        },
+        "stages_ms": {"fused_step": ms_step, "indexer_topk": ms_idx, "sparse_attn": ms_sfa},
+        "algorithmic": {"fused_step_bytes": a["fused_bytes"], "indexer_bytes": a["indexer_bytes"],
+                        "sfa_bytes": a["sfa_bytes"], "indexer_flops_per_head": a["indexer_flops"],
+                        "sfa_flops": a["sfa_flops"]},
+        "step_hbm_frac": a["fused_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "mfma_frac": {
+            "indexer": a["indexer_flops"] / (ms_idx * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[case.idx_dtype],
+            "sfa": a["sfa_flops"] / (ms_sfa * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[case.sfa_dtype],
+        },
+    }
+    if args.cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_sha():
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "sparse_attention_04_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DSA hot path: the fused Lightning
+ * Indexer (per-head relevance scores read straight from a paged K cache, a
+ * head-weighted sum, a causal mask and Top-K selection) and Sparse Flash
+ * Attention over the selected latent KV rows.
+ *
+ * The operations are the ones the pages describe:
+ *   - "Deep Fusion of LI and SFA" (Day0 Inference Optimization on Ascend CANN,
+ *     sec. 2; Inference Acceleration for Next-Gen Attention Architectures,
+ *     sec. 3.1-3.2): relevance scoring, head weighting and Top-K in one operator
+ *     that reads the paged cache directly; SFA then reads the main-attention KV
+ *     rows at the selected indices.
+ *   - causal index computation (Adapting and Optimizing Inference for a New
+ *     Model Architecture on Ascend, sec. 5.2): a query at position t selects
+ *     among positions 0..t only.
+ *   - quantised index path (same page, sec. 4.2): MXFP8 with one scale shared
+ *     by every 32 elements.
+ *
+ * Conventions shared by every entry point
+ *   Ownership: every array argument is a DEVICE pointer owned by the caller;
+ *     the structs themselves are host memory read only during the call.  The
+ *     library never allocates, frees or synchronises device memory; scratch
+ *     memory comes from the caller's workspace `ws` of `ws_bytes` bytes, sized
+ *     with dsa_workspace_size().  One workspace must not be used by two calls
+ *     that may run concurrently.
+ *   Ordering: work is enqueued asynchronously on `stream` (a hipStream_t, NULL
+ *     = the default stream); nothing is waited for.
+ *   Errors: arguments are validated on the host before anything is enqueued;
+ *     a failed check returns its status and enqueues nothing.  A failed launch
+ *     returns DSA_ERR_HIP.  dsa_last_error() returns a thread-local message for
+ *     the last failure.  Contents of device arrays (block-table entries, lengths)
+ *     are preconditions: block_table entries < num_pages, seq_lens[b] <=
+ *     max_pages_per_seq * page_size, 0 <= q_lens <= seq_lens, values finite.
+ *   Positions: sequence b has L_b = seq_lens[b] keys in the caches; its
+ *     T_b = cu_q[b+1] - cu_q[b] query tokens are the LAST T_b positions, query
+ *     i sitting at t = L_b - T_b + i.  Key position s of sequence b lives in
+ *     row s % P of physical page block_table[b][s / P] of both caches.
+ *   Top-K: a query at t keeps n = min(topk, t + 1) positions with the largest
+ *     scores; equal scores go to the smaller position.  Output rows hold the n
+ *     LOGICAL positions in any order followed by -1 in slots n..topk-1.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,         /* null pointer, negative size, inconsistent scalars */
+  DSA_ERR_UNSUPPORTED = 2,         /* shape / dtype / page size not compiled in        */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < dsa_workspace_size(...)              */
+  DSA_ERR_HIP = 4                  /* a HIP runtime call failed                         */
+} dsa_status;
+
+typedef enum {
+  DSA_F32 = 0,         /* float32                                                */
+  DSA_BF16 = 1,        /* bfloat16                                               */
+  DSA_FP8_E4M3 = 2,    /* OCP e4m3fn bytes + one float32 scale per row           */
+  DSA_MXFP8_E4M3 = 3   /* OCP e4m3fn bytes + one e8m0 scale byte per 32 elements */
+} dsa_dtype;
+
+typedef enum {
+  DSA_OP_INDEXER_TOPK = 0,
+  DSA_OP_SPARSE_ATTN = 1,
+  DSA_OP_FUSED_DECODE = 2,
+  DSA_OP_FUSED_PREFILL = 3
+} dsa_op;
+
+/* A paged pool: data [num_pages][page_size][dim] elements of `dtype`.
+ * scale: DSA_FP8_E4M3   -> float32 [num_pages][page_size] (one per token)
+ *        DSA_MXFP8_E4M3 -> uint8 e8m0 [num_pages][page_size][dim / 32]
+ *        otherwise NULL.                                                      */
+typedef struct {
+  const void* data;
+  const void* scale;
+  int32_t dtype;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t dim;
+} dsa_paged_cache;
+
+/* The batch: B sequences, device arrays plus host-side scalars that bound them. */
+typedef struct {
+  int32_t batch;               /* B >= 1                                          */
+  const int32_t* seq_lens;     /* device [B]: L_b                                 */
+  const int32_t* cu_q;         /* device [B+1]: query-token offsets, cu_q[0] = 0  */
+  const int32_t* block_table;  /* device [B][max_pages_per_seq]                   */
+  int32_t max_pages_per_seq;
+  int32_t total_q;             /* == cu_q[B]                                      */
+  int32_t max_q_len;           /* >= every T_b                                    */
+  int32_t max_seq_len;         /* >= every L_b                                    */
+} dsa_batch;
+
+/* Indexer operands.
+ * q            device [total_q][n_heads][head_dim] of q_dtype (== k_cache->dtype)
+ * q_scale      DSA_FP8_E4M3: float32 [total_q][n_heads];
+ *              DSA_MXFP8_E4M3: uint8 e8m0 [total_q][n_heads][head_dim / 32]; else NULL
+ * head_weights device float32 [total_q][n_heads] (any sign)
+ * k_cache      paged pool with dim == head_dim                                */
+typedef struct {
+  const void* q;
+  int32_t q_dtype;
+  const void* q_scale;
+  const float* head_weights;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t topk;
+  const dsa_paged_cache* k_cache;
+} dsa_indexer_args;
+
+/* SFA operands (absorbed MLA form: one latent row per position, shared by all heads).
+ * q        device [total_q][n_heads][qk_dim] of q_dtype (== kv_cache->dtype, F32 or BF16)
+ * kv_cache paged pool with dim == qk_dim; V is the first v_dim columns of a row.
+ * Logits are softmax_scale * q_h . row over all qk_dim columns.                */
+typedef struct {
+  const void* q;
+  int32_t q_dtype;
+  int32_t n_heads;
+  int32_t qk_dim;
+  int32_t v_dim;
+  float softmax_scale;
+  const dsa_paged_cache* kv_cache;
+} dsa_sfa_args;
+
+/* Bytes of workspace the call needs (0 is possible).  Pointer fields are not
+ * read; only the scalars are.  `topk` for DSA_OP_SPARSE_ATTN comes from
+ * idx->topk when idx is given, else 2048. Returns 0 for an invalid op.        */
+size_t dsa_workspace_size(int32_t op, const dsa_batch* batch,
+                          const dsa_indexer_args* idx, const dsa_sfa_args* sfa);
+
+/* Fused Lightning Indexer: scores, head weighting, causal mask and Top-K in
+ * one pass over the paged K cache; the full score row is never written to
+ * device memory.  idx_out: device int32 [total_q][topk] (see Top-K above).   */
+dsa_status dsa_indexer_topk(const dsa_batch* batch, const dsa_indexer_args* args,
+                            int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse Flash Attention over the given index rows.
+ * idx: device int32 [total_q][topk] logical positions, -1 entries ignored
+ *      (each row must hold at least one valid position <= the query's t).
+ * out: device [total_q][n_heads][v_dim] in q_dtype.
+ * lse: device float32 [total_q][n_heads] natural-log sum-exp of the scaled
+ *      logits, or NULL.                                                       */
+dsa_status dsa_sparse_attn(const dsa_batch* batch, const dsa_sfa_args* args,
+                           const int32_t* idx, int32_t topk, void* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Decode step (small T_b): indexer + Top-K, then SFA on the selected rows.
+ * idx_out may be NULL (the indices then live in the workspace).              */
+dsa_status dsa_fused_decode(const dsa_batch* batch, const dsa_indexer_args* iargs,
+                            const dsa_sfa_args* sargs, void* out, float* lse,
+                            int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Causal (chunked) prefill (large T_b): query blocks of q_block tokens are
+ * paired from the two ends of each sequence (zigzag) so that every workgroup
+ * gets one short-history and one long-history block; results are written back
+ * to their original rows.  q_block must be 64.  idx_out may be NULL.          */
+dsa_status dsa_fused_prefill(const dsa_batch* batch, const dsa_indexer_args* iargs,
+                             const dsa_sfa_args* sargs, int32_t q_block, void* out,
+                             float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Static text for a status code. */
+const char* dsa_status_string(int32_t status);
+
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,382 @@
+// C ABI of the DSA hot path: argument validation, workspace planning and the
+// launch sequence of each entry point (see include/dsa.h for the contract).
+#include "dsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+
+using namespace dsa;
+
+namespace {
+
+thread_local std::string g_err;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dsa_status hip_fail(hipError_t e, const char* what) {
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxGrid = 2048;           // workspace is sized for up to this many indexer workgroups
+constexpr int kSfaTargetWG = 512;        // SFA workgroups aimed for when splitting index rows
+constexpr int kSfaRowTile = 32;
+constexpr size_t kLdsMax = 160 * 1024;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ------------------------------------------------------------ validation ---
+
+dsa_status check_batch(const dsa_batch* b) {
+  if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is NULL");
+  if (b->batch < 1) return fail(DSA_ERR_INVALID_ARG, "batch->batch must be >= 1 (got %d)", b->batch);
+  if (!b->seq_lens || !b->cu_q || !b->block_table)
+    return fail(DSA_ERR_INVALID_ARG, "batch->seq_lens, cu_q and block_table must be non-NULL");
+  if (b->max_pages_per_seq < 1) return fail(DSA_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
+  if (b->total_q < 0 || b->max_q_len < 0 || b->max_seq_len < 0)
+    return fail(DSA_ERR_INVALID_ARG, "negative total_q / max_q_len / max_seq_len");
+  if (b->max_q_len > b->max_seq_len) return fail(DSA_ERR_INVALID_ARG, "max_q_len > max_seq_len");
+  if (b->total_q > 0 && b->max_q_len == 0) return fail(DSA_ERR_INVALID_ARG, "total_q > 0 but max_q_len == 0");
+  if ((int64_t)b->max_q_len * b->batch < b->total_q)
+    return fail(DSA_ERR_INVALID_ARG, "total_q exceeds batch * max_q_len");
+  return DSA_OK;
+}
+
+dsa_status check_cache(const dsa_paged_cache* c, const char* name, int dim, int dtype,
+                       const dsa_batch* b) {
+  if (!c) return fail(DSA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!c->data) return fail(DSA_ERR_INVALID_ARG, "%s->data is NULL", name);
+  if (c->dtype != dtype) return fail(DSA_ERR_INVALID_ARG, "%s->dtype %d differs from the query dtype %d", name, c->dtype, dtype);
+  if (c->dim != dim) return fail(DSA_ERR_INVALID_ARG, "%s->dim %d differs from %d", name, c->dim, dim);
+  if (c->page_size < 1 || c->page_size > 4096) return fail(DSA_ERR_UNSUPPORTED, "%s->page_size %d outside [1, 4096]", name, c->page_size);
+  if (c->num_pages < 1) return fail(DSA_ERR_INVALID_ARG, "%s->num_pages must be >= 1", name);
+  if ((int64_t)b->max_pages_per_seq * c->page_size < b->max_seq_len)
+    return fail(DSA_ERR_INVALID_ARG, "max_pages_per_seq * page_size < max_seq_len");
+  if ((int64_t)c->num_pages * c->page_size >= (1ll << 31))
+    return fail(DSA_ERR_UNSUPPORTED, "%s holds 2^31 rows or more", name);
+  const bool need_scale = (dtype == DSA_FP8_E4M3 || dtype == DSA_MXFP8_E4M3);
+  if (need_scale && !c->scale) return fail(DSA_ERR_INVALID_ARG, "%s->scale is NULL for a quantised dtype", name);
+  return DSA_OK;
+}
+
+dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "indexer args are NULL");
+  if (!a->q || !a->head_weights) return fail(DSA_ERR_INVALID_ARG, "indexer q / head_weights are NULL");
+  if (a->topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", a->topk);
+  if (a->q_dtype < DSA_F32 || a->q_dtype > DSA_MXFP8_E4M3) return fail(DSA_ERR_INVALID_ARG, "unknown indexer dtype %d", a->q_dtype);
+  const bool ok_shape = (a->q_dtype == DSA_F32 && a->n_heads == 4 && a->head_dim == 32) ||
+                        (a->q_dtype != DSA_F32 && a->n_heads == 64 && a->head_dim == 128);
+  if (!ok_shape)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer shape (dtype %d, heads %d, dim %d) is not compiled in; supported: f32 4x32, bf16/fp8/mxfp8 64x128",
+                a->q_dtype, a->n_heads, a->head_dim);
+  if ((a->q_dtype == DSA_FP8_E4M3 || a->q_dtype == DSA_MXFP8_E4M3) && !a->q_scale)
+    return fail(DSA_ERR_INVALID_ARG, "indexer q_scale is NULL for a quantised dtype");
+  return check_cache(a->k_cache, "k_cache", a->head_dim, a->q_dtype, b);
+}
+
+dsa_status check_sfa(const dsa_batch* b, const dsa_sfa_args* a) {
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "sfa args are NULL");
+  if (!a->q) return fail(DSA_ERR_INVALID_ARG, "sfa q is NULL");
+  if (a->q_dtype != DSA_F32 && a->q_dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "sfa dtype %d not supported (f32, bf16)", a->q_dtype);
+  const bool ok_shape = (a->q_dtype == DSA_F32 && a->n_heads == 8 && a->qk_dim == 80 && a->v_dim == 64) ||
+                        (a->q_dtype == DSA_BF16 && a->n_heads == 128 && a->qk_dim == 576 && a->v_dim == 512);
+  if (!ok_shape)
+    return fail(DSA_ERR_UNSUPPORTED, "sfa shape (dtype %d, heads %d, qk %d, v %d) is not compiled in; supported: f32 8x80/64, bf16 128x576/512",
+                a->q_dtype, a->n_heads, a->qk_dim, a->v_dim);
+  if (!(a->softmax_scale > 0.f) || !(a->softmax_scale < 1e30f)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  return check_cache(a->kv_cache, "kv_cache", a->qk_dim, a->q_dtype, b);
+}
+
+int dt_kernel(int d) {
+  switch (d) {
+    case DSA_F32: return kF32;
+    case DSA_BF16: return kBF16;
+    case DSA_FP8_E4M3: return kFP8;
+    default: return kMX;
+  }
+}
+
+BatchView view_of(const dsa_batch* b, int page_size) {
+  BatchView v;
+  v.batch = b->batch;
+  v.seq_lens = b->seq_lens;
+  v.cu_q = b->cu_q;
+  v.block_table = b->block_table;
+  v.max_pages = b->max_pages_per_seq;
+  v.page_size = page_size;
+  v.total_q = b->total_q;
+  return v;
+}
+
+// ------------------------------------------------------ workspace planning ---
+
+struct SfaPlan {
+  int splits, rows_per_split;
+  size_t part_o_bytes, part_ml_bytes;
+};
+
+SfaPlan plan_sfa(const dsa_batch* b, int H, int Dv, int topk, bool bf16) {
+  SfaPlan pl{};
+  const int hg = bf16 ? std::max(1, H / 64) : 1;
+  const int64_t units = std::max<int64_t>(1, (int64_t)b->total_q * hg);
+  int splits = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(1, topk / 64), kSfaTargetWG / units));
+  int rps = (int)align_up((size_t)((topk + splits - 1) / splits), kSfaRowTile);
+  splits = (topk + rps - 1) / rps;
+  pl.splits = splits;
+  pl.rows_per_split = rps;
+  if (splits > 1) {
+    pl.part_o_bytes = align_up((size_t)b->total_q * splits * H * Dv * 4, 256);
+    pl.part_ml_bytes = align_up((size_t)b->total_q * splits * H * 4, 256);
+  }
+  return pl;
+}
+
+size_t indexer_bytes(const dsa_batch* b) {
+  return align_up(indexer_ws_bytes(b->batch, b->total_q, kMaxGrid), 256);
+}
+
+struct DeviceInfo {
+  int dev = -1, cus = 0;
+};
+thread_local DeviceInfo g_dev;
+
+dsa_status device_info(DeviceInfo& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (g_dev.dev != dev) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    g_dev.dev = dev;
+    g_dev.cus = cus;
+  }
+  out = g_dev;
+  return DSA_OK;
+}
+
+bool debug_mode() {
+  const char* s = getenv("DSA_DEBUG");
+  return s && s[0] == '1';
+}
+
+// ------------------------------------------------------------ launchers ---
+
+dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out,
+                              uint32_t* ws, hipStream_t st) {
+  if (b->total_q == 0) return DSA_OK;
+  const int maxq = (b->max_q_len <= 1) ? 1 : kMaxDecodeQ;
+  if (b->max_q_len > kMaxDecodeQ)
+    return fail(DSA_ERR_UNSUPPORTED, "decode indexer handles at most %d query tokens per sequence (max_q_len %d); use dsa_fused_prefill",
+                kMaxDecodeQ, b->max_q_len);
+  DeviceInfo di;
+  dsa_status s = device_info(di);
+  if (s != DSA_OK) return s;
+  const int P = a->k_cache->page_size;
+  const int maxp = (b->max_seq_len + P - 1) / P;
+  const int dt = dt_kernel(a->q_dtype);
+
+  hipError_t e = launch_zero(ws, indexer_ws_zero_bytes(b->batch, b->total_q) / 4, st);
+  if (e != hipSuccess) return hip_fail(e, "zero-fill launch");
+
+  // Pick the largest co-resident grid (2 or 1 workgroups per CU) and the
+  // largest sub-batch whose per-workgroup score buffer fits in LDS.
+  int grid = 0, chunk_cap = 0, sub = 0;
+  for (int per_cu = 2; per_cu >= 1 && grid == 0; per_cu--) {
+    const int G = std::min(kMaxGrid, per_cu * di.cus);
+    for (int nb = std::min(b->batch, G / 2); nb >= 1; nb = (nb > 1) ? nb / 2 : 0) {
+      const int64_t cap_pages = ((int64_t)nb * std::max(1, maxp) + (G - nb) - 1) / (G - nb);
+      const int64_t cap_keys = cap_pages * P;
+      const size_t lds = indexer_decode_lds_bytes(maxq, (int)std::min<int64_t>(cap_keys, 1 << 24));
+      if (lds > kLdsMax) continue;
+      int occ = 0;
+      e = indexer_decode_occupancy(dt, a->n_heads, a->head_dim, maxq, lds, &occ);
+      if (e != hipSuccess) return hip_fail(e, "occupancy query");
+      if (occ * di.cus < G) break;  // try fewer workgroups per CU
+      grid = G;
+      chunk_cap = (int)cap_keys;
+      sub = nb;
+      break;
+    }
+  }
+  if (grid == 0) return fail(DSA_ERR_UNSUPPORTED, "context too long for the decode indexer's on-chip score buffer");
+
+  IndexerDecodeParams p{};
+  p.q = a->q;
+  p.q_scale = a->q_scale;
+  p.w = a->head_weights;
+  p.k_data = a->k_cache->data;
+  p.k_scale = a->k_cache->scale;
+  p.topk = a->topk;
+  p.idx_out = idx_out;
+  p.ws = ws;
+  p.ws_nseq = b->batch;
+  p.ws_nq = b->total_q;
+  p.ws_grid_pad = (kMaxGrid + 31) / 32 * 32;
+  p.grid = grid;
+  p.chunk_cap = chunk_cap;
+  for (int b0 = 0; b0 < b->batch; b0 += sub) {
+    const int nb = std::min(sub, b->batch - b0);
+    p.bv = view_of(b, P);
+    p.bv.batch = nb;
+    p.bv.seq_lens = b->seq_lens + b0;
+    p.bv.cu_q = b->cu_q + b0;
+    p.bv.block_table = b->block_table + (size_t)b0 * b->max_pages_per_seq;
+    p.seq_base = b0;
+    e = launch_indexer_decode(dt, a->n_heads, a->head_dim, maxq, p, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  }
+  if (debug_mode()) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "indexer (debug sync)");
+    uint32_t flags = 0;
+    e = hipMemcpy(&flags, ws, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "indexer (debug flags)");
+    if (flags) return fail(DSA_ERR_HIP, "indexer reported error bits 0x%x (bounded wait expired or LDS bound)", flags);
+  }
+  return DSA_OK;
+}
+
+dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx, int topk,
+                   void* out, float* lse, unsigned char* ws, hipStream_t st) {
+  if (b->total_q == 0) return DSA_OK;
+  const bool bf16 = (a->q_dtype == DSA_BF16);
+  const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, bf16);
+  SfaParams p{};
+  p.bv = view_of(b, a->kv_cache->page_size);
+  p.q = a->q;
+  p.kv = a->kv_cache->data;
+  p.idx = idx;
+  p.topk = topk;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p.splits = pl.splits;
+  p.rows_per_split = pl.rows_per_split;
+  p.out = out;
+  p.lse = lse;
+  p.part_o = (float*)ws;
+  p.part_ml = (float*)(ws + pl.part_o_bytes);
+  const int dt = dt_kernel(a->q_dtype);
+  hipError_t e = launch_sfa(dt, a->n_heads, a->qk_dim, a->v_dim, p, st);
+  if (e != hipSuccess) return hip_fail(e, "sfa launch");
+  e = launch_sfa_combine(dt, a->n_heads, a->v_dim, p, st);
+  if (e != hipSuccess) return hip_fail(e, "sfa combine launch");
+  return DSA_OK;
+}
+
+size_t sfa_bytes(const dsa_batch* b, const dsa_sfa_args* a, int topk) {
+  const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, a->q_dtype == DSA_BF16);
+  return pl.part_o_bytes + pl.part_ml_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int32_t s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+size_t dsa_workspace_size(int32_t op, const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa) {
+  if (!b || b->batch < 1 || b->total_q < 0) return 0;
+  const int topk = ia ? ia->topk : 2048;
+  switch (op) {
+    case DSA_OP_INDEXER_TOPK:
+      return indexer_bytes(b);
+    case DSA_OP_SPARSE_ATTN:
+      return sa ? sfa_bytes(b, sa, topk) : 0;
+    case DSA_OP_FUSED_DECODE:
+    case DSA_OP_FUSED_PREFILL:
+      if (!ia || !sa) return 0;
+      return indexer_bytes(b) + align_up((size_t)b->total_q * std::max(1, topk) * 4, 256) + sfa_bytes(b, sa, topk);
+    default:
+      return 0;
+  }
+}
+
+dsa_status dsa_indexer_topk(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  dsa_status s = check_batch(b);
+  if (s == DSA_OK) s = check_indexer(b, a);
+  if (s != DSA_OK) return s;
+  if (!idx_out) return fail(DSA_ERR_INVALID_ARG, "idx_out is NULL");
+  const size_t need = dsa_workspace_size(DSA_OP_INDEXER_TOPK, b, a, nullptr);
+  if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  return run_indexer_decode(b, a, idx_out, (uint32_t*)ws, (hipStream_t)stream);
+}
+
+dsa_status dsa_sparse_attn(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx, int32_t topk,
+                           void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  dsa_status s = check_batch(b);
+  if (s == DSA_OK) s = check_sfa(b, a);
+  if (s != DSA_OK) return s;
+  if (!idx || !out) return fail(DSA_ERR_INVALID_ARG, "idx / out is NULL");
+  if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", topk);
+  const size_t need = sfa_bytes(b, a, topk);
+  if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  return run_sfa(b, a, idx, topk, out, lse, (unsigned char*)ws, (hipStream_t)stream);
+}
+
+dsa_status dsa_fused_decode(const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa,
+                            void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  g_err.clear();
+  dsa_status s = check_batch(b);
+  if (s == DSA_OK) s = check_indexer(b, ia);
+  if (s == DSA_OK) s = check_sfa(b, sa);
+  if (s != DSA_OK) return s;
+  if (!out) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
+  if (ia->k_cache->page_size != sa->kv_cache->page_size)
+    return fail(DSA_ERR_INVALID_ARG, "k_cache and kv_cache must share the page size (one block table)");
+  const size_t need = dsa_workspace_size(DSA_OP_FUSED_DECODE, b, ia, sa);
+  if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  unsigned char* w = (unsigned char*)ws;
+  const size_t ib = indexer_bytes(b);
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(w + ib);
+  hipStream_t st = (hipStream_t)stream;
+  s = run_indexer_decode(b, ia, idx, (uint32_t*)w, st);
+  if (s != DSA_OK) return s;
+  return run_sfa(b, sa, idx, ia->topk, out, lse, w + ib + align_up((size_t)b->total_q * ia->topk * 4, 256), st);
+}
+
+dsa_status dsa_fused_prefill(const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa,
+                             int32_t q_block, void* out, float* lse, int32_t* idx_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  g_err.clear();
+  dsa_status s = check_batch(b);
+  if (s == DSA_OK) s = check_indexer(b, ia);
+  if (s == DSA_OK) s = check_sfa(b, sa);
+  if (s != DSA_OK) return s;
+  if (!out) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
+  if (q_block != 64) return fail(DSA_ERR_UNSUPPORTED, "q_block must be 64 (got %d)", q_block);
+  (void)lse; (void)idx_out; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(DSA_ERR_UNSUPPORTED, "prefill path not built yet");
+}
+
+}  // extern "C"

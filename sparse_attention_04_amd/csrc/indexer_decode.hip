@@ -1,0 +1,638 @@
+// Fused Lightning Indexer for decode (few query tokens per sequence, long
+// contexts): per-head relevance scores q_h . k_s read straight from the paged
+// K cache, the head-weighted sum over heads, the causal mask and an exact
+// Top-K, without ever writing the score row to device memory.
+//
+// Method: "Deep Fusion of LI and SFA" (Day0 Inference Optimization on Ascend
+// CANN, sec. 2) and the three-step fused indexer (Inference Acceleration for
+// Next-Gen Attention Architectures, sec. 3.1).  The pages' design is a single
+// on-chip operator; here one sequence's keys are spread over several
+// workgroups so that the whole chip streams the cache, and the Top-K is an
+// exact cross-workgroup radix select:
+//
+//   1. each workgroup scores its page range (MFMA for bf16 / fp8 / MXFP8,
+//      VALU for small f32 shapes) and keeps the scores in LDS as
+//      order-preserving 32-bit keys;
+//   2. three 11/11/10-bit radix passes: local LDS histogram of the candidates
+//      that still match the fixed prefix, added into a per-query histogram in
+//      the workspace, a barrier among the sequence's workgroups, then every
+//      workgroup reads the same histogram and fixes the next digit of the k-th
+//      key (passes stop early once the boundary bin is taken whole);
+//   3. if equal keys straddle the boundary, one more exchange of per-workgroup
+//      tie counts hands the remaining slots to the smallest positions;
+//   4. each workgroup appends its selected positions to the query's output row.
+//
+// All workgroups of a launch are co-resident (cooperative launch), every wait
+// is bounded (group_barrier), and the grid always drains.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+constexpr int kIdxThreads = 256;
+constexpr int kIdxWaves = kIdxThreads / kWave;
+
+// Workspace layout (uint32 words), see indexer_ws_words().
+//   [0, 64)                        header: error bits
+//   [64, 64 + 32*B)                per sequence: barrier counter (own 128-B line)
+//   zeroed region ends here + per query {hist0[2048], outcnt (+31 pad)}
+//   then per query {hist1[2048], hist2[2048], tie[grid_pad]}
+struct WsLayout {
+  uint32_t* base;
+  int32_t nseq, nq, grid_pad;
+  __host__ __device__ uint32_t* err() const { return base; }
+  __host__ __device__ uint32_t* seq_ctr(int b) const { return base + 64 + 32 * b; }
+  __host__ __device__ uint32_t* qa(int g) const { return base + 64 + 32 * nseq + (size_t)g * 2080; }
+  __host__ __device__ uint32_t* hist(int g, int pass) const {
+    if (pass == 0) return qa(g);
+    return base + 64 + 32 * nseq + (size_t)nq * 2080 + (size_t)g * (4096 + grid_pad) + (pass - 1) * 2048;
+  }
+  __host__ __device__ uint32_t* outcnt(int g) const { return qa(g) + 2048; }
+  __host__ __device__ uint32_t* tie(int g) const {
+    return base + 64 + 32 * nseq + (size_t)nq * 2080 + (size_t)g * (4096 + grid_pad) + 4096;
+  }
+  __host__ __device__ size_t zero_words() const { return 64 + 32 * (size_t)nseq + (size_t)nq * 2080; }
+  __host__ __device__ size_t total_words() const {
+    return zero_words() + (size_t)nq * (4096 + grid_pad);
+  }
+};
+
+size_t indexer_ws_bytes(int nseq, int nq, int grid) {
+  WsLayout L{nullptr, nseq, nq, (grid + 31) / 32 * 32};
+  return L.total_words() * 4;
+}
+
+size_t indexer_ws_zero_bytes(int nseq, int nq) {
+  WsLayout L{nullptr, nseq, nq, 0};
+  return L.zero_words() * 4;
+}
+
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = 0u;
+}
+
+hipError_t launch_zero(uint32_t* p, size_t nwords, hipStream_t st) {
+  if (nwords == 0) return hipSuccess;
+  int blocks = (int)((nwords + 255) / 256);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, st, p, nwords);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- scoring ---
+
+// Score one 32-key tile per wave with 32x32 MFMAs.  Lane l owns key column
+// l%32; lane half h = l/32 holds the contiguous half [h*D/2, (h+1)*D/2) of the
+// key (and of every query row), which fixes the order of the contraction index
+// for both operands alike.  Returns the head-weighted score of key l%32 in
+// every lane (both halves).
+template <int DT, int H, int D>
+struct MfmaScorer;
+
+template <int H, int D>
+struct MfmaScorer<kBF16, H, D> {
+  static constexpr int MT = H / 32;       // M-tiles over heads
+  static constexpr int KS = D / 16;       // K-steps of 16 (8 per lane half)
+  bf16x8 a[MT][KS];
+  float wr[MT][16];
+  __device__ void load_query(const IndexerDecodeParams& p, int tok) {
+    const int lane = threadIdx.x & 63;
+    const uint16_t* q = (const uint16_t*)p.q + (size_t)tok * H * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const bf16x8* src = (const bf16x8*)(q + (size_t)(32 * mt + (lane & 31)) * D + (lane >> 5) * (D / 2));
+#pragma unroll
+      for (int kk = 0; kk < KS; kk++) a[mt][kk] = src[kk];
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        wr[mt][i] = p.w[(size_t)tok * H + 32 * mt + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3)];
+    }
+  }
+  struct Tile { u32x4 v[KS]; };
+  __device__ void load_tile(const IndexerDecodeParams& p, int64_t row, Tile& t) const {
+    const int lane = threadIdx.x & 63;
+    const u32x4* src = (const u32x4*)((const uint16_t*)p.k_data + row * D + (lane >> 5) * (D / 2));
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) t.v[kk] = src[kk];
+  }
+  __device__ float score(const IndexerDecodeParams& p, int64_t row, const Tile& t) const {
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[mt][i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) {
+      bf16x8 b = __builtin_bit_cast(bf16x8, t.v[kk]);
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], b, acc[mt], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[mt][i], s);
+    return s + __shfl_xor(s, 32);
+  }
+};
+
+// FP8 (per-token K scale, per-token-head Q scale) and MXFP8 (e8m0 per 32
+// elements): 32x32x64 scaled MFMAs on e4m3 bytes.  In this instruction a
+// lane's bytes 0..15 belong to k-block 0 and bytes 16..31 to k-block 1, and the
+// scale of block b of row m is taken from lane m + 32*b.  K-step kk covers the
+// two 32-element groups 2kk and 2kk+1 of the row, so lane half h carries the
+// h-th 16-byte half of each: bytes 0..15 <- dims 64kk + 16h .. +15 (group 2kk),
+// bytes 16..31 <- dims 64kk + 32 + 16h .. +15 (group 2kk+1), and supplies the
+// scale of group 2kk + h.
+template <int DT, int H, int D>
+struct MfmaScorerF8 {
+  static constexpr int MT = H / 32;
+  static constexpr int KS = D / 64;       // K-steps of 64
+  i32x8 a[MT][KS];
+  int32_t sa[MT][KS];                     // MX: e8m0 byte of group 2kk + h of this lane's row
+  float wr[MT][16];                       // FP8: w * q_scale
+  __device__ static i32x8 load_step(const uint8_t* rowp, int kk, int h) {
+    const u32x4* v = (const u32x4*)rowp;
+    const u32x4 lo = v[4 * kk + h], hi = v[4 * kk + 2 + h];
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+  __device__ void load_query(const IndexerDecodeParams& p, int tok) {
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const uint8_t* q = (const uint8_t*)p.q + (size_t)tok * H * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const int hrow = 32 * mt + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < KS; kk++) {
+        a[mt][kk] = load_step(q + (size_t)hrow * D, kk, h);
+        if constexpr (DT == kMX)
+          sa[mt][kk] = ((const uint8_t*)p.q_scale)[((size_t)tok * H + hrow) * (D / 32) + 2 * kk + h];
+        else
+          sa[mt][kk] = 127;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int hh = 32 * mt + 8 * (i / 4) + 4 * h + (i & 3);
+        float wv = p.w[(size_t)tok * H + hh];
+        if constexpr (DT == kFP8) wv *= ((const float*)p.q_scale)[(size_t)tok * H + hh];
+        wr[mt][i] = wv;
+      }
+    }
+  }
+  struct Tile { i32x8 v[KS]; uint32_t sc; };
+  __device__ void load_tile(const IndexerDecodeParams& p, int64_t row, Tile& t) const {
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const uint8_t* kr = (const uint8_t*)p.k_data + row * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) t.v[kk] = load_step(kr, kk, h);
+    if constexpr (DT == kFP8) {
+      t.sc = __float_as_uint(((const float*)p.k_scale)[row]);
+    } else {
+      const uint8_t* s8 = (const uint8_t*)p.k_scale + row * (D / 32);
+      uint32_t v = 0;
+#pragma unroll
+      for (int kk = 0; kk < KS; kk++) v |= (uint32_t)s8[2 * kk + h] << (8 * kk);
+      t.sc = v;
+    }
+  }
+  __device__ float score(const IndexerDecodeParams& p, int64_t row, const Tile& t) const {
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[mt][i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) {
+      const int sb = (DT == kMX) ? (int)((t.sc >> (8 * kk)) & 0xFFu) : 127;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+        acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][kk], t.v[kk], acc[mt], 0, 0,
+                                                                  0, sa[mt][kk], 0, sb);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[mt][i], s);
+    s += __shfl_xor(s, 32);
+    if constexpr (DT == kFP8) {
+      // the key's per-token scale (lane l%32 loaded it for its own key)
+      s *= __uint_as_float(t.sc);
+    }
+    return s;
+  }
+};
+
+template <int H, int D>
+struct MfmaScorer<kFP8, H, D> : MfmaScorerF8<kFP8, H, D> {};
+template <int H, int D>
+struct MfmaScorer<kMX, H, D> : MfmaScorerF8<kMX, H, D> {};
+
+// ---------------------------------------------------------- block helpers ---
+
+// Exclusive rank of `pred` among the block's threads in thread order, and the
+// block total.  `scratch` holds kIdxWaves+1 ints of LDS.
+__device__ __forceinline__ int block_rank(bool pred, int* scratch, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t m = __ballot(pred);
+  const int in_wave = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+  if (lane == 0) scratch[wave] = __popcll(m);
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kIdxWaves; w++) {
+    const int c = scratch[w];
+    before += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return before + in_wave;
+}
+
+// ------------------------------------------------------------------ kernel ---
+
+enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3 };
+
+template <int DT, int H, int D, int MAXQ>
+__global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerDecodeParams p) {
+  extern __shared__ uint32_t smem[];
+  // dynamic LDS: sc[MAXQ][cap] | lhist[2048] | scratch
+  uint32_t* sc = smem;
+  uint32_t* lhist = smem + (size_t)MAXQ * p.chunk_cap;
+  __shared__ int s_seqinfo[8];
+  __shared__ int s_scan[kIdxThreads];
+  __shared__ int s_rank[kIdxWaves + 1];
+  __shared__ uint32_t s_prefix[MAXQ], s_pmask[MAXQ];
+  __shared__ int s_need[MAXQ], s_state[MAXQ], s_take[MAXQ];
+  __shared__ int s_bin, s_above, s_bincnt;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const BatchView& bv = p.bv;
+  const int P = bv.page_size;
+  WsLayout W{p.ws, p.ws_nseq, p.ws_nq, p.ws_grid_pad};
+
+  // ---- 1. which sequence / page range this workgroup owns ------------------
+  // pages_b = ceil(L_b / P); cap = ceil(sum pages / (grid - B)); sequence b
+  // gets ceil(pages_b / cap) workgroups of at most cap pages each.
+  if (tid < kWave) {
+    int tot = 0;
+    for (int b0 = 0; b0 < bv.batch; b0 += kWave) {
+      const int b = b0 + lane;
+      const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) / P : 0;
+      tot += wave_sum(pg);
+    }
+    const int cap = (tot + (p.grid - bv.batch) - 1) / (p.grid - bv.batch);
+    int acc = 0, found = 0;
+    for (int b0 = 0; b0 < bv.batch && !found; b0 += kWave) {
+      const int b = b0 + lane;
+      const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) / P : 0;
+      const int nb = (cap > 0) ? (pg + cap - 1) / cap : 0;
+      // inclusive prefix of nb over the wave
+      int inc = nb;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+      }
+      const int start = acc + inc - nb;
+      const bool mine = (b < bv.batch) && (int)blockIdx.x >= start && (int)blockIdx.x < start + nb;
+      const uint64_t m = __ballot(mine);
+      if (m) {
+        const int src = __ffsll((unsigned long long)m) - 1;
+        if (lane == src) {
+          s_seqinfo[0] = b;
+          s_seqinfo[1] = (int)blockIdx.x - start;  // j
+          s_seqinfo[2] = nb;
+          s_seqinfo[3] = cap;
+          s_seqinfo[4] = pg;
+        }
+        found = 1;
+      }
+      acc += __shfl(inc, 63);
+    }
+    if (lane == 0 && !found) s_seqinfo[0] = -1;
+  }
+  __syncthreads();
+  const int b = s_seqinfo[0];
+  if (b < 0) return;  // surplus workgroup: owns nothing, joins no barrier
+  const int j = s_seqinfo[1], nb = s_seqinfo[2], cap = s_seqinfo[3], npg = s_seqinfo[4];
+  const int L = bv.seq_lens[b];
+  const int tok0 = bv.cu_q[b];
+  const int T = bv.cu_q[b + 1] - tok0;
+  const int s0 = j * cap * P;
+  int s1 = min(min(npg, (j + 1) * cap) * P, L);
+  if (s1 - s0 > p.chunk_cap) {  // cannot happen with the host's bound; stay in LDS bounds
+    if (tid == 0) atomic_add_agent(W.err(), 2u);
+    s1 = s0 + p.chunk_cap;
+  }
+  const int nloc = s1 - s0;
+  const int* bt = bv.block_table + (size_t)b * bv.max_pages;
+  const int K = p.topk;
+  uint32_t* ctr = W.seq_ctr(p.seq_base + b);
+
+  if (tid < MAXQ) {
+    s_prefix[tid] = 0u;
+    s_pmask[tid] = 0u;
+    s_need[tid] = K;
+    int st = kActive;
+    if (tid >= T) st = kAll;                       // no such query
+    else if (L - T + tid + 1 <= K) st = kAll;      // every visible position is kept
+    s_state[tid] = st;
+    s_take[tid] = 0;
+  }
+  __syncthreads();
+
+  // ---- queries that keep every visible position: slot s <- position s -------
+  for (int q = 0; q < T && q < MAXQ; q++) {
+    const int t = L - T + q;
+    if (t + 1 > K) continue;
+    int32_t* row = p.idx_out + (size_t)(tok0 + q) * K;
+    for (int s = s0 + tid; s < s1; s += kIdxThreads)
+      if (s <= t) row[s] = s;
+    if (j == 0)
+      for (int s = t + 1 + tid; s < K; s += kIdxThreads) row[s] = -1;
+  }
+  bool any_active = false;
+  for (int q = 0; q < MAXQ; q++) any_active |= (s_state[q] == kActive);
+  if (!any_active) return;  // uniform over the sequence's workgroups
+
+  // ---- 2. scores of this page range, kept in LDS as orderable keys ----------
+  {
+    MfmaScorer<DT, H, D> scorer;
+    using Tile = typename MfmaScorer<DT, H, D>::Tile;
+    const int ntiles = (nloc + 31) / 32;
+    for (int q = 0; q < T && q < MAXQ; q++) {
+      if (s_state[q] != kActive) continue;
+      const int t = L - T + q;
+      scorer.load_query(p, tok0 + q);
+      uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+      int tile = wave;
+      Tile cur;
+      int64_t row_cur = 0;
+      if (tile < ntiles) {
+        const int s = min(s0 + 32 * tile + (lane & 31), s1 - 1);
+        row_cur = (int64_t)bt[s / P] * P + (s % P);
+        scorer.load_tile(p, row_cur, cur);
+      }
+      for (; tile < ntiles; tile += kIdxWaves) {
+        Tile nxt;
+        int64_t row_nxt = 0;
+        const int tn = tile + kIdxWaves;
+        if (tn < ntiles) {
+          const int s = min(s0 + 32 * tn + (lane & 31), s1 - 1);
+          row_nxt = (int64_t)bt[s / P] * P + (s % P);
+          scorer.load_tile(p, row_nxt, nxt);
+        }
+        const float v = scorer.score(p, row_cur, cur);
+        const int s = s0 + 32 * tile + lane;
+        if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
+        cur = nxt;
+        row_cur = row_nxt;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. radix passes ------------------------------------------------------
+  int round = 0;
+  for (int pass = 0; pass < kMaxPasses; pass++) {
+    bool act = false;
+    for (int q = 0; q < MAXQ; q++) act |= (s_state[q] == kActive);
+    if (!act) break;
+    const int shift = (pass == 0) ? 21 : (pass == 1) ? 10 : 0;
+    const uint32_t dmask = (pass < 2) ? 0x7FFu : 0x3FFu;
+    for (int q = 0; q < T && q < MAXQ; q++) {
+      if (s_state[q] != kActive) continue;
+      for (int i = tid; i < kRadixBins; i += kIdxThreads) lhist[i] = 0u;
+      __syncthreads();
+      const uint32_t pre = s_prefix[q], pm = s_pmask[q];
+      const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+      for (int i = tid; i < nloc; i += kIdxThreads) {
+        const uint32_t x = scq[i];
+        if (x != 0u && (x & pm) == pre) atomicAdd(&lhist[(x >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      uint32_t* gh = W.hist(tok0 + q, pass);
+      for (int i = tid; i < kRadixBins; i += kIdxThreads) {
+        const uint32_t c = lhist[i];
+        if (c) atomic_add_agent(&gh[i], c);
+      }
+      if (j == 0 && pass + 1 < kMaxPasses) {
+        uint32_t* nh = W.hist(tok0 + q, pass + 1);
+        for (int i = tid; i < kRadixBins; i += kIdxThreads) nh[i] = 0u;
+      }
+    }
+    round++;
+    group_barrier(ctr, (uint32_t)(nb * round), W.err());
+    for (int q = 0; q < T && q < MAXQ; q++) {
+      if (s_state[q] != kActive) continue;
+      const uint32_t* gh = W.hist(tok0 + q, pass);
+      // each thread owns 8 consecutive bins; suffix sums from the top bin down
+      uint32_t h8[8];
+      uint32_t csum = 0;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        h8[e] = load_relaxed_agent(&gh[8 * tid + e]);
+        csum += h8[e];
+      }
+      s_scan[tid] = (int)csum;
+      __syncthreads();
+      // inclusive suffix scan (Hillis-Steele) over threads: above[t] = sum_{t' > t}
+      for (int o = 1; o < kIdxThreads; o <<= 1) {
+        const int v = (tid + o < kIdxThreads) ? s_scan[tid + o] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+      }
+      const int need = s_need[q];
+      if (tid == 0) {
+        s_bin = 0;
+        s_above = 0;
+        s_bincnt = 0;
+      }
+      __syncthreads();
+      const int above = s_scan[tid] - (int)csum;  // bins above this thread's 8
+      if (above < need && need <= above + (int)csum) {
+        int run = above;
+        for (int e = 7; e >= 0; e--) {
+          if (run + (int)h8[e] >= need) {
+            s_bin = 8 * tid + e;
+            s_above = run;
+            s_bincnt = (int)h8[e];
+            break;
+          }
+          run += (int)h8[e];
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        const int nneed = need - s_above;
+        s_need[q] = nneed;
+        s_prefix[q] |= ((uint32_t)s_bin) << shift;
+        s_pmask[q] |= dmask << shift;
+        if (s_bincnt == nneed) s_state[q] = kTakeBin;
+        else if (pass == kMaxPasses - 1) s_state[q] = kTiePass;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- 3b. equal keys straddle the boundary: smallest positions win ---------
+  bool any_tie = false;
+  for (int q = 0; q < MAXQ; q++) any_tie |= (s_state[q] == kTiePass);
+  if (any_tie) {
+    for (int q = 0; q < T && q < MAXQ; q++) {
+      if (s_state[q] != kTiePass) continue;
+      const uint32_t pre = s_prefix[q];
+      const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+      int cnt = 0;
+      for (int i = tid; i < nloc; i += kIdxThreads) cnt += (scq[i] == pre) ? 1 : 0;
+      cnt = wave_sum(cnt);
+      if (lane == 0) s_scan[wave] = cnt;
+      __syncthreads();
+      if (tid == 0) {
+        int c = 0;
+        for (int w = 0; w < kIdxWaves; w++) c += s_scan[w];
+        __hip_atomic_store(&W.tie(tok0 + q)[j], (uint32_t)c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+    }
+    round++;
+    group_barrier(ctr, (uint32_t)(nb * round), W.err());
+    for (int q = 0; q < T && q < MAXQ; q++) {
+      if (s_state[q] != kTiePass) continue;
+      if (tid == 0) {
+        int lower = 0;
+        const uint32_t* tc = W.tie(tok0 + q);
+        for (int jj = 0; jj < j; jj++) lower += (int)load_relaxed_agent(&tc[jj]);
+        s_take[q] = max(0, s_need[q] - lower);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- 4. append this workgroup's selected positions ------------------------
+  for (int q = 0; q < T && q < MAXQ; q++) {
+    const int st = s_state[q];
+    if (st == kAll) continue;
+    const uint32_t pre = s_prefix[q], pm = s_pmask[q];
+    const int take = s_take[q];
+    const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+    int32_t* row = p.idx_out + (size_t)(tok0 + q) * K;
+    __shared__ int s_base;
+    // count first (one atomic per workgroup), then write in position order
+    int mine = 0, ties_seen = 0;
+    for (int i0 = 0; i0 < nloc; i0 += kIdxThreads) {
+      const int i = i0 + tid;
+      const uint32_t x = (i < nloc) ? scq[i] : 0u;
+      const bool above = x != 0u && (x & pm) > pre;
+      const bool tie = x != 0u && (x & pm) == pre;
+      int tot_tie;
+      const int r = block_rank(tie, s_rank, tot_tie);
+      const bool sel = above || (tie && (st == kTakeBin || ties_seen + r < take));
+      int tot_sel;
+      (void)block_rank(sel, s_rank, tot_sel);
+      mine += tot_sel;
+      ties_seen += tot_tie;
+    }
+    if (tid == 0) s_base = (int)atomic_add_agent((uint32_t*)W.outcnt(tok0 + q), (uint32_t)mine);
+    __syncthreads();
+    int base = s_base;
+    ties_seen = 0;
+    for (int i0 = 0; i0 < nloc; i0 += kIdxThreads) {
+      const int i = i0 + tid;
+      const uint32_t x = (i < nloc) ? scq[i] : 0u;
+      const bool above = x != 0u && (x & pm) > pre;
+      const bool tie = x != 0u && (x & pm) == pre;
+      int tot_tie;
+      const int r = block_rank(tie, s_rank, tot_tie);
+      const bool sel = above || (tie && (st == kTakeBin || ties_seen + r < take));
+      int tot_sel;
+      const int rs = block_rank(sel, s_rank, tot_sel);
+      if (sel && base + rs < K) row[base + rs] = s0 + i;
+      base += tot_sel;
+      ties_seen += tot_tie;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------- f32 (small shapes) ---
+// VALU scorer: one key per thread, q and w staged in LDS.  Same selection code
+// path is shared by instantiating the kernel above with a VALU scorer.
+template <int H, int D>
+struct MfmaScorer<kF32, H, D> {
+  // Tile = one key per lane (64 keys per wave-tile would break the 32-key tile
+  // contract, so only lanes 0..31 score; lanes 32..63 duplicate the work).
+  float qv[H][D];
+  float wv[H];
+  __device__ void load_query(const IndexerDecodeParams& p, int tok) {
+    const float* q = (const float*)p.q + (size_t)tok * H * D;
+    for (int h = 0; h < H; h++) {
+      wv[h] = p.w[(size_t)tok * H + h];
+      for (int d = 0; d < D; d++) qv[h][d] = q[h * D + d];
+    }
+  }
+  struct Tile { float k[D]; };
+  __device__ void load_tile(const IndexerDecodeParams& p, int64_t row, Tile& t) const {
+    const float* src = (const float*)p.k_data + row * D;
+#pragma unroll
+    for (int d = 0; d < D; d++) t.k[d] = src[d];
+  }
+  __device__ float score(const IndexerDecodeParams& p, int64_t row, const Tile& t) const {
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < H; h++) {
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; d++) dot = fmaf(qv[h][d], t.k[d], dot);
+      s = fmaf(wv[h], dot, s);
+    }
+    return s;
+  }
+};
+
+// ------------------------------------------------------------------ launch ---
+
+template <int DT, int H, int D, int MAXQ>
+static hipError_t launch_one(const IndexerDecodeParams& p, size_t lds, hipStream_t st) {
+  auto kern = indexer_decode_kernel<DT, H, D, MAXQ>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  void* args[] = {(void*)&p};
+  return hipLaunchCooperativeKernel((const void*)kern, dim3(p.grid), dim3(kIdxThreads), args, (unsigned)lds, st);
+}
+
+int indexer_decode_max_q() { return kMaxDecodeQ; }
+
+size_t indexer_decode_lds_bytes(int maxq, int chunk_cap) {
+  return ((size_t)maxq * chunk_cap + kRadixBins) * 4;
+}
+
+hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t lds, int* blocks_per_cu) {
+  const void* k = nullptr;
+#define DSA_PICK(DT_, H_, D_, Q_) \
+  if (dtype == DT_ && H == H_ && D == D_ && maxq == Q_) k = (const void*)indexer_decode_kernel<DT_, H_, D_, Q_>;
+  DSA_INDEXER_DECODE_SHAPES(DSA_PICK)
+#undef DSA_PICK
+  if (!k) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k, kIdxThreads, lds);
+}
+
+hipError_t launch_indexer_decode(int dtype, int H, int D, int maxq, const IndexerDecodeParams& p,
+                                 hipStream_t st) {
+  const size_t lds = indexer_decode_lds_bytes(maxq, p.chunk_cap);
+#define DSA_PICK(DT_, H_, D_, Q_) \
+  if (dtype == DT_ && H == H_ && D == D_ && maxq == Q_) return launch_one<DT_, H_, D_, Q_>(p, lds, st);
+  DSA_INDEXER_DECODE_SHAPES(DSA_PICK)
+#undef DSA_PICK
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

@@ -1,0 +1,69 @@
+// Internal kernel entry points and launch parameter blocks (not part of the ABI).
+#pragma once
+#include "common.h"
+
+namespace dsa {
+
+constexpr int kMaxDecodeQ = 4;   // query tokens per sequence handled by the decode indexer
+
+// (dtype, H, D, MAXQ) instantiations of the decode indexer.
+#define DSA_INDEXER_DECODE_SHAPES(X) \
+  X(kF32, 4, 32, 1)                  \
+  X(kF32, 4, 32, 4)                  \
+  X(kBF16, 64, 128, 1)               \
+  X(kBF16, 64, 128, 4)               \
+  X(kFP8, 64, 128, 1)                \
+  X(kFP8, 64, 128, 4)                \
+  X(kMX, 64, 128, 1)                 \
+  X(kMX, 64, 128, 4)
+
+struct IndexerDecodeParams {
+  BatchView bv;            // (possibly a sub-range of) the batch
+  const void* q;           // [total_q][H][D]
+  const void* q_scale;     // fp8: f32 [total_q][H]; mx: u8 [total_q][H][D/32]
+  const float* w;          // [total_q][H]
+  const void* k_data;      // [num_pages][P][D]
+  const void* k_scale;     // fp8: f32 [num_pages][P]; mx: u8 [num_pages][P][D/32]
+  int32_t topk;
+  int32_t* idx_out;        // [total_q][topk]
+  uint32_t* ws;            // indexer workspace base
+  int32_t ws_nseq, ws_nq, ws_grid_pad;  // workspace geometry (whole batch)
+  int32_t seq_base;        // index of bv's first sequence in the whole batch
+  int32_t grid;            // workgroups launched
+  int32_t chunk_cap;       // LDS score slots per query (keys)
+};
+
+size_t indexer_ws_bytes(int nseq, int nq, int grid);
+size_t indexer_ws_zero_bytes(int nseq, int nq);
+size_t indexer_decode_lds_bytes(int maxq, int chunk_cap);
+hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t lds, int* blocks_per_cu);
+hipError_t launch_indexer_decode(int dtype, int H, int D, int maxq, const IndexerDecodeParams& p,
+                                 hipStream_t st);
+hipError_t launch_zero(uint32_t* p, size_t nwords, hipStream_t st);
+
+// ------------------------------------------------------------------- SFA ---
+
+// (dtype, H_S, Dqk, Dv) instantiations of SFA.
+#define DSA_SFA_SHAPES(X) \
+  X(kF32, 8, 80, 64)      \
+  X(kBF16, 128, 576, 512)
+
+struct SfaParams {
+  BatchView bv;
+  const void* q;           // [total_q][H][Dqk]
+  const void* kv;          // [num_pages][P][Dqk]
+  const int32_t* idx;      // [total_q][topk]
+  int32_t topk;
+  float scale_log2;        // softmax_scale * log2(e)
+  int32_t splits;          // row splits per (token, head group)
+  int32_t rows_per_split;  // multiple of the row tile
+  void* out;               // splits == 1: final [total_q][H][Dv] in q dtype
+  float* lse;              // splits == 1: [total_q][H] (natural log) or null
+  float* part_o;           // splits > 1: [total_q][splits][H][Dv] f32
+  float* part_ml;          // splits > 1: [total_q][splits][H][2] (max in log2 units, sum)
+};
+
+hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hipStream_t st);
+hipError_t launch_sfa_combine(int dtype, int H, int Dv, const SfaParams& p, hipStream_t st);
+
+}  // namespace dsa

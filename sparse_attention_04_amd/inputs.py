@@ -242,11 +242,15 @@ def _fill_pool(pool, scale_pool, logical_fn, n_rows, phys_rows, dtype, chunk_row
             sflat[phys_rows[r0:r1]] = sc.reshape(r1 - r0, -1)
 
 
-def make_case(name: str, seed: int = 0, device: str = "cpu", **overrides) -> Case:
+def make_case(name: str, seed: int = 0, device: str = "cpu", value_seed: Optional[int] = None,
+              **overrides) -> Case:
     """Build a preset workload (``PRESETS``) with optional overrides, e.g. a
-    smaller ``batch``/``seq_len_range``/``q_len`` for fast checks."""
+    smaller ``batch``/``seq_len_range``/``q_len`` for fast checks.  ``seed``
+    fixes the lengths and the page permutation; ``value_seed`` (default: seed)
+    fixes every drawn value, so several value sets can share one layout."""
     p = dict(PRESETS[name])
     p.update(overrides)
+    vseed = seed if value_seed is None else value_seed
     B, P = p["batch"], p["page_size"]
     lo, hi = p["seq_len_range"]
     # 1. sequence lengths
@@ -295,7 +299,7 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", **overrides) -> Cas
         return {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.uint8, MXFP8: torch.uint8}[dt]
 
     # 3. indexer q
-    g, og = _gen(seed, "q_i", dev), _gen(seed, "out_q_i", dev)
+    g, og = _gen(vseed, "q_i", dev), _gen(vseed, "out_q_i", dev)
     q_i, q_i_scale = _encode(_randn((total_q, h_i, d_i), g, dev, 1.0, outl, og), idt)
     # 4. indexer K, logical rows scattered into the pool
     k_pool = torch.empty((num_pages, P, d_i), dtype=storage_dtype(idt), device=dev)
@@ -305,14 +309,14 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", **overrides) -> Cas
         k_scale = torch.full((num_pages, P), float("nan"), dtype=torch.float32, device=dev)
     elif idt == MXFP8:
         k_scale = torch.full((num_pages, P, d_i // MX_GROUP), 127, dtype=torch.uint8, device=dev)
-    g, og = _gen(seed, "k_i", dev), _gen(seed, "out_k_i", dev)
+    g, og = _gen(vseed, "k_i", dev), _gen(vseed, "out_k_i", dev)
     _fill_pool(k_pool, k_scale, lambda n: _randn((n, d_i), g, dev, 1.0, outl, og),
                n_keys, phys_t, idt, chunk)
     # 5. head weights U(0,1)/w_div
-    g = _gen(seed, "w", dev)
+    g = _gen(vseed, "w", dev)
     w = (torch.rand((total_q, h_i), generator=g, device=dev) / p["w_div"]).float()
     # 6. SFA q
-    g, og = _gen(seed, "q_s", dev), _gen(seed, "out_q_s", dev)
+    g, og = _gen(vseed, "q_s", dev), _gen(vseed, "out_q_s", dev)
     q_s = torch.empty((total_q, h_s, d_qk), dtype=storage_dtype(sdt), device=dev)
     qrows = max(1, (1 << 22) // (h_s * d_qk))
     for r0 in range(0, total_q, qrows):
@@ -321,7 +325,7 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", **overrides) -> Cas
     # 7. latent KV rows
     kv_pool = torch.empty((num_pages, P, d_qk), dtype=storage_dtype(sdt), device=dev)
     kv_pool.fill_(float("nan"))
-    g, og = _gen(seed, "kv", dev), _gen(seed, "out_kv", dev)
+    g, og = _gen(vseed, "kv", dev), _gen(vseed, "out_kv", dev)
     _fill_pool(kv_pool, None, lambda n: _randn((n, d_qk), g, dev, mult, outl, og),
                n_keys, phys_t, sdt, chunk)
 

@@ -1,0 +1,189 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case is seeded; sizes are chosen so that the oracle finishes in seconds
+while the kernels still see several workgroups per sequence, several tiles and
+ragged last pages.  Full-size workloads are checked on sampled queries.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from checker import check_sfa, check_topk_row
+from sparse_attention_04_amd import binding as B
+from sparse_attention_04_amd.inputs import case_to, make_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    B.lib()  # fail loudly if the HIP library is missing
+
+
+def _host_out(t):
+    return t.float().cpu().numpy()
+
+
+def _queries(case, limit=None):
+    qs = [(b, i) for b in range(case.batch) for i in range(int(case.q_lens_host[b]))]
+    if limit is not None and len(qs) > limit:
+        r = np.random.default_rng(1234)
+        sel = sorted(r.choice(len(qs), limit, replace=False))
+        qs = [qs[s] for s in sel]
+    return qs
+
+
+def _check_indexer(case, call, idx, queries):
+    idx_h = idx.cpu().numpy()
+    diffs = 0
+    refs = {}
+    for (b, i) in queries:
+        ref = oracle.run_query(case, b, i)
+        refs[(b, i)] = ref
+        diffs += check_topk_row(idx_h[case.token(b, i)], ref, case.topk)
+    return refs, diffs
+
+
+def _check_sfa_on(case, out, queries, idx_rows):
+    """out rows vs the oracle's SFA run on the given index rows."""
+    out_h = _host_out(out)
+    worst = (0.0, 0.0)
+    for (b, i) in queries:
+        tok = case.token(b, i)
+        sel = idx_rows[tok]
+        sel = sel[sel >= 0]
+        ref_o, _ = oracle.sfa_query(case, b, i, sel)
+        mx, rel = check_sfa(out_h[tok], ref_o, case.sfa_dtype)
+        worst = (max(worst[0], mx), max(worst[1], rel))
+    return worst
+
+
+def _run_all_paths(case, queries=None, fused=True):
+    queries = queries or _queries(case)
+    call = B.Call(case)
+    _say(f"{case.name} seed={case.seed} B={case.batch} L={list(case.seq_lens_host[:4])} "
+         f"T={case.total_q} k={case.topk} P={case.page_size} dtype={case.idx_dtype}: indexer_topk")
+    idx = call.indexer_topk().clone()
+    torch.cuda.synchronize()
+    refs, diffs = _check_indexer(case, call, idx, queries)
+    # SFA on the oracle's index sets
+    _say(f"{case.name}: sparse_attn on oracle indices")
+    oidx = torch.full((case.total_q, case.topk), -1, dtype=torch.int32)
+    for (b, i), ref in refs.items():
+        row = ref["idx"]
+        oidx[case.token(b, i), :len(row)] = torch.from_numpy(row.astype(np.int32))
+    oidx_d = oidx.to(case.q_s.device)
+    out, lse = call.sparse_attn(oidx_d)
+    torch.cuda.synchronize()
+    out_h, lse_h = _host_out(out), lse.cpu().numpy()
+    for (b, i), ref in refs.items():
+        tok = case.token(b, i)
+        check_sfa(out_h[tok], ref["out"], case.sfa_dtype)
+        assert np.allclose(lse_h[tok], ref["lse"], atol=2e-3, rtol=1e-4), (lse_h[tok][:4], ref["lse"][:4])
+    if fused:
+        _say(f"{case.name}: fused_decode")
+        out, lse, fidx = call.fused_decode()
+        torch.cuda.synchronize()
+        fidx_h = fidx.cpu().numpy()
+        for (b, i), ref in refs.items():
+            check_topk_row(fidx_h[case.token(b, i)], ref, case.topk)
+        _check_sfa_on(case, out, list(refs.keys()), fidx_h)
+    return diffs
+
+
+def test_c1_tiny_f32():
+    case = case_to(make_case("c1_tiny_f32", 1), "cuda")
+    _run_all_paths(case)
+
+
+def test_c1_tiny_f32_ragged_pages():
+    case = case_to(make_case("c1_tiny_f32", 11, batch=3, seq_len_range=(60, 250)), "cuda")
+    _run_all_paths(case)
+
+
+def test_c2_bf16_small():
+    case = case_to(make_case("c2_decode_bf16", 2, batch=4, seq_len_range=(2500, 9000)), "cuda")
+    _run_all_paths(case)
+
+
+def test_c2_bf16_page16_ragged():
+    case = case_to(make_case("c2_decode_bf16", 12, batch=3, seq_len_range=(2049, 5000), page_size=16), "cuda")
+    _run_all_paths(case)
+
+
+def test_short_contexts_keep_every_position():
+    # t + 1 <= k: the index set is {0..t}, padded with -1
+    case = case_to(make_case("c2_decode_bf16", 3, batch=3, seq_lens=[1, 777, 2048]), "cuda")
+    _run_all_paths(case)
+
+
+def test_context_just_above_k():
+    case = case_to(make_case("c2_decode_bf16", 4, batch=2, seq_lens=[2049, 2050]), "cuda")
+    _run_all_paths(case)
+
+
+def test_equal_scores_go_to_smaller_positions():
+    case = make_case("c2_decode_bf16", 5, batch=2, seq_lens=[3000, 6000])
+    case.k_pool[:] = case.k_pool[0, 0]  # every key identical (poison included, but never read)
+    case = case_to(case, "cuda")
+    call = B.Call(case)
+    _say("equal scores: indexer_topk")
+    idx = call.indexer_topk().cpu().numpy()
+    for b in range(2):
+        row = np.sort(idx[b])
+        assert np.array_equal(row, np.arange(case.topk)), row[:10]
+
+
+@pytest.mark.parametrize("name", ["c4_decode_fp8", "c4_decode_mxfp8"])
+def test_c4_quantised_small(name):
+    case = case_to(make_case(name, 6, batch=3, seq_len_range=(3000, 7000)), "cuda")
+    _run_all_paths(case)
+
+
+def test_c5_multi_token_decode_small():
+    case = case_to(make_case("c5_decode4", 7, batch=2, seq_len_range=(3000, 6000)), "cuda")
+    _run_all_paths(case)
+
+
+def test_c2_full_size_sampled():
+    """The full decode workload (32 sequences, contexts U[4096, 32768]) in the
+    launch configuration the benchmark times, checked on sampled queries."""
+    _say("c2 full size: generating on device")
+    case = make_case("c2_decode_bf16", 2, device="cuda")
+    call = B.Call(case)
+    _say("c2 full size: fused_decode")
+    out, lse, idx = call.fused_decode()
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    qs = _queries(case, limit=4)
+    for (b, i) in qs:
+        ref = oracle.run_query(case, b, i)
+        check_topk_row(idx_h[case.token(b, i)], ref, case.topk)
+    _check_sfa_on(case, out, qs, idx_h)
+    # every row of the batch is a valid index set (property at full size)
+    for tok in range(case.total_q):
+        row = idx_h[tok]
+        assert len(set(row.tolist())) == case.topk and row.min() >= 0
+        assert row.max() < case.seq_lens_host[tok]
+
+
+def test_fused_equals_composition():
+    case = case_to(make_case("c2_decode_bf16", 8, batch=3, seq_len_range=(3000, 5000)), "cuda")
+    call = B.Call(case)
+    _say("composition: fused vs indexer+sparse_attn")
+    out_f, _, idx_f = call.fused_decode()
+    out_f = out_f.clone()
+    idx_f = idx_f.clone()
+    idx = call.indexer_topk().clone()
+    assert torch.equal(torch.sort(idx, 1).values, torch.sort(idx_f, 1).values)
+    out, _ = call.sparse_attn(idx_f)
+    assert torch.allclose(out.float(), out_f.float(), atol=1e-6)

@@ -53,17 +53,28 @@ __device__ __forceinline__ uint32_t load_relaxed_agent(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ void store_relaxed_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Barrier among the `count` workgroups sharing `ctr` (all co-resident).  The
-// round-th call returns once count*round arrivals are seen.  The wait is
-// bounded: on timeout an error bit is set and the workgroup continues, so the
-// grid always drains.
+// round-th call returns once count*round arrivals are seen.
+//
+// Every datum exchanged across workgroups around this barrier is itself an
+// agent-scope atomic (RMW, load or store), which the hardware performs at the
+// device-coherent level; the barrier therefore only has to order them: each
+// wave waits for its own outstanding memory operations to complete before the
+// workgroup arrives, and readers issue their loads after observing the count.
+// No cache write-back or invalidation is needed, which keeps a barrier round to
+// a few microseconds.  The wait is bounded: on timeout an error bit is set and
+// the workgroup continues, so the grid always drains.
 __device__ __forceinline__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    atomic_add_agent(ctr, 1u);
     uint32_t spins = 0;
-    while (load_acquire_agent(ctr) < target) {
+    while (load_relaxed_agent(ctr) < target) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
         atomic_add_agent(err, kErrBarrierTimeout);

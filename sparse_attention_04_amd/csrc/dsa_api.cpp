@@ -176,6 +176,14 @@ bool debug_mode() {
   return s && s[0] == '1';
 }
 
+// DSA_PROFILE=1: kernels record per-phase clock sums of their first workgroup
+// in the last kProfileBytes of the workspace.
+constexpr size_t kProfileBytes = 256;
+bool profile_mode() {
+  const char* s = getenv("DSA_PROFILE");
+  return s && s[0] == '1';
+}
+
 // ------------------------------------------------------------ launchers ---
 
 dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out,
@@ -271,6 +279,7 @@ dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx
   p.lse = lse;
   p.part_o = (float*)ws;
   p.part_ml = (float*)(ws + pl.part_o_bytes);
+  p.dbg = profile_mode() ? (unsigned long long*)(ws + pl.part_o_bytes + pl.part_ml_bytes) : nullptr;
   const int dt = dt_kernel(a->q_dtype);
   hipError_t e = launch_sfa(dt, a->n_heads, a->qk_dim, a->v_dim, p, st);
   if (e != hipSuccess) return hip_fail(e, "sfa launch");
@@ -281,7 +290,7 @@ dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx
 
 size_t sfa_bytes(const dsa_batch* b, const dsa_sfa_args* a, int topk) {
   const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, a->q_dtype == DSA_BF16);
-  return pl.part_o_bytes + pl.part_ml_bytes;
+  return pl.part_o_bytes + pl.part_ml_bytes + kProfileBytes;
 }
 
 }  // namespace

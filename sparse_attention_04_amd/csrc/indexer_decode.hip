@@ -257,6 +257,14 @@ __device__ __forceinline__ int block_rank(bool pred, int* scratch, int& total) {
 
 enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3 };
 
+// Phase timestamps of workgroup 0 (100 MHz real-time counter) in header words
+// 16.. of the workspace, for profiling the phases of one launch.
+#define DSA_STAMP(i)                                                                          \
+  do {                                                                                        \
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (i) < 24)                                      \
+      ((unsigned long long*)(W.base + 16))[(i)] = __builtin_amdgcn_s_memrealtime();            \
+  } while (0)
+
 template <int DT, int H, int D, int MAXQ>
 __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerDecodeParams p) {
   extern __shared__ uint32_t smem[];
@@ -274,6 +282,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
   const BatchView& bv = p.bv;
   const int P = bv.page_size;
   WsLayout W{p.ws, p.ws_nseq, p.ws_nq, p.ws_grid_pad};
+  DSA_STAMP(0);
 
   // ---- 1. which sequence / page range this workgroup owns ------------------
   // pages_b = ceil(L_b / P); cap = ceil(sum pages / (grid - B)); sequence b
@@ -359,6 +368,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
   bool any_active = false;
   for (int q = 0; q < MAXQ; q++) any_active |= (s_state[q] == kActive);
   if (!any_active) return;  // uniform over the sequence's workgroups
+  DSA_STAMP(1);
 
   // ---- 2. scores of this page range, kept in LDS as orderable keys ----------
   {
@@ -396,6 +406,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
     }
   }
   __syncthreads();
+  DSA_STAMP(2);
 
   // ---- 3. radix passes ------------------------------------------------------
   int round = 0;
@@ -423,11 +434,13 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
       }
       if (j == 0 && pass + 1 < kMaxPasses) {
         uint32_t* nh = W.hist(tok0 + q, pass + 1);
-        for (int i = tid; i < kRadixBins; i += kIdxThreads) nh[i] = 0u;
+        for (int i = tid; i < kRadixBins; i += kIdxThreads) store_relaxed_agent(&nh[i], 0u);
       }
     }
+    DSA_STAMP(3 + 3 * pass);
     round++;
     group_barrier(ctr, (uint32_t)(nb * round), W.err());
+    DSA_STAMP(4 + 3 * pass);
     for (int q = 0; q < T && q < MAXQ; q++) {
       if (s_state[q] != kActive) continue;
       const uint32_t* gh = W.hist(tok0 + q, pass);
@@ -439,15 +452,19 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
         h8[e] = load_relaxed_agent(&gh[8 * tid + e]);
         csum += h8[e];
       }
-      s_scan[tid] = (int)csum;
-      __syncthreads();
-      // inclusive suffix scan (Hillis-Steele) over threads: above[t] = sum_{t' > t}
-      for (int o = 1; o < kIdxThreads; o <<= 1) {
-        const int v = (tid + o < kIdxThreads) ? s_scan[tid + o] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
+      // suffix sums over threads: above[t] = sum of the counts of threads > t
+      int x = (int)csum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_down(x, o);
+        if (lane + o < 64) x += v;
       }
+      if (lane == 0) s_scan[wave] = x;  // wave total
+      __syncthreads();
+      int later = 0;
+#pragma unroll
+      for (int w = 0; w < kIdxWaves; w++) later += (w > wave) ? s_scan[w] : 0;
+      const int incl = x + later;       // this thread's bins and everything above
       const int need = s_need[q];
       if (tid == 0) {
         s_bin = 0;
@@ -455,7 +472,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
         s_bincnt = 0;
       }
       __syncthreads();
-      const int above = s_scan[tid] - (int)csum;  // bins above this thread's 8
+      const int above = incl - (int)csum;  // bins above this thread's 8
       if (above < need && need <= above + (int)csum) {
         int run = above;
         for (int e = 7; e >= 0; e--) {
@@ -479,7 +496,9 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
       }
       __syncthreads();
     }
+    DSA_STAMP(5 + 3 * pass);
   }
+  DSA_STAMP(12);
 
   // ---- 3b. equal keys straddle the boundary: smallest positions win ---------
   bool any_tie = false;
@@ -515,6 +534,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
     }
   }
 
+  DSA_STAMP(13);
   // ---- 4. append this workgroup's selected positions ------------------------
   for (int q = 0; q < T && q < MAXQ; q++) {
     const int st = s_state[q];
@@ -523,8 +543,33 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
     const int take = s_take[q];
     const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
     int32_t* row = p.idx_out + (size_t)(tok0 + q) * K;
+    uint32_t* oc = W.outcnt(tok0 + q);
+    if (st == kTakeBin) {
+      // every key at or above the boundary bin: each wave counts its keys,
+      // reserves its slots with one atomic, then writes them
+      int cnt = 0;
+      for (int i0 = wave * kWave; i0 < nloc; i0 += kIdxThreads) {
+        const int i = i0 + lane;
+        const uint32_t x = (i < nloc) ? scq[i] : 0u;
+        cnt += __popcll(__ballot(x != 0u && (x & pm) >= pre));
+      }
+      int base = 0;
+      if (lane == 0 && cnt) base = (int)atomic_add_agent(oc, (uint32_t)cnt);
+      base = __shfl(base, 0);
+      for (int i0 = wave * kWave; i0 < nloc; i0 += kIdxThreads) {
+        const int i = i0 + lane;
+        const uint32_t x = (i < nloc) ? scq[i] : 0u;
+        const bool sel = x != 0u && (x & pm) >= pre;
+        const uint64_t m = __ballot(sel);
+        const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (sel && base + r < K) row[base + r] = s0 + i;
+        base += __popcll(m);
+      }
+      continue;
+    }
+    // equal keys straddle the boundary: ties are taken in position order, so
+    // rank them across the whole workgroup
     __shared__ int s_base;
-    // count first (one atomic per workgroup), then write in position order
     int mine = 0, ties_seen = 0;
     for (int i0 = 0; i0 < nloc; i0 += kIdxThreads) {
       const int i = i0 + tid;
@@ -533,13 +578,13 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
       const bool tie = x != 0u && (x & pm) == pre;
       int tot_tie;
       const int r = block_rank(tie, s_rank, tot_tie);
-      const bool sel = above || (tie && (st == kTakeBin || ties_seen + r < take));
+      const bool sel = above || (tie && ties_seen + r < take);
       int tot_sel;
       (void)block_rank(sel, s_rank, tot_sel);
       mine += tot_sel;
       ties_seen += tot_tie;
     }
-    if (tid == 0) s_base = (int)atomic_add_agent((uint32_t*)W.outcnt(tok0 + q), (uint32_t)mine);
+    if (tid == 0) s_base = (int)atomic_add_agent(oc, (uint32_t)mine);
     __syncthreads();
     int base = s_base;
     ties_seen = 0;
@@ -550,7 +595,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
       const bool tie = x != 0u && (x & pm) == pre;
       int tot_tie;
       const int r = block_rank(tie, s_rank, tot_tie);
-      const bool sel = above || (tie && (st == kTakeBin || ties_seen + r < take));
+      const bool sel = above || (tie && ties_seen + r < take);
       int tot_sel;
       const int rs = block_rank(sel, s_rank, tot_sel);
       if (sel && base + rs < K) row[base + rs] = s0 + i;
@@ -559,6 +604,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
     }
     __syncthreads();
   }
+  DSA_STAMP(14);
 }
 
 // ------------------------------------------------------- f32 (small shapes) ---

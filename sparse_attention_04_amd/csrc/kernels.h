@@ -60,7 +60,8 @@ struct SfaParams {
   void* out;               // splits == 1: final [total_q][H][Dv] in q dtype
   float* lse;              // splits == 1: [total_q][H] (natural log) or null
   float* part_o;           // splits > 1: [total_q][splits][H][Dv] f32
-  float* part_ml;          // splits > 1: [total_q][splits][H][2] (max in log2 units, sum)
+  float* part_ml;          // splits > 1: [total_q][splits][H] log2-sum-exp of each range
+  unsigned long long* dbg; // optional: per-phase clock sums of workgroup 0, wave 0 (profiling)
 };
 
 hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hipStream_t st);

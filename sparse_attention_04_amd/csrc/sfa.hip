@@ -27,9 +27,6 @@ namespace dsa {
 namespace {
 
 constexpr int kSfaThreads = 256;
-constexpr int kTileRows = 32;
-constexpr int kHeadsPerWG = 64;
-constexpr int kLog2e_x = 0;  // (unused marker)
 
 __device__ __forceinline__ int find_seq(const BatchView& bv, int tok) {
   // largest b with cu_q[b] <= tok (binary search over cu_q[0..batch])
@@ -43,213 +40,330 @@ __device__ __forceinline__ int find_seq(const BatchView& bv, int tok) {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Workgroup barrier that waits only for this wave's LDS traffic, not for its
+// outstanding global->LDS tile loads (a plain __syncthreads() waits for every
+// memory operation, which would drain the load pipeline at each barrier).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte-per-lane global->LDS load (64 lanes fill lds_base .. +1 KiB in
+// lane order).  Issued through inline assembly so that the compiler's
+// wait-count pass, which cannot tell these LDS writes apart from the LDS reads
+// of other ring slots, does not drain every in-flight tile before each read;
+// the kernel orders them itself with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
+// vmcnt-only wait (expcnt and lgkmcnt left at their maxima): gfx9 encoding.
+#define DSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+constexpr int kSfaHeadsPerWG = 64;
+
+// bf16 SFA, H = 128, Dqk = 576, Dv = 512.
+//
+// A workgroup serves 64 heads of one token and one range of index slots with
+// 4 waves, one per SIMD: wave w takes heads 32*(w%2) .. +31 of the group
+// together with its partner w ^ 2.  The pair splits the QK^T contraction
+// (half = w/2 takes dims [288*half, 288*half + 288)) and exchanges the 32x32
+// partial logits through LDS, then splits the PV columns (half takes v in
+// [256*half, 256*half + 256)).  Per wave that is q^T in 72 registers and the
+// O^T accumulators in 128.  The two head groups of a token run as workgroups
+// 8 apart in launch order, which places them on the same XCD, so the second
+// gather of each row hits that XCD's L2.
+//
+// Per tile of 32 index slots:
+//   S^T[row, head] = KV[row, :] . q[head, :]     32x32x16 bf16 MFMAs, rows on M
+//   online softmax per head (lazy rescaling, see below)
+//   O^T[v, head] += V^T[v, row] P^T[row, head]   V^T read with ds_read_b64_tr_b16
+// The probabilities leave the first product already in the B-operand layout
+// of the second.  Rows stream through a 3-deep ring of LDS tiles filled by
+// direct global->LDS loads; slots holding -1 are masked.
 template <int DQK, int DV>
 __global__ __launch_bounds__(kSfaThreads, 1) void sfa_bf16_kernel(SfaParams p) {
-  constexpr int PITCH = DQK * 2 + 16;           // bytes per LDS row (padded)
-  constexpr int KSTEPS = DQK / 32;               // QK^T K-steps (18)
-  constexpr int VTILES = DV / 16;                // PV M-tiles (32)
-  constexpr int CHUNKS = DQK * 2 / 16;           // 16-byte chunks per row (72)
-  constexpr int LOADS = (kTileRows * CHUNKS + kSfaThreads - 1) / kSfaThreads;  // 9
+  constexpr int ROWB = DQK * 2;              // bytes of one latent row (1152)
+  constexpr int PITCH = ROWB + 16;           // LDS bytes per row (73 chunks of 16 B)
+  constexpr int TR = 32;                     // rows per tile
+  constexpr int TILE = 40 * 1024;            // 32 rows of PITCH bytes, rounded up to whole loads
+  constexpr int NBUF = 3;                    // tiles in flight
+  constexpr int NW = kSfaThreads / 64;       // 4 waves
+  constexpr int LPW = TILE / 1024 / NW;      // 1-KiB load instructions per wave per tile (10)
+  constexpr int KSH = DQK / 16 / 2;          // QK^T K-steps per wave (18)
+  constexpr int MVH = DV / 32 / 2;           // PV M-tiles per wave (8)
+  static_assert(TILE % (1024 * NW) == 0, "tile must split into whole 1-KiB loads per wave");
+  static_assert(TR * PITCH <= TILE, "tile rows must fit the buffer");
   extern __shared__ __attribute__((aligned(16))) unsigned char sfa_smem[];
-  unsigned char* buf0 = sfa_smem;
-  unsigned char* buf1 = sfa_smem + kTileRows * PITCH;
-  int32_t* s_rows = (int32_t*)(sfa_smem + 2 * kTileRows * PITCH);   // [rows_per_split]
+  float* s_x = (float*)(sfa_smem + NBUF * TILE);                      // [4 waves][16][64] partial logits
+  int32_t* s_rows = (int32_t*)(sfa_smem + NBUF * TILE + NW * 4096);   // [rows_per_split]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = blockIdx.x;                      // query token
-  const int hg = blockIdx.y;                     // head group of 64
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int hg = wave & 1, half = wave >> 1;
+  // launch order L -> (token, head block): L = 16*(t/8) + 8*hb + t%8
+  const int L = blockIdx.x;
+  const int g = 8 * (L >> 4) + (L & 7);
+  const int hb = (L >> 3) & 1;
   const int split = blockIdx.z;
+  if (g >= p.bv.total_q) return;
   const BatchView& bv = p.bv;
   const int P = bv.page_size;
+  const int H = 2 * kSfaHeadsPerWG;
   const int b = find_seq(bv, g);
   const int* bt = bv.block_table + (size_t)b * bv.max_pages;
   const int slot0 = split * p.rows_per_split;
   const int nslots = max(0, min(p.topk - slot0, p.rows_per_split));
   const int32_t* idx = p.idx + (size_t)g * p.topk + slot0;
 
-  // physical rows of this range (-1 for empty slots)
   for (int r = tid; r < nslots; r += kSfaThreads) {
     const int pos = idx[r];
     s_rows[r] = (pos >= 0) ? bt[pos / P] * P + (pos % P) : -1;
   }
   __syncthreads();
-  int fallback = -1;  // a valid row to read in place of empty slots
+  int fallback = -1;
   for (int r = 0; r < nslots && fallback < 0; r++) fallback = s_rows[r];
 
-  // q^T as the B operand of S^T = KV q^T: lane l holds head 16*wave + l%16,
-  // dims 32*kk + 8*(l/16) .. +7 for K-step kk.
-  const int head = hg * kHeadsPerWG + 16 * wave + (lane & 15);
-  const int grp = lane >> 4;
-  bf16x8 qb[KSTEPS];
+  // q^T as the B operand of S^T = KV q^T (32x32x16): lane l holds head
+  // 32*hg + l%32 and dims 16*kk + 8*(l/32) .. +7 of K-step kk (this half's kk).
+  const int head = kSfaHeadsPerWG * hb + 32 * hg + l32;
+  bf16x8 qb[KSH];
   {
-    const bf16x8* qs = (const bf16x8*)((const uint16_t*)p.q + ((size_t)g * (gridDim.y * kHeadsPerWG) + head) * DQK);
+    const bf16x8* qs = (const bf16x8*)((const uint16_t*)p.q + ((size_t)g * H + head) * DQK);
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; kk++) qb[kk] = qs[4 * kk + grp];
+    for (int k = 0; k < KSH; k++) qb[k] = qs[2 * (KSH * half + k) + hh];
   }
-
-  f32x4 o[VTILES];
+  f32x16 o[MVH];
 #pragma unroll
-  for (int i = 0; i < VTILES; i++) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MVH; i++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) o[i][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  // every compiler-visible load is complete before the tile loop, so the
+  // compiler's own waits never count the loop's asm-issued tile loads
+  __builtin_amdgcn_s_waitcnt(0);
 
-  const int ntiles = (nslots + kTileRows - 1) / kTileRows;
-  u32x4 stage[LOADS];
-  auto gather = [&](int tile) {
+  const int ntiles = (fallback >= 0) ? (nslots + TR - 1) / TR : 0;
+  // Row r of a tile sits at byte r * PITCH of its buffer.  The 16-byte pad
+  // makes consecutive rows start 9 bank groups apart (73 = 9 mod 16), so 16
+  // rows read at one column, and 4 rows x 2 chunks read by the transposing
+  // loads, hit distinct banks.  Each wave fills whole 1-KiB stretches of the
+  // buffer; lanes that land on a pad or on the slack after row 31 load chunk 0
+  // of the tile's row 0.
+  int ld_row[LPW], ld_col[LPW];
 #pragma unroll
-    for (int i = 0; i < LOADS; i++) {
-      const int c = tid + kSfaThreads * i;
-      if (c < kTileRows * CHUNKS) {
-        const int r = c / CHUNKS, col = c % CHUNKS;
-        const int slot = tile * kTileRows + r;
-        int row = (slot < nslots) ? s_rows[slot] : -1;
-        if (row < 0) row = fallback;
-        stage[i] = ((const u32x4*)((const uint16_t*)p.kv + (size_t)row * DQK))[col];
-      }
-    }
-  };
-  auto put = [&](unsigned char* buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; i++) {
-      const int c = tid + kSfaThreads * i;
-      if (c < kTileRows * CHUNKS) {
-        const int r = c / CHUNKS, col = c % CHUNKS;
-        *(u32x4*)(buf + r * PITCH + col * 16) = stage[i];
-      }
-    }
-  };
-
-  if (ntiles > 0 && fallback >= 0) {
-    gather(0);
-    put(buf0);
+  for (int k = 0; k < LPW; k++) {
+    const int off = (wave + NW * k) * 1024 + lane * 16;
+    const int r = off / PITCH, c = (off % PITCH) / 16;
+    const bool real = r < TR && c < ROWB / 16;
+    ld_row[k] = real ? r : 0;
+    ld_col[k] = real ? c * 16 : 0;
   }
-  __syncthreads();
-  for (int tile = 0; tile < ntiles && fallback >= 0; tile++) {
-    unsigned char* cur = (tile & 1) ? buf1 : buf0;
-    unsigned char* nxt = (tile & 1) ? buf0 : buf1;
-    if (tile + 1 < ntiles) gather(tile + 1);
+  auto issue = [&](int tile) {
+    unsigned char* buf = sfa_smem + (tile % NBUF) * TILE;
+    int rows[LPW];
+#pragma unroll
+    for (int k = 0; k < LPW; k++) {
+      const int slot = tile * TR + ld_row[k];
+      rows[k] = (slot < nslots) ? s_rows[slot] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < LPW; k++) {
+      const int row = (rows[k] < 0) ? fallback : rows[k];
+      const unsigned char* src = (const unsigned char*)p.kv + (size_t)row * ROWB + ld_col[k];
+      dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(buf + (wave + NW * k) * 1024)));
+    }
+  };
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  for (int tile = 0; tile < ntiles; tile++) {
+    if (tile + 2 < ntiles) {
+      issue(tile + 2);
+      DSA_WAIT_VMCNT(2 * LPW);
+    } else if (tile + 1 < ntiles) {
+      DSA_WAIT_VMCNT(LPW);
+    } else {
+      DSA_WAIT_VMCNT(0);
+    }
+    // rows of this tile that hold a selected position (bit r)
+    const int rslot = tile * TR + l32;
+    const uint32_t valid = (uint32_t)__ballot(hh == 0 && rslot < nslots && s_rows[rslot] >= 0);
+    lds_barrier();
+    const unsigned char* cur = sfa_smem + (tile % NBUF) * TILE;
 
-    // ---- S^T = KV q^T : rows on M (two 16-row tiles), this wave's 16 heads on N
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* ra = cur + (lane & 15) * PITCH + grp * 16;
+    // ---- partial S^T[row, head] over this half's dims: rows on M, heads on N;
+    // two independent accumulator chains keep the MFMA pipe busy
+    f32x16 sacc, sacc2;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; kk++) {
-      const bf16x8 a0 = *(const bf16x8*)(ra + kk * 64);
-      const bf16x8 a1 = *(const bf16x8*)(ra + 16 * PITCH + kk * 64);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[kk], s1, 0, 0, 0);
+    for (int e = 0; e < 16; e++) {
+      sacc[e] = 0.f;
+      sacc2[e] = 0.f;
     }
-    // ---- online softmax over this tile for head (lane & 15); this lane holds
-    // rows 4*grp + i (s0) and 16 + 4*grp + i (s1)
-    float z[8];
+    {
+      const unsigned char* rp = cur + l32 * PITCH + (2 * KSH * half + hh) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r0 = tile * kTileRows + 4 * grp + i, r1 = r0 + 16;
-      z[i] = (r0 < nslots && s_rows[r0] >= 0) ? s0[i] * p.scale_log2 : -INFINITY;
-      z[4 + i] = (r1 < nslots && s_rows[r1] >= 0) ? s1[i] * p.scale_log2 : -INFINITY;
+      for (int k = 0; k < KSH; k += 2) {
+        const bf16x8 a0 = *(const bf16x8*)(rp + 32 * k);
+        const bf16x8 a1 = *(const bf16x8*)(rp + 32 * (k + 1));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[k], sacc, 0, 0, 0);
+        sacc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[k + 1], sacc2, 0, 0, 0);
+      }
     }
-    float mt = z[0];
+    sacc += sacc2;
 #pragma unroll
-    for (int i = 1; i < 8; i++) mt = fmaxf(mt, z[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    for (int e = 0; e < 16; e++) s_x[(wave * 16 + e) * 64 + lane] = sacc[e];
+    lds_barrier();
+#pragma unroll
+    for (int e = 0; e < 16; e++) sacc[e] += s_x[((wave ^ 2) * 16 + e) * 64 + lane];
+
+    // ---- online softmax for head l%32; this lane holds rows 8*(i/4) + 4*hh + i%4
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int r = 8 * (i / 4) + 4 * hh + (i & 3);
+      sacc[i] = ((valid >> r) & 1u) ? sacc[i] * p.scale_log2 : -INFINITY;
+      mt = fmaxf(mt, sacc[i]);
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const bool none = (m_new == -INFINITY);
-    const float alpha = none ? 1.f : exp2f(m_run - m_new);
-    float pv[8], psum = 0.f;
+    // Lazy rescaling: the reference maximum m_run only moves when the tile's
+    // maximum exceeds it by more than 8 (log2 units), so probabilities stay
+    // below 2^8 (exact in fp32, in range for bf16) and the accumulators are
+    // rescaled only on those rare jumps.  The result is independent of m_run.
+    float alpha = 1.f;
+    if (m_run == -INFINITY) {
+      m_run = mt;                         // nothing accumulated yet
+    } else if (mt > m_run + 8.f) {
+      alpha = exp2f(m_run - mt);
+      m_run = mt;
+    }
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      pv[i] = none ? 0.f : exp2f(z[i] - m_new);
-      psum += pv[i];
+      for (int i = 0; i < MVH; i++) o[i] *= alpha;
+    }
+    const bool none = (m_run == -INFINITY);
+    float psum = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      // the denominator sums the same bf16-rounded weights the PV product uses
+      const __bf16 pv = (__bf16)(none ? 0.f : __builtin_amdgcn_exp2f(sacc[i] - m_run));
+      psum += (float)pv;
+      pb[i / 8][i % 8] = pv;
     }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
-    bf16x8 pb;
-#pragma unroll
-    for (int i = 0; i < 8; i++) pb[i] = (__bf16)pv[i];
-#pragma unroll
-    for (int i = 0; i < VTILES; i++) o[i] *= alpha;
 
-    // ---- O^T[v, head] += V^T[v, rows] P^T[rows, head]
-    // ds_read_b64_tr_b16 within each 16-lane group: source lane s = 4j + r
-    // reads row (4*grp + j) [+16], columns 16*mv + 4r .. +3; lane l then holds
-    // column 16*mv + l%16 of those 4 rows.
-    const int sl = lane & 15;
-    const unsigned char* tb0 = cur + (4 * grp + (sl >> 2)) * PITCH + (sl & 3) * 8;
-    const unsigned char* tb1 = tb0 + 16 * PITCH;
+    // ---- O^T[v, head] += V^T[v, rows] P^T[rows, head]: v on M (32), heads on N,
+    // K = 16 rows per MFMA.  K-block kb holds rows 16*kb + {4*hh + j, 8 + 4*hh + j}
+    // (j < 4) in this lane's slots, matching pb[kb].  V^T comes from
+    // ds_read_b64_tr_b16: in each 16-lane group, source lane s = 4j + r reads
+    // 4 columns (vbase + 4r ..) of row j of the group's 4 rows; lane i then holds
+    // column vbase + i of those 4 rows.
+    {
+      const int sl = lane & 15;
+      const int v0 = 32 * MVH * half + ((lane >> 4) & 1) * 16 + 4 * (sl & 3);   // first column loaded
 #pragma unroll
-    for (int mv = 0; mv < VTILES; mv++) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb0 + mv * 32));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb1 + mv * 32));
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[mv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, o[mv], 0, 0, 0);
+      for (int kb = 0; kb < 2; kb++) {
+        const int r0 = 16 * kb + 4 * hh + (sl >> 2);  // rows for the first 4 slots
+        const unsigned char* rp0 = cur + r0 * PITCH + v0 * 2;
+        const unsigned char* rp1 = rp0 + 8 * PITCH;   // rows for the last 4 slots
+#pragma unroll
+        for (int mv = 0; mv < MVH; mv++) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rp0 + 64 * mv));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rp1 + 64 * mv));
+          typedef short s16x8 __attribute__((ext_vector_type(8)));
+          const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[kb], o[mv], 0, 0, 0);
+        }
+      }
     }
-
-    if (tile + 1 < ntiles) put(nxt);
-    __syncthreads();
+    lds_barrier();
   }
 
-  // ---- epilogue: full row sum for this head, then write
-  l_run += __shfl_xor(l_run, 16);
+  // ---- epilogue: o[mv][i] holds head l%32, v = 32*(MVH*half + mv) + 8*(i/4) + 4*hh + (i%4)
   l_run += __shfl_xor(l_run, 32);
-  const int H = gridDim.y * kHeadsPerWG;
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   if (p.splits == 1) {
     uint16_t* out = (uint16_t*)p.out + ((size_t)g * H + head) * DV;
 #pragma unroll
-    for (int mv = 0; mv < VTILES; mv++) {
-      const int v = 16 * mv + 4 * grp;
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(o[mv][0] * inv) | ((uint32_t)f32_to_bf16(o[mv][1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16(o[mv][2] * inv) | ((uint32_t)f32_to_bf16(o[mv][3] * inv) << 16);
-      *(uint2*)(out + v) = pk;
-    }
-    if (p.lse && grp == 0)
+    for (int mv = 0; mv < MVH; mv++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        const int v = 32 * (MVH * half + mv) + 8 * q4 + 4 * hh;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(o[mv][4 * q4] * inv) | ((uint32_t)f32_to_bf16(o[mv][4 * q4 + 1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(o[mv][4 * q4 + 2] * inv) | ((uint32_t)f32_to_bf16(o[mv][4 * q4 + 3] * inv) << 16);
+        *(uint2*)(out + v) = pk;
+      }
+    if (p.lse && hh == 0 && half == 0)
       p.lse[(size_t)g * H + head] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
   } else {
     float* po = p.part_o + (((size_t)g * p.splits + split) * H + head) * DV;
 #pragma unroll
-    for (int mv = 0; mv < VTILES; mv++) {
-      const int v = 16 * mv + 4 * grp;
-      *(f32x4*)(po + v) = o[mv] * inv;
-    }
-    if (grp == 0)
+    for (int mv = 0; mv < MVH; mv++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        const int v = 32 * (MVH * half + mv) + 8 * q4 + 4 * hh;
+        f32x4 val = {o[mv][4 * q4] * inv, o[mv][4 * q4 + 1] * inv, o[mv][4 * q4 + 2] * inv, o[mv][4 * q4 + 3] * inv};
+        *(f32x4*)(po + v) = val;
+      }
+    if (hh == 0 && half == 0)
       p.part_ml[((size_t)g * p.splits + split) * H + head] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
   }
 }
 
-// Merge the per-range partials of one token: weights 2^(lse_j - lse).
+// Merge the per-range partials of one token: weights 2^(lse_j - lse).  One
+// workgroup per (token, group of 4 heads); each thread owns DV/64 columns.
 template <int DV, bool BF16OUT>
 __global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p, int H) {
+  constexpr int CPT = DV / 64;  // columns per thread
   const int g = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int c0 = (threadIdx.x & 63) * CPT;
   const int S = p.splits;
-  for (int e = threadIdx.x; e < H * (DV / 4); e += blockDim.x) {
-    const int h = e / (DV / 4), v = 4 * (e % (DV / 4));
-    float mx = -INFINITY;
-    for (int j = 0; j < S; j++) mx = fmaxf(mx, p.part_ml[((size_t)g * S + j) * H + h]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    for (int j = 0; j < S; j++) {
-      const float l = p.part_ml[((size_t)g * S + j) * H + h];
-      if (l == -INFINITY) continue;
-      const float wj = exp2f(l - mx);
-      den += wj;
-      acc += wj * *(const f32x4*)(p.part_o + (((size_t)g * S + j) * H + h) * DV + v);
-    }
-    const float inv = (den > 0.f) ? 1.f / den : 0.f;
-    acc *= inv;
-    if (BF16OUT) {
-      uint16_t* out = (uint16_t*)p.out + ((size_t)g * H + h) * DV + v;
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-      pk.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-      *(uint2*)out = pk;
+  if (h >= H) return;
+  float mx = -INFINITY;
+  for (int j = 0; j < S; j++) mx = fmaxf(mx, p.part_ml[((size_t)g * S + j) * H + h]);
+  float acc[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; c++) acc[c] = 0.f;
+  float den = 0.f;
+  for (int j = 0; j < S; j++) {
+    const float l = p.part_ml[((size_t)g * S + j) * H + h];
+    if (l == -INFINITY) continue;
+    const float wj = exp2f(l - mx);
+    den += wj;
+    const float* src = p.part_o + (((size_t)g * S + j) * H + h) * DV + c0;
+    if constexpr (CPT % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4) {
+        const f32x4 v = *(const f32x4*)(src + c);
+        acc[c] += wj * v[0]; acc[c + 1] += wj * v[1]; acc[c + 2] += wj * v[2]; acc[c + 3] += wj * v[3];
+      }
     } else {
-      *(f32x4*)((float*)p.out + ((size_t)g * H + h) * DV + v) = acc;
+#pragma unroll
+      for (int c = 0; c < CPT; c++) acc[c] += wj * src[c];
     }
-    if (p.lse && v == 0)
-      p.lse[(size_t)g * H + h] = (den > 0.f) ? (mx + log2f(den)) * 0.69314718055994531f : -INFINITY;
   }
+  const float inv = (den > 0.f) ? 1.f / den : 0.f;
+  if constexpr (BF16OUT && CPT % 4 == 0) {
+    uint16_t* out = (uint16_t*)p.out + ((size_t)g * H + h) * DV + c0;
+#pragma unroll
+    for (int c = 0; c < CPT; c += 4) {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(acc[c] * inv) | ((uint32_t)f32_to_bf16(acc[c + 1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16(acc[c + 2] * inv) | ((uint32_t)f32_to_bf16(acc[c + 3] * inv) << 16);
+      *(uint2*)(out + c) = pk;
+    }
+  } else {
+    float* out = (float*)p.out + ((size_t)g * H + h) * DV + c0;
+#pragma unroll
+    for (int c = 0; c < CPT; c++) out[c] = acc[c] * inv;
+  }
+  if (p.lse && (threadIdx.x & 63) == 0)
+    p.lse[(size_t)g * H + h] = (den > 0.f) ? (mx + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 
 // f32 SFA for small head counts and widths: one workgroup per (token, range),
@@ -361,10 +475,11 @@ hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hip
   if (p.bv.total_q == 0) return hipSuccess;
   if (dtype == kBF16 && H == 128 && Dqk == 576 && Dv == 512) {
     auto kern = sfa_bf16_kernel<576, 512>;
-    const size_t lds = 2 * kTileRows * (576 * 2 + 16) + (size_t)p.rows_per_split * 4;
+    const size_t lds = 3 * 40 * 1024 + 4 * 4096 + (size_t)p.rows_per_split * 4;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(p.bv.total_q, H / kHeadsPerWG, p.splits), dim3(kSfaThreads), lds, st, p);
+    const int tok8 = (p.bv.total_q + 7) / 8 * 8;
+    hipLaunchKernelGGL(kern, dim3(2 * tok8, 1, p.splits), dim3(kSfaThreads), lds, st, p);
     return hipGetLastError();
   }
   if (dtype == kF32 && H == 8 && Dqk == 80 && Dv == 64) {
@@ -377,11 +492,11 @@ hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hip
 hipError_t launch_sfa_combine(int dtype, int H, int Dv, const SfaParams& p, hipStream_t st) {
   if (p.bv.total_q == 0 || p.splits <= 1) return hipSuccess;
   if (dtype == kBF16 && Dv == 512) {
-    hipLaunchKernelGGL((sfa_combine_kernel<512, true>), dim3(p.bv.total_q), dim3(256), 0, st, p, H);
+    hipLaunchKernelGGL((sfa_combine_kernel<512, true>), dim3(p.bv.total_q, (H + 3) / 4), dim3(256), 0, st, p, H);
     return hipGetLastError();
   }
   if (dtype == kF32 && Dv == 64) {
-    hipLaunchKernelGGL((sfa_combine_kernel<64, false>), dim3(p.bv.total_q), dim3(256), 0, st, p, H);
+    hipLaunchKernelGGL((sfa_combine_kernel<64, false>), dim3(p.bv.total_q, (H + 3) / 4), dim3(256), 0, st, p, H);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

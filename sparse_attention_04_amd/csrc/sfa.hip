@@ -64,46 +64,57 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 #define DSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
 constexpr int kSfaHeadsPerWG = 64;
+constexpr int kSfaBf16Threads = 512;
 
 // bf16 SFA, H = 128, Dqk = 576, Dv = 512.
 //
 // A workgroup serves 64 heads of one token and one range of index slots with
-// 4 waves, one per SIMD: wave w takes heads 32*(w%2) .. +31 of the group
-// together with its partner w ^ 2.  The pair splits the QK^T contraction
-// (half = w/2 takes dims [288*half, 288*half + 288)) and exchanges the 32x32
-// partial logits through LDS, then splits the PV columns (half takes v in
-// [256*half, 256*half + 256)).  Per wave that is q^T in 72 registers and the
-// O^T accumulators in 128.  The two head groups of a token run as workgroups
-// 8 apart in launch order, which places them on the same XCD, so the second
-// gather of each row hits that XCD's L2.
+// 8 waves (two per SIMD): wave w takes the 16 heads 16*(w%4) .. +15 of the
+// group together with its partner w ^ 4.  The pair splits the QK^T
+// contraction (half = w/4 takes dims [288*half, 288*half + 288)) and exchanges
+// the 32x16 partial logits through LDS, then splits the PV columns (half takes
+// v in [256*half, 256*half + 256)).  Per wave that is q^T in 36 registers and
+// the O^T accumulators in 64.  The two head groups of a token run as
+// workgroups 8 apart in launch order, which places them on the same XCD, so
+// the second gather of each row hits that XCD's L2.
 //
 // Per tile of 32 index slots:
-//   S^T[row, head] = KV[row, :] . q[head, :]     32x32x16 bf16 MFMAs, rows on M
+//   S^T[row, head] = KV[row, :] . q[head, :]     16x16x32 bf16 MFMAs, rows on M
 //   online softmax per head (lazy rescaling, see below)
 //   O^T[v, head] += V^T[v, row] P^T[row, head]   V^T read with ds_read_b64_tr_b16
 // The probabilities leave the first product already in the B-operand layout
 // of the second.  Rows stream through a 3-deep ring of LDS tiles filled by
 // direct global->LDS loads; slots holding -1 are masked.
 template <int DQK, int DV>
-__global__ __launch_bounds__(kSfaThreads, 1) void sfa_bf16_kernel(SfaParams p) {
+__global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams p) {
   constexpr int ROWB = DQK * 2;              // bytes of one latent row (1152)
   constexpr int PITCH = ROWB + 16;           // LDS bytes per row (73 chunks of 16 B)
   constexpr int TR = 32;                     // rows per tile
   constexpr int TILE = 40 * 1024;            // 32 rows of PITCH bytes, rounded up to whole loads
   constexpr int NBUF = 3;                    // tiles in flight
-  constexpr int NW = kSfaThreads / 64;       // 4 waves
-  constexpr int LPW = TILE / 1024 / NW;      // 1-KiB load instructions per wave per tile (10)
-  constexpr int KSH = DQK / 16 / 2;          // QK^T K-steps per wave (18)
-  constexpr int MVH = DV / 32 / 2;           // PV M-tiles per wave (8)
+  constexpr int NW = kSfaBf16Threads / 64;   // 8 waves
+  constexpr int LPW = TILE / 1024 / NW;      // 1-KiB load instructions per wave per tile (5)
+  constexpr int KSH = DQK / 32 / 2;          // QK^T K-steps of 32 per wave (9)
+  constexpr int MVH = DV / 16 / 2;           // PV M-tiles of 16 columns per wave (16)
   static_assert(TILE % (1024 * NW) == 0, "tile must split into whole 1-KiB loads per wave");
   static_assert(TR * PITCH <= TILE, "tile rows must fit the buffer");
   extern __shared__ __attribute__((aligned(16))) unsigned char sfa_smem[];
-  float* s_x = (float*)(sfa_smem + NBUF * TILE);                      // [4 waves][16][64] partial logits
-  int32_t* s_rows = (int32_t*)(sfa_smem + NBUF * TILE + NW * 4096);   // [rows_per_split]
+  float* s_x = (float*)(sfa_smem + NBUF * TILE);                      // [8 waves][8][64] partial logits
+  int32_t* s_rows = (int32_t*)(sfa_smem + NBUF * TILE + NW * 2048);   // [rows_per_split]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hh = lane >> 5, l32 = lane & 31;
-  const int hg = wave & 1, half = wave >> 1;
+  const int grp = lane >> 4, l16 = lane & 15;
+  // optional phase clocks of the first workgroup's first wave (profiling)
+  const bool prof = p.dbg && blockIdx.x == 0 && blockIdx.z == 0 && tid == 0;
+  unsigned long long ph[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  unsigned long long tprev = prof ? __builtin_amdgcn_s_memtime() : 0;
+#define DSA_PHASE(i)                                             \
+  if (prof) {                                                    \
+    const unsigned long long tn = __builtin_amdgcn_s_memtime();  \
+    ph[i] += tn - tprev;                                         \
+    tprev = tn;                                                  \
+  }
+  const int hg = wave & 3, half = wave >> 2;
   // launch order L -> (token, head block): L = 16*(t/8) + 8*hb + t%8
   const int L = blockIdx.x;
   const int g = 8 * (L >> 4) + (L & 7);
@@ -119,32 +130,32 @@ __global__ __launch_bounds__(kSfaThreads, 1) void sfa_bf16_kernel(SfaParams p) {
   const int nslots = max(0, min(p.topk - slot0, p.rows_per_split));
   const int32_t* idx = p.idx + (size_t)g * p.topk + slot0;
 
-  for (int r = tid; r < nslots; r += kSfaThreads) {
+  for (int r = tid; r < nslots; r += kSfaBf16Threads) {
     const int pos = idx[r];
     s_rows[r] = (pos >= 0) ? bt[pos / P] * P + (pos % P) : -1;
   }
   __syncthreads();
   int fallback = -1;
   for (int r = 0; r < nslots && fallback < 0; r++) fallback = s_rows[r];
+  DSA_PHASE(0);
 
-  // q^T as the B operand of S^T = KV q^T (32x32x16): lane l holds head
-  // 32*hg + l%32 and dims 16*kk + 8*(l/32) .. +7 of K-step kk (this half's kk).
-  const int head = kSfaHeadsPerWG * hb + 32 * hg + l32;
+  // q^T as the B operand of S^T = KV q^T (16x16x32): lane l holds head
+  // 16*hg + l%16 and dims 288*half + 32*kk + 8*(l/16) .. +7 of K-step kk.
+  const int head = kSfaHeadsPerWG * hb + 16 * hg + l16;
   bf16x8 qb[KSH];
   {
     const bf16x8* qs = (const bf16x8*)((const uint16_t*)p.q + ((size_t)g * H + head) * DQK);
 #pragma unroll
-    for (int k = 0; k < KSH; k++) qb[k] = qs[2 * (KSH * half + k) + hh];
+    for (int k = 0; k < KSH; k++) qb[k] = qs[4 * (KSH * half + k) + grp];
   }
-  f32x16 o[MVH];
+  f32x4 o[MVH];
 #pragma unroll
-  for (int i = 0; i < MVH; i++)
-#pragma unroll
-    for (int e = 0; e < 16; e++) o[i][e] = 0.f;
+  for (int i = 0; i < MVH; i++) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   // every compiler-visible load is complete before the tile loop, so the
   // compiler's own waits never count the loop's asm-issued tile loads
   __builtin_amdgcn_s_waitcnt(0);
+  DSA_PHASE(1);
 
   const int ntiles = (fallback >= 0) ? (nslots + TR - 1) / TR : 0;
   // Row r of a tile sits at byte r * PITCH of its buffer.  The 16-byte pad
@@ -189,44 +200,51 @@ __global__ __launch_bounds__(kSfaThreads, 1) void sfa_bf16_kernel(SfaParams p) {
       DSA_WAIT_VMCNT(0);
     }
     // rows of this tile that hold a selected position (bit r)
-    const int rslot = tile * TR + l32;
-    const uint32_t valid = (uint32_t)__ballot(hh == 0 && rslot < nslots && s_rows[rslot] >= 0);
+    const int rslot = tile * TR + (lane & 31);
+    const uint32_t valid = (uint32_t)__ballot(lane < 32 && rslot < nslots && s_rows[rslot] >= 0);
+    DSA_PHASE(2);
     lds_barrier();
+    DSA_PHASE(3);
     const unsigned char* cur = sfa_smem + (tile % NBUF) * TILE;
 
-    // ---- partial S^T[row, head] over this half's dims: rows on M, heads on N;
-    // two independent accumulator chains keep the MFMA pipe busy
-    f32x16 sacc, sacc2;
-#pragma unroll
-    for (int e = 0; e < 16; e++) {
-      sacc[e] = 0.f;
-      sacc2[e] = 0.f;
-    }
+    // ---- partial S^T[row, head] over this half's dims: two 16-row M-tiles
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     {
-      const unsigned char* rp = cur + l32 * PITCH + (2 * KSH * half + hh) * 16;
+      const unsigned char* rp = cur + l16 * PITCH + (288 * half + 8 * grp) * 2;
 #pragma unroll
-      for (int k = 0; k < KSH; k += 2) {
-        const bf16x8 a0 = *(const bf16x8*)(rp + 32 * k);
-        const bf16x8 a1 = *(const bf16x8*)(rp + 32 * (k + 1));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[k], sacc, 0, 0, 0);
-        sacc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[k + 1], sacc2, 0, 0, 0);
+      for (int k = 0; k < KSH; k++) {
+        const bf16x8 a0 = *(const bf16x8*)(rp + 64 * k);
+        const bf16x8 a1 = *(const bf16x8*)(rp + 16 * PITCH + 64 * k);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[k], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[k], s1, 0, 0, 0);
       }
     }
-    sacc += sacc2;
+    float* xw = s_x + wave * 512 + lane;
 #pragma unroll
-    for (int e = 0; e < 16; e++) s_x[(wave * 16 + e) * 64 + lane] = sacc[e];
+    for (int e = 0; e < 4; e++) {
+      xw[64 * e] = s0[e];
+      xw[64 * (4 + e)] = s1[e];
+    }
+    DSA_PHASE(4);
     lds_barrier();
+    const float* xr = s_x + (wave ^ 4) * 512 + lane;
+    float z[8];
 #pragma unroll
-    for (int e = 0; e < 16; e++) sacc[e] += s_x[((wave ^ 2) * 16 + e) * 64 + lane];
+    for (int e = 0; e < 4; e++) {
+      z[e] = s0[e] + xr[64 * e];
+      z[4 + e] = s1[e] + xr[64 * (4 + e)];
+    }
 
-    // ---- online softmax for head l%32; this lane holds rows 8*(i/4) + 4*hh + i%4
+    // ---- online softmax for head l%16; this lane holds rows 4*grp + i and
+    // 16 + 4*grp + i (i < 4)
     float mt = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int r = 8 * (i / 4) + 4 * hh + (i & 3);
-      sacc[i] = ((valid >> r) & 1u) ? sacc[i] * p.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, sacc[i]);
+    for (int e = 0; e < 8; e++) {
+      const int r = 16 * (e >> 2) + 4 * grp + (e & 3);
+      z[e] = ((valid >> r) & 1u) ? z[e] * p.scale_log2 : -INFINITY;
+      mt = fmaxf(mt, z[e]);
     }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     // Lazy rescaling: the reference maximum m_run only moves when the tile's
     // maximum exceeds it by more than 8 (log2 units), so probabilities stay
@@ -245,73 +263,67 @@ __global__ __launch_bounds__(kSfaThreads, 1) void sfa_bf16_kernel(SfaParams p) {
     }
     const bool none = (m_run == -INFINITY);
     float psum = 0.f;
-    bf16x8 pb[2];
+    bf16x8 pb;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
+    for (int e = 0; e < 8; e++) {
       // the denominator sums the same bf16-rounded weights the PV product uses
-      const __bf16 pv = (__bf16)(none ? 0.f : __builtin_amdgcn_exp2f(sacc[i] - m_run));
+      const __bf16 pv = (__bf16)(none ? 0.f : __builtin_amdgcn_exp2f(z[e] - m_run));
       psum += (float)pv;
-      pb[i / 8][i % 8] = pv;
+      pb[e] = pv;
     }
     l_run = l_run * alpha + psum;
+    DSA_PHASE(5);
 
-    // ---- O^T[v, head] += V^T[v, rows] P^T[rows, head]: v on M (32), heads on N,
-    // K = 16 rows per MFMA.  K-block kb holds rows 16*kb + {4*hh + j, 8 + 4*hh + j}
-    // (j < 4) in this lane's slots, matching pb[kb].  V^T comes from
+    // ---- O^T[v, head] += V^T[v, rows] P^T[rows, head]: 16 columns on M, heads
+    // on N, K = the tile's 32 rows.  This lane's K-slots 8*grp .. +7 hold rows
+    // 4*grp + j and 16 + 4*grp + j (j < 4), matching pb.  V^T comes from
     // ds_read_b64_tr_b16: in each 16-lane group, source lane s = 4j + r reads
-    // 4 columns (vbase + 4r ..) of row j of the group's 4 rows; lane i then holds
+    // columns vbase + 4r .. +3 of row j of the group's 4 rows; lane i then holds
     // column vbase + i of those 4 rows.
     {
-      const int sl = lane & 15;
-      const int v0 = 32 * MVH * half + ((lane >> 4) & 1) * 16 + 4 * (sl & 3);   // first column loaded
+      const int r0 = 4 * grp + (l16 >> 2);
+      const unsigned char* rp0 = cur + r0 * PITCH + (256 * half + 4 * (l16 & 3)) * 2;
+      const unsigned char* rp1 = rp0 + 16 * PITCH;
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++) {
-        const int r0 = 16 * kb + 4 * hh + (sl >> 2);  // rows for the first 4 slots
-        const unsigned char* rp0 = cur + r0 * PITCH + v0 * 2;
-        const unsigned char* rp1 = rp0 + 8 * PITCH;   // rows for the last 4 slots
-#pragma unroll
-        for (int mv = 0; mv < MVH; mv++) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rp0 + 64 * mv));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rp1 + 64 * mv));
-          typedef short s16x8 __attribute__((ext_vector_type(8)));
-          const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[kb], o[mv], 0, 0, 0);
-        }
+      for (int mv = 0; mv < MVH; mv++) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rp0 + 32 * mv));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rp1 + 32 * mv));
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[mv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, o[mv], 0, 0, 0);
       }
     }
     lds_barrier();
+    DSA_PHASE(6);
   }
 
-  // ---- epilogue: o[mv][i] holds head l%32, v = 32*(MVH*half + mv) + 8*(i/4) + 4*hh + (i%4)
+  // ---- epilogue: o[mv][i] holds head l%16, v = 256*half + 16*mv + 4*grp + i
+  l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   if (p.splits == 1) {
     uint16_t* out = (uint16_t*)p.out + ((size_t)g * H + head) * DV;
 #pragma unroll
-    for (int mv = 0; mv < MVH; mv++)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        const int v = 32 * (MVH * half + mv) + 8 * q4 + 4 * hh;
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(o[mv][4 * q4] * inv) | ((uint32_t)f32_to_bf16(o[mv][4 * q4 + 1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16(o[mv][4 * q4 + 2] * inv) | ((uint32_t)f32_to_bf16(o[mv][4 * q4 + 3] * inv) << 16);
-        *(uint2*)(out + v) = pk;
-      }
-    if (p.lse && hh == 0 && half == 0)
+    for (int mv = 0; mv < MVH; mv++) {
+      const int v = 256 * half + 16 * mv + 4 * grp;
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(o[mv][0] * inv) | ((uint32_t)f32_to_bf16(o[mv][1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16(o[mv][2] * inv) | ((uint32_t)f32_to_bf16(o[mv][3] * inv) << 16);
+      *(uint2*)(out + v) = pk;
+    }
+    if (p.lse && grp == 0 && half == 0)
       p.lse[(size_t)g * H + head] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
   } else {
     float* po = p.part_o + (((size_t)g * p.splits + split) * H + head) * DV;
 #pragma unroll
-    for (int mv = 0; mv < MVH; mv++)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        const int v = 32 * (MVH * half + mv) + 8 * q4 + 4 * hh;
-        f32x4 val = {o[mv][4 * q4] * inv, o[mv][4 * q4 + 1] * inv, o[mv][4 * q4 + 2] * inv, o[mv][4 * q4 + 3] * inv};
-        *(f32x4*)(po + v) = val;
-      }
-    if (hh == 0 && half == 0)
+    for (int mv = 0; mv < MVH; mv++) *(f32x4*)(po + 256 * half + 16 * mv + 4 * grp) = o[mv] * inv;
+    if (grp == 0 && half == 0)
       p.part_ml[((size_t)g * p.splits + split) * H + head] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
   }
+  DSA_PHASE(7);
+  if (prof)
+    for (int i = 0; i < 8; i++) p.dbg[i] = ph[i];
+#undef DSA_PHASE
 }
 
 // Merge the per-range partials of one token: weights 2^(lse_j - lse).  One
@@ -475,11 +487,11 @@ hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hip
   if (p.bv.total_q == 0) return hipSuccess;
   if (dtype == kBF16 && H == 128 && Dqk == 576 && Dv == 512) {
     auto kern = sfa_bf16_kernel<576, 512>;
-    const size_t lds = 3 * 40 * 1024 + 4 * 4096 + (size_t)p.rows_per_split * 4;
+    const size_t lds = 3 * 40 * 1024 + 8 * 2048 + (size_t)p.rows_per_split * 4;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int tok8 = (p.bv.total_q + 7) / 8 * 8;
-    hipLaunchKernelGGL(kern, dim3(2 * tok8, 1, p.splits), dim3(kSfaThreads), lds, st, p);
+    hipLaunchKernelGGL(kern, dim3(2 * tok8, 1, p.splits), dim3(kSfaBf16Threads), lds, st, p);
     return hipGetLastError();
   }
   if (dtype == kF32 && H == 8 && Dqk == 80 && Dv == 64) {

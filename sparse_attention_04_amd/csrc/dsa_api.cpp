@@ -261,6 +261,37 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
   return DSA_OK;
 }
 
+dsa_status run_indexer_prefill(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out, hipStream_t st) {
+  if (b->total_q == 0) return DSA_OK;
+  if (a->q_dtype != DSA_BF16)
+    return fail(DSA_ERR_UNSUPPORTED, "the prefill indexer (more than %d query tokens per sequence) is built for bf16 only", kMaxDecodeQ);
+  if (a->topk > indexer_prefill_max_topk())
+    return fail(DSA_ERR_UNSUPPORTED, "prefill topk %d above %d", a->topk, indexer_prefill_max_topk());
+  const int P = a->k_cache->page_size;
+  if ((b->max_seq_len + P - 1) / P > indexer_prefill_max_pages())
+    return fail(DSA_ERR_UNSUPPORTED, "prefill context of %d pages above %d", (b->max_seq_len + P - 1) / P,
+                indexer_prefill_max_pages());
+  IndexerPrefillParams p{};
+  p.bv = view_of(b, P);
+  p.q = a->q;
+  p.w = a->head_weights;
+  p.k_data = a->k_cache->data;
+  p.topk = a->topk;
+  p.idx_out = idx_out;
+  p.grid = indexer_prefill_grid(b->total_q, b->batch);
+  hipError_t e = launch_indexer_prefill(dt_kernel(a->q_dtype), a->n_heads, a->head_dim, p, st);
+  if (e != hipSuccess) return hip_fail(e, "prefill indexer launch");
+  return DSA_OK;
+}
+
+// Decode-shaped batches (at most kMaxDecodeQ new tokens per sequence) use the
+// cross-workgroup decode indexer; longer query runs use the zigzag prefill one.
+dsa_status run_indexer(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out, uint32_t* ws,
+                       hipStream_t st) {
+  if (b->max_q_len <= kMaxDecodeQ) return run_indexer_decode(b, a, idx_out, ws, st);
+  return run_indexer_prefill(b, a, idx_out, st);
+}
+
 dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx, int topk,
                    void* out, float* lse, unsigned char* ws, hipStream_t st) {
   if (b->total_q == 0) return DSA_OK;
@@ -336,7 +367,7 @@ dsa_status dsa_indexer_topk(const dsa_batch* b, const dsa_indexer_args* a, int32
   if (!idx_out) return fail(DSA_ERR_INVALID_ARG, "idx_out is NULL");
   const size_t need = dsa_workspace_size(DSA_OP_INDEXER_TOPK, b, a, nullptr);
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
-  return run_indexer_decode(b, a, idx_out, (uint32_t*)ws, (hipStream_t)stream);
+  return run_indexer(b, a, idx_out, (uint32_t*)ws, (hipStream_t)stream);
 }
 
 dsa_status dsa_sparse_attn(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx, int32_t topk,
@@ -369,7 +400,7 @@ dsa_status dsa_fused_decode(const dsa_batch* b, const dsa_indexer_args* ia, cons
   const size_t ib = indexer_bytes(b);
   int32_t* idx = idx_out ? idx_out : (int32_t*)(w + ib);
   hipStream_t st = (hipStream_t)stream;
-  s = run_indexer_decode(b, ia, idx, (uint32_t*)w, st);
+  s = run_indexer(b, ia, idx, (uint32_t*)w, st);
   if (s != DSA_OK) return s;
   return run_sfa(b, sa, idx, ia->topk, out, lse, w + ib + align_up((size_t)b->total_q * ia->topk * 4, 256), st);
 }
@@ -384,8 +415,17 @@ dsa_status dsa_fused_prefill(const dsa_batch* b, const dsa_indexer_args* ia, con
   if (s != DSA_OK) return s;
   if (!out) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
   if (q_block != 64) return fail(DSA_ERR_UNSUPPORTED, "q_block must be 64 (got %d)", q_block);
-  (void)lse; (void)idx_out; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(DSA_ERR_UNSUPPORTED, "prefill path not built yet");
+  if (ia->k_cache->page_size != sa->kv_cache->page_size)
+    return fail(DSA_ERR_INVALID_ARG, "k_cache and kv_cache must share the page size (one block table)");
+  const size_t need = dsa_workspace_size(DSA_OP_FUSED_PREFILL, b, ia, sa);
+  if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  unsigned char* w = (unsigned char*)ws;
+  const size_t ib = indexer_bytes(b);
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(w + ib);
+  hipStream_t st = (hipStream_t)stream;
+  s = run_indexer_prefill(b, ia, idx, st);
+  if (s != DSA_OK) return s;
+  return run_sfa(b, sa, idx, ia->topk, out, lse, w + ib + align_up((size_t)b->total_q * ia->topk * 4, 256), st);
 }
 
 }  // extern "C"

@@ -1,0 +1,360 @@
+// Fused Lightning Indexer for causal (chunked) prefill: every new token t of a
+// sequence keeps the top n = min(k, t + 1) positions s <= t by the
+// head-weighted relevance score, without writing any score row to memory.
+//
+// Method: relevance scoring, head weighting and Top-K in one pass over the
+// paged K cache ("Deep Fusion of LI and SFA", Day0 Inference Optimization on
+// Ascend CANN, sec. 2), causal index computation whose cost grows with t, and
+// the zigzag layout that pairs a short-history block with a long-history one
+// (Adapting and Optimizing Inference for a New Model Architecture on Ascend,
+// sec. 5.2; Inference Acceleration for Next-Gen Attention Architectures,
+// sec. 5.2).  The pages pair segments across devices; here the unit is one
+// workgroup: unit u of a sequence with NB query blocks of 64 tokens owns
+// blocks u and NB-1-u, so every unit scores about the same number of (query,
+// key) pairs, and results go straight to the rows of their own tokens (the
+// "restore order" step is plain indexing).
+//
+// Inside a unit, queries are taken 4 at a time, one per wave.  64-key tiles of
+// the K cache stream through a 2-deep LDS ring shared by the 4 waves; each
+// wave scores its query against the tile with 32x32x16 MFMAs and appends the
+// keys above its current threshold to its own candidate buffer in LDS.  When a
+// buffer fills, a wave-level radix select (four 8-bit digits) keeps exactly
+// the k best, stably (so equal scores stay in position order and the smaller
+// position wins), and raises the threshold to the k-th best score.  After the
+// last tile the same select leaves the final n positions, in ascending order.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kPfThreads = 256;
+constexpr int kPfWaves = 4;
+constexpr int kQBlock = 64;         // query block of the zigzag schedule
+constexpr int kKT = 64;             // keys per tile
+constexpr int kCap = 3072;          // candidate buffer entries per query
+constexpr int kRowPitch = 128 * 2 + 16;            // LDS bytes per key row (bf16, padded)
+constexpr int kTileBytes = 20 * 1024;              // 64 rows of kRowPitch, rounded to whole loads
+constexpr int kMaxPages = 4096;                    // block-table entries staged in LDS
+
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+#define DSA_PF_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ int lane_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// Wave-level exact Top-`need` of a candidate list (keys[], pos[] of `count`
+// entries, in position order).  Four passes over 8-bit digits fix the
+// need-th largest key; entries above it are kept, and of the entries equal to
+// it the first ones in list order.  Compacts in place, stably, and returns the
+// need-th largest key.  hist: 256 words of this wave's LDS.
+__device__ uint32_t wave_select(uint32_t* keys, uint32_t* pos, int& count, int need, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0;
+  int rem = need;
+  bool whole_bin = false;
+  for (int pass = 0; pass < 4 && !whole_bin; pass++) {
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int j = 0; j < 4; j++) hist[4 * lane + j] = 0u;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS writes of this wave done (lgkmcnt(0))
+    for (int i = lane; i < count; i += 64) {
+      const uint32_t x = keys[i];
+      if ((x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    // lane l owns bins 4l .. 4l+3; suffix sums from the top bin down
+    uint32_t h[4];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      h[j] = hist[4 * lane + j];
+      c += (int)h[j];
+    }
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_down(x, o);
+      if (lane + o < 64) x += v;
+    }
+    const int above = x - c;   // entries in bins above this lane's four
+    int bin = -1, binabove = 0, bincnt = 0;
+    if (above < rem && rem <= above + c) {
+      int run = above;
+      for (int j = 3; j >= 0; j--) {
+        if (run + (int)h[j] >= rem) {
+          bin = 4 * lane + j;
+          binabove = run;
+          bincnt = (int)h[j];
+          break;
+        }
+        run += (int)h[j];
+      }
+    }
+    const uint64_t m = __ballot(bin >= 0);
+    const int src = m ? (__ffsll((unsigned long long)m) - 1) : 0;
+    bin = __shfl(bin, src);
+    binabove = __shfl(binabove, src);
+    bincnt = __shfl(bincnt, src);
+    if (bin < 0) bin = 0;  // cannot happen for need <= count
+    rem -= binabove;
+    prefix |= (uint32_t)bin << shift;
+    pmask |= 0xFFu << shift;
+    whole_bin = (bincnt == rem);
+  }
+  // stable in-place compaction: above the prefix, or equal and among the
+  // first `rem` equal ones
+  int out = 0, ties = 0;
+  for (int i0 = 0; i0 < count; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t x = (i < count) ? keys[i] : 0u;
+    const uint32_t ps = (i < count) ? pos[i] : 0u;
+    const bool in = i < count;
+    const bool gt = in && (x & pmask) > prefix;
+    const bool eq = in && (x & pmask) == prefix;
+    const uint64_t me = __ballot(eq);
+    const bool keep = gt || (eq && (whole_bin || ties + lane_rank(me) < rem));
+    const uint64_t mk = __ballot(keep);
+    const int r = out + lane_rank(mk);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // every lane has read before anyone writes
+    if (keep) {
+      keys[r] = x;
+      pos[r] = ps;
+    }
+    out += __popcll(mk);
+    ties += __popcll(me);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  count = out;
+  // the need-th largest key is the smallest kept one
+  uint32_t mn = 0xFFFFFFFFu;
+  for (int i = lane; i < out; i += 64) mn = min(mn, keys[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+  return mn;
+}
+
+template <int H, int D>
+__global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerPrefillParams p) {
+  static_assert(H == 64 && D == 128, "prefill indexer is compiled for 64 heads x 128");
+  constexpr int MT = H / 32;        // M-tiles over heads
+  constexpr int KS = D / 16;        // K-steps of 16
+  constexpr int LPW = kTileBytes / 1024 / kPfWaves;   // 1-KiB loads per wave per tile (5)
+  extern __shared__ __attribute__((aligned(16))) unsigned char pf_smem[];
+  unsigned char* ring = pf_smem;                                              // 2 tiles
+  uint32_t* cand = (uint32_t*)(pf_smem + 2 * kTileBytes);                     // [4][2][kCap]
+  uint32_t* hist = cand + kPfWaves * 2 * kCap;                                // [4][256]
+  int32_t* s_bt = (int32_t*)(hist + kPfWaves * 256);                          // [kMaxPages]
+  __shared__ int s_unit[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const BatchView& bv = p.bv;
+  const int P = bv.page_size;
+  const int K = p.topk;
+
+  // ---- unit -> (sequence, first block): sequence b has NB_b = ceil(T_b/64)
+  // blocks and ceil(NB_b/2) units; unit u owns blocks u and NB_b-1-u.
+  if (wave == 0) {
+    int acc = 0, found = 0;
+    for (int b0 = 0; b0 < bv.batch && !found; b0 += 64) {
+      const int b = b0 + lane;
+      int nu = 0;
+      if (b < bv.batch) {
+        const int T = bv.cu_q[b + 1] - bv.cu_q[b];
+        const int nb = (T + kQBlock - 1) / kQBlock;
+        nu = (nb + 1) / 2;
+      }
+      int inc = nu;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+      }
+      const int start = acc + inc - nu;
+      const bool mine = b < bv.batch && (int)blockIdx.x >= start && (int)blockIdx.x < start + nu;
+      const uint64_t m = __ballot(mine);
+      if (m) {
+        if (lane == __ffsll((unsigned long long)m) - 1) {
+          s_unit[0] = b;
+          s_unit[1] = (int)blockIdx.x - start;
+        }
+        found = 1;
+      }
+      acc += __shfl(inc, 63);
+    }
+    if (lane == 0 && !found) s_unit[0] = -1;
+  }
+  __syncthreads();
+  const int b = s_unit[0];
+  if (b < 0) return;
+  const int u = s_unit[1];
+  const int L = bv.seq_lens[b];
+  const int tok0 = bv.cu_q[b];
+  const int T = bv.cu_q[b + 1] - tok0;
+  const int NB = (T + kQBlock - 1) / kQBlock;
+  // the sequence's block-table row, staged once (page lookups stay on chip)
+  {
+    const int* btg = bv.block_table + (size_t)b * bv.max_pages;
+    const int npg = min((L + P - 1) / P, kMaxPages);
+    for (int i = tid; i < npg; i += kPfThreads) s_bt[i] = btg[i];
+  }
+  __syncthreads();
+  const int* bt = s_bt;
+  const int blocks[2] = {u, NB - 1 - u};
+  const int nblk = (blocks[1] != blocks[0]) ? 2 : 1;
+
+  uint32_t* ckey = cand + (size_t)wave * 2 * kCap;
+  uint32_t* cpos = ckey + kCap;
+  uint32_t* whist = hist + wave * 256;
+
+  for (int bi = 0; bi < nblk; bi++) {
+    const int q0 = blocks[bi] * kQBlock;
+    const int q1 = min(T, q0 + kQBlock);
+    for (int qg = q0; qg < q1; qg += kPfWaves) {
+      const int q = qg + wave;                  // this wave's query (may be >= q1)
+      const bool have_q = q < q1;
+      const int t = L - T + (have_q ? q : q1 - 1);
+      const int tmax = L - T + min(q1, qg + kPfWaves) - 1;   // last position any wave needs
+      int32_t* row = p.idx_out + (size_t)(tok0 + (have_q ? q : 0)) * K;
+      // queries that keep every visible position need no scores
+      const bool all_keep = have_q && (t + 1 <= K);
+      if (all_keep) {
+        for (int s = lane; s < K; s += 64) row[s] = (s <= t) ? s : -1;
+      }
+      const bool groups_all_keep = (tmax + 1 <= K);  // uniform: every wave's t <= tmax
+      if (groups_all_keep) continue;
+
+      // query operands in the 32x32 layout: lane half h holds dims [64h, 64h+64)
+      bf16x8 a[MT][KS];
+      float wr[MT][16];
+      {
+        const int qq = have_q ? q : q1 - 1;
+        const uint16_t* qp = (const uint16_t*)p.q + (size_t)(tok0 + qq) * H * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+          const bf16x8* src = (const bf16x8*)(qp + (size_t)(32 * mt + (lane & 31)) * D + (lane >> 5) * (D / 2));
+#pragma unroll
+          for (int kk = 0; kk < KS; kk++) a[mt][kk] = src[kk];
+#pragma unroll
+          for (int i = 0; i < 16; i++)
+            wr[mt][i] = p.w[(size_t)(tok0 + qq) * H + 32 * mt + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3)];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      int count = 0;
+      uint32_t thr = 0u;    // keys must exceed this to become candidates
+      const int nt = (tmax + 1 + kKT - 1) / kKT;
+      auto issue = [&](int tile) {
+        unsigned char* buf = ring + (tile & 1) * kTileBytes;
+#pragma unroll
+        for (int k = 0; k < LPW; k++) {
+          const int off = (wave + kPfWaves * k) * 1024 + lane * 16;
+          const int r = off / kRowPitch, c = (off % kRowPitch) / 16;
+          const bool real = r < kKT && c < (D * 2) / 16;
+          int s = tile * kKT + (real ? r : 0);
+          s = min(s, tmax);
+          const int64_t prow = (int64_t)bt[s / P] * P + (s % P);
+          const unsigned char* src = (const unsigned char*)p.k_data + prow * (D * 2) + (real ? c * 16 : 0);
+          dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(buf + (wave + kPfWaves * k) * 1024)));
+        }
+      };
+      issue(0);
+      for (int tile = 0; tile < nt; tile++) {
+        if (tile + 1 < nt) {
+          issue(tile + 1);
+          DSA_PF_WAIT_VMCNT(LPW);
+        } else {
+          DSA_PF_WAIT_VMCNT(0);
+        }
+        lds_barrier();
+        const unsigned char* cur = ring + (tile & 1) * kTileBytes;
+        // ---- scores of the 64 keys of this tile for this wave's query
+        float sc[2];
+#pragma unroll
+        for (int n = 0; n < 2; n++) {
+          f32x16 acc[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[mt][e] = 0.f;
+          const unsigned char* kp = cur + (32 * n + (lane & 31)) * kRowPitch + (lane >> 5) * D;
+#pragma unroll
+          for (int kk = 0; kk < KS; kk++) {
+            const bf16x8 kb = *(const bf16x8*)(kp + 16 * kk);
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+              acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], kb, acc[mt], 0, 0, 0);
+          }
+          float s = 0.f;
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[mt][i], s);
+          sc[n] = s + __shfl_xor(s, 32);
+        }
+        lds_barrier();   // the tile buffer may be refilled from here on
+        // lane l takes key tile*64 + l: N-tile l/32, column l%32
+        const int spos = tile * kKT + lane;
+        const float v = (lane < 32) ? sc[0] : sc[1];
+        const uint32_t x = (have_q && spos <= t) ? float_key(v) : 0u;
+        bool cnd = x > thr;
+        uint64_t m = __ballot(cnd);
+        if (count + __popcll(m) > kCap) {
+          thr = wave_select(ckey, cpos, count, K, whist);
+          cnd = x > thr;
+          m = __ballot(cnd);
+        }
+        if (cnd) {
+          const int r = count + lane_rank(m);
+          ckey[r] = x;
+          cpos[r] = (uint32_t)spos;
+        }
+        count += __popcll(m);
+      }
+      if (have_q && !all_keep) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        if (count > K) wave_select(ckey, cpos, count, K, whist);
+        // count == K here (t + 1 > K keys were visible); positions ascend
+        for (int i = lane; i < K; i += 64) row[i] = (i < count) ? (int32_t)cpos[i] : -1;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace
+
+size_t indexer_prefill_lds_bytes() {
+  return 2 * (size_t)kTileBytes + (size_t)kPfWaves * 2 * kCap * 4 + kPfWaves * 256 * 4 + kMaxPages * 4;
+}
+
+int indexer_prefill_max_pages() { return kMaxPages; }
+int indexer_prefill_max_topk() { return kCap - 64; }
+
+int indexer_prefill_grid(int total_q, int batch) {
+  const int blocks = (total_q + kQBlock - 1) / kQBlock + batch;   // >= sum of ceil(T_b/64)
+  return (blocks + batch + 1) / 2;                                // >= sum of ceil(NB_b/2)
+}
+
+hipError_t launch_indexer_prefill(int dtype, int H, int D, const IndexerPrefillParams& p, hipStream_t st) {
+  if (dtype != kBF16 || H != 64 || D != 128) return hipErrorInvalidValue;
+  if (p.grid <= 0) return hipSuccess;
+  auto kern = indexer_prefill_kernel<64, 128>;
+  const size_t lds = indexer_prefill_lds_bytes();
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kPfThreads), lds, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -41,6 +41,22 @@ hipError_t launch_indexer_decode(int dtype, int H, int D, int maxq, const Indexe
                                  hipStream_t st);
 hipError_t launch_zero(uint32_t* p, size_t nwords, hipStream_t st);
 
+struct IndexerPrefillParams {
+  BatchView bv;
+  const void* q;           // [total_q][H][D] bf16
+  const float* w;          // [total_q][H]
+  const void* k_data;      // [num_pages][P][D] bf16
+  int32_t topk;
+  int32_t* idx_out;        // [total_q][topk]
+  int32_t grid;            // workgroups launched (>= number of zigzag units)
+};
+
+size_t indexer_prefill_lds_bytes();
+int indexer_prefill_grid(int total_q, int batch);
+int indexer_prefill_max_pages();
+int indexer_prefill_max_topk();
+hipError_t launch_indexer_prefill(int dtype, int H, int D, const IndexerPrefillParams& p, hipStream_t st);
+
 // ------------------------------------------------------------------- SFA ---
 
 // (dtype, H_S, Dqk, Dv) instantiations of SFA.

@@ -187,3 +187,87 @@ def test_fused_equals_composition():
     assert torch.equal(torch.sort(idx, 1).values, torch.sort(idx_f, 1).values)
     out, _ = call.sparse_attn(idx_f)
     assert torch.allclose(out.float(), out_f.float(), atol=1e-6)
+
+
+# ------------------------------------------------------------------ prefill ---
+
+def _sample_prefill_queries(case, per_seq=40, seed=0):
+    """Block edges, the k boundary, the first and last tokens, plus random ones."""
+    r = np.random.default_rng(seed)
+    qs = []
+    for b in range(case.batch):
+        T = int(case.q_lens_host[b])
+        L = int(case.seq_lens_host[b])
+        cand = {0, T - 1, min(T - 1, 63), min(T - 1, 64), T // 2}
+        for i in range(T):
+            t = L - T + i
+            if t in (case.topk - 2, case.topk - 1, case.topk, case.topk + 1, 3071, 3072, 3073):
+                cand.add(i)
+        cand |= set(r.integers(0, T, per_seq).tolist())
+        qs += [(b, i) for i in sorted(cand) if 0 <= i < T]
+    return qs
+
+
+def _run_prefill(case, queries):
+    call = B.Call(case)
+    _say(f"{case.name} seed={case.seed} B={case.batch} L={list(case.seq_lens_host[:4])} "
+         f"T={list(case.q_lens_host[:4])} k={case.topk}: fused_prefill")
+    out, lse, idx = call.fused_prefill()
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    for (b, i) in queries:
+        ref = oracle.run_query(case, b, i)
+        check_topk_row(idx_h[case.token(b, i)], ref, case.topk)
+    _check_sfa_on(case, out, queries, idx_h)
+    return idx_h
+
+
+def test_prefill_compaction_small_k():
+    # 5000 keys with k = 256: candidate buffers overflow and are compacted
+    case = case_to(make_case("c3_prefill_bf16", 21, seq_len_range=(5000, 5000), q_len=5000, topk=256), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=60))
+
+
+def test_prefill_full_k_ragged_tail():
+    # k = 2048 over 4133 keys: ragged last query block and last page
+    case = case_to(make_case("c3_prefill_bf16", 22, seq_len_range=(4133, 4133), q_len=4133), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=40))
+
+
+def test_chunked_prefill_after_cache():
+    # a 700-token chunk appended after 5300 cached tokens (every t >= 5300)
+    case = case_to(make_case("c5_chunk_prefill", 23, seq_len_range=(6000, 6000), q_len=700, batch=2), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=25))
+
+
+def test_prefill_mixed_batch_zigzag_units():
+    # sequences with different numbers of query blocks (odd, even, one) share a launch
+    case = case_to(make_case("c3_prefill_bf16", 24, batch=3, seq_lens=[3000, 2100, 4100], q_lens=[130, 64, 257],
+                             topk=512), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=20))
+
+
+def test_prefill_equal_scores():
+    case = make_case("c3_prefill_bf16", 25, seq_len_range=(3500, 3500), q_len=300, topk=1024)
+    case.k_pool[:] = case.k_pool[0, 0]
+    case = case_to(case, "cuda")
+    call = B.Call(case)
+    _say("prefill equal scores")
+    _, _, idx = call.fused_prefill()
+    idx = idx.cpu().numpy()
+    for i in range(300):
+        assert np.array_equal(np.sort(idx[i]), np.arange(1024)), i
+
+
+def test_c3_full_size_sampled():
+    """The 32768-token causal prefill at full size, checked on sampled queries
+    and, for every query, on the properties of its index row."""
+    _say("c3 full size: generating on device")
+    case = make_case("c3_prefill_bf16", 3, device="cuda")
+    qs = [(0, i) for i in (0, 2047, 2048, 2049, 9000, 20000, 32767)]
+    idx_h = _run_prefill(case, qs)
+    t = np.arange(case.total_q)
+    n = np.minimum(case.topk, t + 1)
+    valid = idx_h >= 0
+    assert np.array_equal(valid.sum(1), n)
+    assert np.all(np.where(valid, idx_h <= t[:, None], True))

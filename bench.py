@@ -120,6 +120,8 @@ def main():
     ap.add_argument("--workload", default="c2_decode_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--sets", type=int, default=4, help="value sets rotated between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--no-ctx32k", dest="ctx32k", action="store_false",
+                    help="skip the extra all-32k-context measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -205,6 +207,17 @@ def main():
             "sfa": a["sfa_flops"] / (ms_sfa * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[case.sfa_dtype],
         },
     }
+    if args.workload == "c2_decode_bf16" and args.ctx32k:
+        # the same step with every context at 32768 tokens ("at 32k ctx")
+        c32 = [B.Call(make_case("c2_decode_bf16_32k", seed, device="cuda", value_seed=seed + 100 * r))
+               for r in range(args.sets)]
+        for c in c32:
+            c.workspace(B.DSA_OP_FUSED_DECODE)
+        ms32 = time_calls(lambda s: c32[s % len(c32)].fused_decode(), args.steps, args.warmup, torch)
+        a32 = algorithmic(c32[0].case)
+        line["ctx32k"] = {"us_per_step": ms32 * 1e3, "tokens_per_s": c32[0].case.total_q / (ms32 * 1e-3),
+                          "step_hbm_frac": a32["fused_bytes"] / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del c32
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(line), flush=True)

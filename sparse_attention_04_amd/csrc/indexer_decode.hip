@@ -22,8 +22,9 @@
 //      tie counts hands the remaining slots to the smallest positions;
 //   4. each workgroup appends its selected positions to the query's output row.
 //
-// All workgroups of a launch are co-resident (cooperative launch), every wait
-// is bounded (group_barrier), and the grid always drains.
+// All workgroups of a launch are co-resident (the grid is sized from the
+// occupancy of the kernel), every wait is bounded (group_barrier), and the grid
+// always drains.
 #include "common.h"
 #include "kernels.h"
 
@@ -644,13 +645,17 @@ struct MfmaScorer<kF32, H, D> {
 
 // ------------------------------------------------------------------ launch ---
 
+// The grid never exceeds what the device holds at once (the host sizes it from
+// the occupancy query), and kernels on one stream run one after another, so
+// every workgroup of a sequence is resident while its peers wait at a barrier.
+// A plain launch therefore suffices; the bounded waits remain the safety net.
 template <int DT, int H, int D, int MAXQ>
 static hipError_t launch_one(const IndexerDecodeParams& p, size_t lds, hipStream_t st) {
   auto kern = indexer_decode_kernel<DT, H, D, MAXQ>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  void* args[] = {(void*)&p};
-  return hipLaunchCooperativeKernel((const void*)kern, dim3(p.grid), dim3(kIdxThreads), args, (unsigned)lds, st);
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kIdxThreads), lds, st, p);
+  return hipGetLastError();
 }
 
 int indexer_decode_max_q() { return kMaxDecodeQ; }

@@ -35,7 +35,7 @@ dsa_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxGrid = 2048;           // workspace is sized for up to this many indexer workgroups
-constexpr int kSfaTargetWG = 512;        // SFA workgroups aimed for when splitting index rows
+constexpr int kSfaTargetWG = 256;        // SFA workgroups aimed for (one per compute unit) when splitting index rows
 constexpr int kSfaRowTile = 32;
 constexpr size_t kLdsMax = 160 * 1024;
 

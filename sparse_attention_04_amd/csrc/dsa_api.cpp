@@ -37,6 +37,7 @@ dsa_status hip_fail(hipError_t e, const char* what) {
 constexpr int kMaxGrid = 2048;           // workspace is sized for up to this many indexer workgroups
 constexpr int kSfaTargetWG = 256;        // SFA workgroups aimed for (one per compute unit) when splitting index rows
 constexpr int kSfaRowTile = 32;
+constexpr int kSfaMaxRows = 2048;       // index slots one SFA workgroup stages in LDS
 constexpr size_t kLdsMax = 160 * 1024;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -133,9 +134,14 @@ struct SfaPlan {
 
 SfaPlan plan_sfa(const dsa_batch* b, int H, int Dv, int topk, bool bf16) {
   SfaPlan pl{};
-  const int hg = bf16 ? std::max(1, H / 64) : 1;
-  const int64_t units = std::max<int64_t>(1, (int64_t)b->total_q * hg);
+  // A workgroup serves one (token, range of index slots) with all heads.
+  // With few tokens the slot ranges are split until about kSfaTargetWG
+  // workgroups exist.  Ranges are multiples of the row tile and hold at most
+  // kSfaMaxRows slots.
+  (void)bf16;
+  const int64_t units = std::max<int64_t>(1, (int64_t)b->total_q);
   int splits = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(1, topk / 64), kSfaTargetWG / units));
+  splits = std::max(splits, (topk + kSfaMaxRows - 1) / kSfaMaxRows);
   int rps = (int)align_up((size_t)((topk + splits - 1) / splits), kSfaRowTile);
   splits = (topk + rps - 1) / rps;
   pl.splits = splits;
@@ -306,6 +312,11 @@ dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
   p.splits = pl.splits;
   p.rows_per_split = pl.rows_per_split;
+  // Launches with fewer query tokens than workgroup slots (decode) are bound
+  // by memory and latency, so the matrix units can afford the weight
+  // residuals; large prefill launches are bound by the matrix units and use
+  // bf16 weights (error <= 2^-9 max|V|).
+  p.precise_weights = (int64_t)b->total_q < kSfaTargetWG ? 1 : 0;
   p.out = out;
   p.lse = lse;
   p.part_o = (float*)ws;

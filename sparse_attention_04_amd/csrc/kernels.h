@@ -71,7 +71,8 @@ struct SfaParams {
   const int32_t* idx;      // [total_q][topk]
   int32_t topk;
   float scale_log2;        // softmax_scale * log2(e)
-  int32_t splits;          // row splits per (token, head group)
+  int32_t splits;          // ranges of index slots per token
+  int32_t precise_weights; // bf16: also multiply in the bf16 rounding residuals of the weights
   int32_t rows_per_split;  // multiple of the row tile
   void* out;               // splits == 1: final [total_q][H][Dv] in q dtype
   float* lse;              // splits == 1: [total_q][H] (natural log) or null

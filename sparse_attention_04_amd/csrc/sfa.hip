@@ -10,11 +10,11 @@
 // columns and V is the first Dv columns of the same row.
 //
 // bf16 kernel (H = 128, Dqk = 576, Dv = 512): a workgroup owns one query token,
-// a group of 64 heads and a contiguous range of index slots.  Per tile of 32
-// slots it gathers the 32 latent rows through the block table into LDS
-// (double-buffered), then every wave (16 heads) computes
+// all of its heads and a contiguous range of index slots.  Per tile of 32
+// slots it gathers the 32 latent rows through the block table into LDS (a
+// 3-deep ring), then every wave (32 heads) computes
 //   S^T[row, head] = KV[row, :] . q[head, :]     (16x16x32 bf16 MFMAs, rows on M)
-// so that after the online-softmax update the probabilities already sit in the
+// so that after the softmax weights are formed the probabilities already sit in the
 // B-operand layout of the second product
 //   O^T[v, head] += V^T[v, row] P^T[row, head]   (V^T read with ds_read_b64_tr_b16).
 // Slots holding -1 are masked.  With several slot ranges per token, each range
@@ -25,8 +25,6 @@
 namespace dsa {
 
 namespace {
-
-constexpr int kSfaThreads = 256;
 
 __device__ __forceinline__ int find_seq(const BatchView& bv, int tok) {
   // largest b with cu_q[b] <= tok (binary search over cu_q[0..batch])
@@ -63,48 +61,100 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima): gfx9 encoding.
 #define DSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-constexpr int kSfaHeadsPerWG = 64;
-constexpr int kSfaBf16Threads = 512;
+// LDS operand loads of the MFMA loops, issued through inline assembly so that
+// the compiler neither hoists all of them at once (which would need more
+// registers than a wave has) nor waits on them early.  Each result is used
+// only after lds_wait<N>() has taken it as an operand, which orders the use
+// after the wait; N counts the LDS loads issued after it (they complete in
+// order).
+// (The byte offset OFF is an immediate, so one address register serves a
+// whole loop.)
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  bf16x8 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ s16x4 lds_read_tr16_b64(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  s16x4 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8& a, bf16x8& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(s16x4& a, s16x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
 
 // bf16 SFA, H = 128, Dqk = 576, Dv = 512.
 //
-// A workgroup serves 64 heads of one token and one range of index slots with
-// 8 waves (two per SIMD): wave w takes the 16 heads 16*(w%4) .. +15 of the
-// group together with its partner w ^ 4.  The pair splits the QK^T
-// contraction (half = w/4 takes dims [288*half, 288*half + 288)) and exchanges
-// the 32x16 partial logits through LDS, then splits the PV columns (half takes
-// v in [256*half, 256*half + 256)).  Per wave that is q^T in 36 registers and
-// the O^T accumulators in 64.  The two head groups of a token run as
-// workgroups 8 apart in launch order, which places them on the same XCD, so
-// the second gather of each row hits that XCD's L2.
+// A workgroup serves all 128 heads of one token for one range of index slots,
+// with 4 waves, one per SIMD, so each wave may use the whole register file.
+// Wave w owns the 32 heads 32w .. 32w+31 as two 16-head groups ht: q^T for
+// all 576 dims stays in registers (144 VGPRs) and the O^T accumulators for all
+// 512 columns (256) live in the accumulation registers.  Each K/V operand read
+// from LDS feeds both head groups, and a gathered row is brought on chip once
+// per token and range.
 //
 // Per tile of 32 index slots:
 //   S^T[row, head] = KV[row, :] . q[head, :]     16x16x32 bf16 MFMAs, rows on M
-//   online softmax per head (lazy rescaling, see below)
+//   softmax weights against a fixed reference (see below)
 //   O^T[v, head] += V^T[v, row] P^T[row, head]   V^T read with ds_read_b64_tr_b16
-// The probabilities leave the first product already in the B-operand layout
-// of the second.  Rows stream through a 3-deep ring of LDS tiles filled by
-// direct global->LDS loads; slots holding -1 are masked.
+// The weights leave the first product already in the B-operand layout of the
+// second, rounded to bf16, which bounds their contribution to the output
+// error by 2^-9 max|V|.  With LO the wave also multiplies in the rounding
+// residuals (a second bf16 part), so the weights enter to ~2^-17 relative; it
+// costs the PV product twice the MFMAs and is used where the launch is bound
+// by memory rather than by the matrix units (few query tokens).  Rows stream
+// through a 4-deep ring of LDS tiles filled by direct global->LDS loads; slots
+// holding -1 are masked.
+constexpr int kSfaBf16Threads = 256;
+constexpr int kSfaMaxRows = 2048;          // index slots per workgroup (LDS row table)
+constexpr float kSfaRefMargin = 40.f;      // softmax reference above the first tile maximum (log2 units)
+
 template <int DQK, int DV>
+struct SfaBf16Geom {
+  static constexpr int ROWB = DQK * 2;               // bytes of one latent row (1152)
+  static constexpr int PITCH = ROWB + 32;            // LDS bytes per row (74 chunks of 16 B)
+  static constexpr int TR = 32;                      // rows per tile
+  static constexpr int NW = kSfaBf16Threads / 64;    // 4 waves
+  static constexpr int LOADS = (TR * PITCH + 1023) / 1024;  // 1-KiB loads per tile (37)
+  static constexpr int LPW = (LOADS + NW - 1) / NW;  // loads of wave 0 per tile (10)
+  static constexpr int TILE = LOADS * 1024;          // LDS bytes per tile buffer
+  static constexpr int NBUF = 4;                     // tiles in flight
+  static_assert(LOADS % NW == 1, "wave 0 issues one load more than the others");
+  static constexpr size_t lds_bytes(int rows) { return (size_t)NBUF * TILE + (size_t)rows * 4; }
+};
+
+template <int DQK, int DV, bool LO>
 __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams p) {
-  constexpr int ROWB = DQK * 2;              // bytes of one latent row (1152)
-  constexpr int PITCH = ROWB + 16;           // LDS bytes per row (73 chunks of 16 B)
-  constexpr int TR = 32;                     // rows per tile
-  constexpr int TILE = 40 * 1024;            // 32 rows of PITCH bytes, rounded up to whole loads
-  constexpr int NBUF = 3;                    // tiles in flight
-  constexpr int NW = kSfaBf16Threads / 64;   // 8 waves
-  constexpr int LPW = TILE / 1024 / NW;      // 1-KiB load instructions per wave per tile (5)
-  constexpr int KSH = DQK / 32 / 2;          // QK^T K-steps of 32 per wave (9)
-  constexpr int MVH = DV / 16 / 2;           // PV M-tiles of 16 columns per wave (16)
-  static_assert(TILE % (1024 * NW) == 0, "tile must split into whole 1-KiB loads per wave");
-  static_assert(TR * PITCH <= TILE, "tile rows must fit the buffer");
+  using G = SfaBf16Geom<DQK, DV>;
+  constexpr int ROWB = G::ROWB, PITCH = G::PITCH, TR = G::TR, TILE = G::TILE, NBUF = G::NBUF;
+  constexpr int NW = G::NW, LPW = G::LPW;
+  constexpr int KS = DQK / 32;               // QK^T K-steps of 32 (18)
+  constexpr int MV = DV / 16;                // PV M-tiles of 16 columns (32)
+  constexpr int H = 128;
   extern __shared__ __attribute__((aligned(16))) unsigned char sfa_smem[];
-  float* s_x = (float*)(sfa_smem + NBUF * TILE);                      // [8 waves][8][64] partial logits
-  int32_t* s_rows = (int32_t*)(sfa_smem + NBUF * TILE + NW * 2048);   // [rows_per_split]
+  int32_t* s_rows = (int32_t*)(sfa_smem + NBUF * TILE);   // [rows_per_split]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, l16 = lane & 15;
-  // optional phase clocks of the first workgroup's first wave (profiling)
+  // Optional phase clocks of the first workgroup's first wave, compiled in
+  // only with DSA_SFA_PHASES (they cost registers the tile loop needs).
+#ifdef DSA_SFA_PHASES
   const bool prof = p.dbg && blockIdx.x == 0 && blockIdx.z == 0 && tid == 0;
   unsigned long long ph[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   unsigned long long tprev = prof ? __builtin_amdgcn_s_memtime() : 0;
@@ -114,16 +164,17 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     ph[i] += tn - tprev;                                         \
     tprev = tn;                                                  \
   }
-  const int hg = wave & 3, half = wave >> 2;
-  // launch order L -> (token, head block): L = 16*(t/8) + 8*hb + t%8
-  const int L = blockIdx.x;
-  const int g = 8 * (L >> 4) + (L & 7);
-  const int hb = (L >> 3) & 1;
+#else
+#define DSA_PHASE(i)
+#endif
+  // Workgroup L runs on XCD L % 8 (round-robin dispatch); each XCD takes a
+  // contiguous run of tokens, and all slot ranges of a token share one XCD.
+  const int chunk = gridDim.x / 8;
+  const int g = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
   const int split = blockIdx.z;
   if (g >= p.bv.total_q) return;
   const BatchView& bv = p.bv;
   const int P = bv.page_size;
-  const int H = 2 * kSfaHeadsPerWG;
   const int b = find_seq(bv, g);
   const int* bt = bv.block_table + (size_t)b * bv.max_pages;
   const int slot0 = split * p.rows_per_split;
@@ -137,192 +188,240 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
   __syncthreads();
   int fallback = -1;
   for (int r = 0; r < nslots && fallback < 0; r++) fallback = s_rows[r];
+  const int ntiles = (fallback >= 0) ? (nslots + TR - 1) / TR : 0;
   DSA_PHASE(0);
 
-  // q^T as the B operand of S^T = KV q^T (16x16x32): lane l holds head
-  // 16*hg + l%16 and dims 288*half + 32*kk + 8*(l/16) .. +7 of K-step kk.
-  const int head = kSfaHeadsPerWG * hb + 16 * hg + l16;
-  bf16x8 qb[KSH];
-  {
-    const bf16x8* qs = (const bf16x8*)((const uint16_t*)p.q + ((size_t)g * H + head) * DQK);
+  // Row r of a tile sits at byte r * PITCH of its buffer.  With the 32-byte
+  // pad both read patterns below (16 rows x 16 bytes per K-step, and the
+  // transposing reads of 16 rows x 32 bytes) measured free of LDS bank
+  // conflicts on this part.  Load c (< LOADS) of a tile fills bytes
+  // 1024c .. +1023 of its buffer and is issued by wave c % NW (wave 0 issues
+  // LPW loads, the others LPW - 1); lanes that land on a pad or past row 31
+  // load chunk 0 of the tile's row 0.
+  const int nld = (wave == 0) ? LPW : LPW - 1;
+  auto issue = [&](int tile) {
+    unsigned char* buf = sfa_smem + (tile % NBUF) * TILE;
+    // recomputed per tile (cheap ALU) rather than held in registers across
+    // the loop: the lane's byte offset is hidden from loop-invariant hoisting
+    int lo = lane * 16;
+    asm volatile("" : "+v"(lo));
+    int rows[LPW], cols[LPW];
 #pragma unroll
-    for (int k = 0; k < KSH; k++) qb[k] = qs[4 * (KSH * half + k) + grp];
+    for (int k = 0; k < LPW; k++) {
+      const int off = (wave + NW * k) * 1024 + lo;
+      const int r = off / PITCH, c = off - r * PITCH;
+      const bool real = r < TR && c < ROWB;
+      const int slot = tile * TR + (real ? r : 0);
+      rows[k] = (slot < nslots && k < nld) ? s_rows[slot] : -1;
+      cols[k] = real ? c : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < LPW; k++) {
+      if (k < LPW - 1 || wave == 0) {
+        const int row = (rows[k] < 0) ? fallback : rows[k];
+        const unsigned char* src = (const unsigned char*)p.kv + (size_t)row * ROWB + cols[k];
+        dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(buf + (wave + NW * k) * 1024)));
+      }
+    }
+  };
+  // the first tiles' loads overlap the q load below
+  for (int t = 0; t < NBUF - 1 && t < ntiles; t++) issue(t);
+
+  // q^T as the B operand of S^T = KV q^T (16x16x32): for head group ht, lane l
+  // holds head 32*wave + 16*ht + l%16 and dims 32*k + 8*(l/16) .. +7 of K-step k.
+  const int head0 = 32 * wave + l16;
+  bf16x8 qb[2][KS];
+#pragma unroll
+  for (int ht = 0; ht < 2; ht++) {
+    const bf16x8* qs = (const bf16x8*)((const uint16_t*)p.q + ((size_t)g * H + head0 + 16 * ht) * DQK);
+#pragma unroll
+    for (int k = 0; k < KS; k++) qb[ht][k] = qs[4 * k + grp];
   }
-  f32x4 o[MVH];
+  f32x4 o[2][MV];
 #pragma unroll
-  for (int i = 0; i < MVH; i++) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  // every compiler-visible load is complete before the tile loop, so the
-  // compiler's own waits never count the loop's asm-issued tile loads
+  for (int ht = 0; ht < 2; ht++)
+#pragma unroll
+    for (int i = 0; i < MV; i++) o[ht][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // Every compiler-visible load is complete before the tile loop, so the
+  // compiler's own waits never count the loop's asm-issued tile loads.  (This
+  // also waits for the first tiles, which the first iterations need anyway.)
   __builtin_amdgcn_s_waitcnt(0);
   DSA_PHASE(1);
 
-  const int ntiles = (fallback >= 0) ? (nslots + TR - 1) / TR : 0;
-  // Row r of a tile sits at byte r * PITCH of its buffer.  The 16-byte pad
-  // makes consecutive rows start 9 bank groups apart (73 = 9 mod 16), so 16
-  // rows read at one column, and 4 rows x 2 chunks read by the transposing
-  // loads, hit distinct banks.  Each wave fills whole 1-KiB stretches of the
-  // buffer; lanes that land on a pad or on the slack after row 31 load chunk 0
-  // of the tile's row 0.
-  int ld_row[LPW], ld_col[LPW];
-#pragma unroll
-  for (int k = 0; k < LPW; k++) {
-    const int off = (wave + NW * k) * 1024 + lane * 16;
-    const int r = off / PITCH, c = (off % PITCH) / 16;
-    const bool real = r < TR && c < ROWB / 16;
-    ld_row[k] = real ? r : 0;
-    ld_col[k] = real ? c * 16 : 0;
-  }
-  auto issue = [&](int tile) {
-    unsigned char* buf = sfa_smem + (tile % NBUF) * TILE;
-    int rows[LPW];
-#pragma unroll
-    for (int k = 0; k < LPW; k++) {
-      const int slot = tile * TR + ld_row[k];
-      rows[k] = (slot < nslots) ? s_rows[slot] : -1;
-    }
-#pragma unroll
-    for (int k = 0; k < LPW; k++) {
-      const int row = (rows[k] < 0) ? fallback : rows[k];
-      const unsigned char* src = (const unsigned char*)p.kv + (size_t)row * ROWB + ld_col[k];
-      dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(buf + (wave + NW * k) * 1024)));
-    }
-  };
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
   for (int tile = 0; tile < ntiles; tile++) {
-    if (tile + 2 < ntiles) {
-      issue(tile + 2);
-      DSA_WAIT_VMCNT(2 * LPW);
-    } else if (tile + 1 < ntiles) {
-      DSA_WAIT_VMCNT(LPW);
+    // this wave's loads of the tile have landed; up to NBUF - 2 younger tiles
+    // may still be in flight
+    const int later = min(NBUF - 2, ntiles - 1 - tile);
+    if (wave == 0) {
+      if (later >= 2) DSA_WAIT_VMCNT(2 * LPW); else if (later == 1) DSA_WAIT_VMCNT(LPW); else DSA_WAIT_VMCNT(0);
     } else {
-      DSA_WAIT_VMCNT(0);
+      if (later >= 2) DSA_WAIT_VMCNT(2 * (LPW - 1)); else if (later == 1) DSA_WAIT_VMCNT(LPW - 1); else DSA_WAIT_VMCNT(0);
     }
     // rows of this tile that hold a selected position (bit r)
     const int rslot = tile * TR + (lane & 31);
     const uint32_t valid = (uint32_t)__ballot(lane < 32 && rslot < nslots && s_rows[rslot] >= 0);
     DSA_PHASE(2);
+    // every wave's loads of this tile are in LDS, and every wave is done with
+    // the previous tile, whose buffer the next load refills
     lds_barrier();
+    if (tile + NBUF - 1 < ntiles) issue(tile + NBUF - 1);
     DSA_PHASE(3);
     const unsigned char* cur = sfa_smem + (tile % NBUF) * TILE;
 
-    // ---- partial S^T[row, head] over this half's dims: two 16-row M-tiles
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- S^T[row, head]: two 16-row M-tiles x two 16-head groups
+    f32x4 s[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+      for (int ht = 0; ht < 2; ht++) s[rt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      const unsigned char* rp = cur + l16 * PITCH + (288 * half + 8 * grp) * 2;
+      // K-step k reads dims 32k + 8*grp .. +7 of rows l%16 and 16 + l%16;
+      // QD steps are in flight at a time
+      constexpr int QD = 4;
+      const uint32_t ra = lds_addr(cur) + l16 * PITCH + 16 * grp;
+      bf16x8 a[QD][2];
+      static_for<0, QD>([&](auto D) {
+        constexpr int d = decltype(D)::value;
+        a[d][0] = lds_read_b128<64 * d>(ra);
+        a[d][1] = lds_read_b128<16 * PITCH + 64 * d>(ra);
+      });
+      static_for<0, KS>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        constexpr int sl = k % QD;
+        lds_wait<2 * (k + QD <= KS ? QD - 1 : KS - 1 - k)>(a[sl][0], a[sl][1]);
 #pragma unroll
-      for (int k = 0; k < KSH; k++) {
-        const bf16x8 a0 = *(const bf16x8*)(rp + 64 * k);
-        const bf16x8 a1 = *(const bf16x8*)(rp + 16 * PITCH + 64 * k);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[k], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[k], s1, 0, 0, 0);
-      }
-    }
-    float* xw = s_x + wave * 512 + lane;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      xw[64 * e] = s0[e];
-      xw[64 * (4 + e)] = s1[e];
+        for (int ht = 0; ht < 2; ht++) {
+          s[0][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][0], qb[ht][k], s[0][ht], 0, 0, 0);
+          s[1][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][1], qb[ht][k], s[1][ht], 0, 0, 0);
+        }
+        if constexpr (k + QD < KS) {
+          a[sl][0] = lds_read_b128<64 * (k + QD)>(ra);
+          a[sl][1] = lds_read_b128<16 * PITCH + 64 * (k + QD)>(ra);
+        }
+      });
     }
     DSA_PHASE(4);
-    lds_barrier();
-    const float* xr = s_x + (wave ^ 4) * 512 + lane;
-    float z[8];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      z[e] = s0[e] + xr[64 * e];
-      z[4 + e] = s1[e] + xr[64 * (4 + e)];
-    }
 
-    // ---- online softmax for head l%16; this lane holds rows 4*grp + i and
-    // 16 + 4*grp + i (i < 4)
-    float mt = -INFINITY;
+    // ---- softmax weights for heads l%16 (+16 ht); this lane holds rows
+    // 4*grp + i and 16 + 4*grp + i (i < 4) of each head group.
+    // Fixed reference: the first tile with a selected row sets m_ref to its
+    // maximum plus kSfaRefMargin (log2 units) and it never moves afterwards,
+    // so the accumulators are never rescaled.  Weights 2^(z - m_ref) stay in
+    // the normal fp32/bf16 range while a later logit exceeds that first maximum
+    // by less than ~150 (overflow there shows up as a non-finite output); terms
+    // more than ~80 below it are flushed and negligible next to the first
+    // maximum's own weight.  The normalised result does not depend on m_ref.
+    bf16x8 phi[2], plo[2];
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const int r = 16 * (e >> 2) + 4 * grp + (e & 3);
-      z[e] = ((valid >> r) & 1u) ? z[e] * p.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, z[e]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // Lazy rescaling: the reference maximum m_run only moves when the tile's
-    // maximum exceeds it by more than 8 (log2 units), so probabilities stay
-    // below 2^8 (exact in fp32, in range for bf16) and the accumulators are
-    // rescaled only on those rare jumps.  The result is independent of m_run.
-    float alpha = 1.f;
-    if (m_run == -INFINITY) {
-      m_run = mt;                         // nothing accumulated yet
-    } else if (mt > m_run + 8.f) {
-      alpha = exp2f(m_run - mt);
-      m_run = mt;
-    }
-    if (__ballot(alpha != 1.f)) {
+    for (int ht = 0; ht < 2; ht++) {
+      float z[8];
+      float mt = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < MVH; i++) o[i] *= alpha;
-    }
-    const bool none = (m_run == -INFINITY);
-    float psum = 0.f;
-    bf16x8 pb;
+      for (int e = 0; e < 8; e++) {
+        const int r = 16 * (e >> 2) + 4 * grp + (e & 3);
+        const float v = s[e >> 2][ht][e & 3];
+        z[e] = ((valid >> r) & 1u) ? v * p.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, z[e]);
+      }
+      if (m_run[ht] == -INFINITY) {
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        m_run[ht] = mt + kSfaRefMargin;     // still -inf if no row of the tile is selected
+      }
+      const bool none = (m_run[ht] == -INFINITY);
+      float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      // the denominator sums the same bf16-rounded weights the PV product uses
-      const __bf16 pv = (__bf16)(none ? 0.f : __builtin_amdgcn_exp2f(z[e] - m_run));
-      psum += (float)pv;
-      pb[e] = pv;
+      for (int e = 0; e < 8; e++) {
+        const float pw = none ? 0.f : __builtin_amdgcn_exp2f(z[e] - m_run[ht]);
+        const __bf16 hi = (__bf16)pw;
+        phi[ht][e] = hi;
+        if constexpr (LO) {
+          const __bf16 lo = (__bf16)(pw - (float)hi);
+          plo[ht][e] = lo;
+          // the denominator sums exactly what the PV product multiplies in
+          psum += (float)hi + (float)lo;
+        } else {
+          psum += (float)hi;
+        }
+      }
+      l_run[ht] += psum;
     }
-    l_run = l_run * alpha + psum;
     DSA_PHASE(5);
 
     // ---- O^T[v, head] += V^T[v, rows] P^T[rows, head]: 16 columns on M, heads
     // on N, K = the tile's 32 rows.  This lane's K-slots 8*grp .. +7 hold rows
-    // 4*grp + j and 16 + 4*grp + j (j < 4), matching pb.  V^T comes from
-    // ds_read_b64_tr_b16: in each 16-lane group, source lane s = 4j + r reads
-    // columns vbase + 4r .. +3 of row j of the group's 4 rows; lane i then holds
-    // column vbase + i of those 4 rows.
+    // 4*grp + j and 16 + 4*grp + j (j < 4), matching the weights.  V^T comes
+    // from ds_read_b64_tr_b16: in each 16-lane group, source lane s = 4j + r
+    // reads columns vbase + 4r .. +3 of row j of the group's 4 rows; lane i
+    // then holds column vbase + i of those 4 rows.
     {
+      // M-tile mv reads columns 16 mv .. +15 of rows r0 and 16 + r0; PD tiles
+      // are in flight at a time
+      constexpr int PD = 6;
       const int r0 = 4 * grp + (l16 >> 2);
-      const unsigned char* rp0 = cur + r0 * PITCH + (256 * half + 4 * (l16 & 3)) * 2;
-      const unsigned char* rp1 = rp0 + 16 * PITCH;
-#pragma unroll
-      for (int mv = 0; mv < MVH; mv++) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rp0 + 32 * mv));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rp1 + 32 * mv));
+      const uint32_t rv = lds_addr(cur) + r0 * PITCH + 8 * (l16 & 3);
+      s16x4 v[PD][2];
+      static_for<0, PD>([&](auto D) {
+        constexpr int d = decltype(D)::value;
+        v[d][0] = lds_read_tr16_b64<32 * d>(rv);
+        v[d][1] = lds_read_tr16_b64<16 * PITCH + 32 * d>(rv);
+      });
+      static_for<0, MV>([&](auto M) {
+        constexpr int mv = decltype(M)::value;
+        constexpr int sl = mv % PD;
+        lds_wait<2 * (mv + PD <= MV ? PD - 1 : MV - 1 - mv)>(v[sl][0], v[sl][1]);
         typedef short s16x8 __attribute__((ext_vector_type(8)));
-        const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[mv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, o[mv], 0, 0, 0);
-      }
+        const s16x8 av = {v[sl][0][0], v[sl][0][1], v[sl][0][2], v[sl][0][3],
+                          v[sl][1][0], v[sl][1][1], v[sl][1][2], v[sl][1][3]};
+        const bf16x8 am = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (int ht = 0; ht < 2; ht++) {
+          o[ht][mv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, phi[ht], o[ht][mv], 0, 0, 0);
+          if constexpr (LO) o[ht][mv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, plo[ht], o[ht][mv], 0, 0, 0);
+        }
+        if constexpr (mv + PD < MV) {
+          v[sl][0] = lds_read_tr16_b64<32 * (mv + PD)>(rv);
+          v[sl][1] = lds_read_tr16_b64<16 * PITCH + 32 * (mv + PD)>(rv);
+        }
+      });
     }
-    lds_barrier();
     DSA_PHASE(6);
   }
 
-  // ---- epilogue: o[mv][i] holds head l%16, v = 256*half + 16*mv + 4*grp + i
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-  if (p.splits == 1) {
-    uint16_t* out = (uint16_t*)p.out + ((size_t)g * H + head) * DV;
+  // ---- epilogue: o[ht][mv][i] holds head head0 + 16*ht, v = 16*mv + 4*grp + i
 #pragma unroll
-    for (int mv = 0; mv < MVH; mv++) {
-      const int v = 256 * half + 16 * mv + 4 * grp;
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(o[mv][0] * inv) | ((uint32_t)f32_to_bf16(o[mv][1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16(o[mv][2] * inv) | ((uint32_t)f32_to_bf16(o[mv][3] * inv) << 16);
-      *(uint2*)(out + v) = pk;
+  for (int ht = 0; ht < 2; ht++) {
+    float l = l_run[ht];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const int head = head0 + 16 * ht;
+    if (p.splits == 1) {
+      uint16_t* out = (uint16_t*)p.out + ((size_t)g * H + head) * DV;
+#pragma unroll
+      for (int mv = 0; mv < MV; mv++) {
+        const int v = 16 * mv + 4 * grp;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(o[ht][mv][0] * inv) | ((uint32_t)f32_to_bf16(o[ht][mv][1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(o[ht][mv][2] * inv) | ((uint32_t)f32_to_bf16(o[ht][mv][3] * inv) << 16);
+        *(uint2*)(out + v) = pk;
+      }
+      if (p.lse && grp == 0)
+        p.lse[(size_t)g * H + head] = (l > 0.f) ? (m_run[ht] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    } else {
+      float* po = p.part_o + (((size_t)g * p.splits + split) * H + head) * DV;
+#pragma unroll
+      for (int mv = 0; mv < MV; mv++) *(f32x4*)(po + 16 * mv + 4 * grp) = o[ht][mv] * inv;
+      if (grp == 0)
+        p.part_ml[((size_t)g * p.splits + split) * H + head] = (l > 0.f) ? m_run[ht] + log2f(l) : -INFINITY;
     }
-    if (p.lse && grp == 0 && half == 0)
-      p.lse[(size_t)g * H + head] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
-  } else {
-    float* po = p.part_o + (((size_t)g * p.splits + split) * H + head) * DV;
-#pragma unroll
-    for (int mv = 0; mv < MVH; mv++) *(f32x4*)(po + 256 * half + 16 * mv + 4 * grp) = o[mv] * inv;
-    if (grp == 0 && half == 0)
-      p.part_ml[((size_t)g * p.splits + split) * H + head] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
   }
   DSA_PHASE(7);
+#ifdef DSA_SFA_PHASES
   if (prof)
     for (int i = 0; i < 8; i++) p.dbg[i] = ph[i];
+#endif
 #undef DSA_PHASE
 }
 
@@ -486,12 +585,18 @@ __global__ __launch_bounds__(256) void sfa_f32_kernel(SfaParams p) {
 hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hipStream_t st) {
   if (p.bv.total_q == 0) return hipSuccess;
   if (dtype == kBF16 && H == 128 && Dqk == 576 && Dv == 512) {
-    auto kern = sfa_bf16_kernel<576, 512>;
-    const size_t lds = 3 * 40 * 1024 + 8 * 2048 + (size_t)p.rows_per_split * 4;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (p.rows_per_split > kSfaMaxRows) return hipErrorInvalidValue;
+    const void* kern = p.precise_weights ? (const void*)sfa_bf16_kernel<576, 512, true>
+                                         : (const void*)sfa_bf16_kernel<576, 512, false>;
+    const size_t lds = SfaBf16Geom<576, 512>::lds_bytes(p.rows_per_split);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    const int tok8 = (p.bv.total_q + 7) / 8 * 8;
-    hipLaunchKernelGGL(kern, dim3(2 * tok8, 1, p.splits), dim3(kSfaBf16Threads), lds, st, p);
+    const int chunk = (p.bv.total_q + 7) / 8;
+    const dim3 grid(8 * chunk, 1, p.splits);
+    if (p.precise_weights)
+      hipLaunchKernelGGL((sfa_bf16_kernel<576, 512, true>), grid, dim3(kSfaBf16Threads), lds, st, p);
+    else
+      hipLaunchKernelGGL((sfa_bf16_kernel<576, 512, false>), grid, dim3(kSfaBf16Threads), lds, st, p);
     return hipGetLastError();
   }
   if (dtype == kF32 && H == 8 && Dqk == 80 && Dv == 64) {

@@ -211,13 +211,17 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
 
   // Pick the largest co-resident grid (2 or 1 workgroups per CU) and the
   // largest sub-batch whose per-workgroup score buffer fits in LDS.
-  int grid = 0, chunk_cap = 0, sub = 0;
+  int grid = 0, chunk_cap = 0, sub = 0, stage = 0;
   for (int per_cu = 2; per_cu >= 1 && grid == 0; per_cu--) {
     const int G = std::min(kMaxGrid, per_cu * di.cus);
     for (int nb = std::min(b->batch, G / 2); nb >= 1; nb = (nb > 1) ? nb / 2 : 0) {
       const int64_t cap_pages = ((int64_t)nb * std::max(1, maxp) + (G - nb) - 1) / (G - nb);
       const int64_t cap_keys = cap_pages * P;
-      const size_t lds = indexer_decode_lds_bytes(maxq, (int)std::min<int64_t>(cap_keys, 1 << 24));
+      // a workgroup's keys span at most cap_pages pages (+1 when P does not
+      // divide its range start, which the page-aligned assignment avoids)
+      const int64_t stage_pages = cap_pages + 1;
+      const size_t lds = indexer_decode_lds_bytes(maxq, (int)std::min<int64_t>(cap_keys, 1 << 24),
+                                                  (int)std::min<int64_t>(stage_pages, 1 << 24));
       if (lds > kLdsMax) continue;
       int occ = 0;
       e = indexer_decode_occupancy(dt, a->n_heads, a->head_dim, maxq, lds, &occ);
@@ -225,6 +229,7 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
       if (occ * di.cus < G) break;  // try fewer workgroups per CU
       grid = G;
       chunk_cap = (int)cap_keys;
+      stage = (int)stage_pages;
       sub = nb;
       break;
     }
@@ -245,6 +250,7 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
   p.ws_grid_pad = (kMaxGrid + 31) / 32 * 32;
   p.grid = grid;
   p.chunk_cap = chunk_cap;
+  p.stage_pages = stage;
   for (int b0 = 0; b0 < b->batch; b0 += sub) {
     const int nb = std::min(sub, b->batch - b0);
     p.bv = view_of(b, P);

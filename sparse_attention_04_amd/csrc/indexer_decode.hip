@@ -269,9 +269,10 @@ enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3 };
 template <int DT, int H, int D, int MAXQ>
 __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerDecodeParams p) {
   extern __shared__ uint32_t smem[];
-  // dynamic LDS: sc[MAXQ][cap] | lhist[2048] | scratch
+  // dynamic LDS: sc[MAXQ][cap] | lhist[2048] | s_bt[stage_pages]
   uint32_t* sc = smem;
   uint32_t* lhist = smem + (size_t)MAXQ * p.chunk_cap;
+  int* s_bt = (int*)(lhist + kRadixBins);
   __shared__ int s_seqinfo[8];
   __shared__ int s_scan[kIdxThreads];
   __shared__ int s_rank[kIdxWaves + 1];
@@ -372,37 +373,48 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
   DSA_STAMP(1);
 
   // ---- 2. scores of this page range, kept in LDS as orderable keys ----------
+  // The workgroup's slice of the block table is staged in LDS first, so the
+  // address of a tile is an LDS lookup rather than a dependent global load.
+  const int pg0 = s0 / P;
+  const int npg_loc = (s1 > s0) ? (s1 - 1) / P + 1 - pg0 : 0;
+  const bool staged = npg_loc <= p.stage_pages;
+  if (!staged && tid == 0) atomic_add_agent(W.err(), 4u);  // host sizing guarantees staging
+  for (int i = tid; i < npg_loc && staged; i += kIdxThreads) s_bt[i] = bt[pg0 + i];
+  __syncthreads();
   {
     MfmaScorer<DT, H, D> scorer;
     using Tile = typename MfmaScorer<DT, H, D>::Tile;
+    // tiles held per wave: the one being scored and kAhead in flight
+    constexpr int kAhead = (DT == kFP8 || DT == kMX) ? 4 : 2;
+    constexpr int RD = kAhead + 1;
     const int ntiles = (nloc + 31) / 32;
+    auto fetch = [&](int tile, Tile& t) {
+      if (tile < ntiles) {
+        const int s = min(s0 + 32 * tile + (lane & 31), s1 - 1);
+        const int page = staged ? s_bt[s / P - pg0] : bt[s / P];
+        scorer.load_tile(p, (int64_t)page * P + (s % P), t);
+      }
+    };
     for (int q = 0; q < T && q < MAXQ; q++) {
       if (s_state[q] != kActive) continue;
       const int t = L - T + q;
       scorer.load_query(p, tok0 + q);
       uint32_t* scq = sc + (size_t)q * p.chunk_cap;
-      int tile = wave;
-      Tile cur;
-      int64_t row_cur = 0;
-      if (tile < ntiles) {
-        const int s = min(s0 + 32 * tile + (lane & 31), s1 - 1);
-        row_cur = (int64_t)bt[s / P] * P + (s % P);
-        scorer.load_tile(p, row_cur, cur);
-      }
-      for (; tile < ntiles; tile += kIdxWaves) {
-        Tile nxt;
-        int64_t row_nxt = 0;
-        const int tn = tile + kIdxWaves;
-        if (tn < ntiles) {
-          const int s = min(s0 + 32 * tn + (lane & 31), s1 - 1);
-          row_nxt = (int64_t)bt[s / P] * P + (s % P);
-          scorer.load_tile(p, row_nxt, nxt);
+      Tile ring[RD];
+#pragma unroll
+      for (int d = 0; d < RD - 1; d++) fetch(wave + d * kIdxWaves, ring[d]);
+      for (int base = wave; base < ntiles; base += RD * kIdxWaves) {
+#pragma unroll
+        for (int d = 0; d < RD; d++) {
+          const int tile = base + d * kIdxWaves;
+          if (tile < ntiles) {
+            // refill the slot of the previous tile with the one kAhead later
+            fetch(tile + kAhead * kIdxWaves, ring[(d + RD - 1) % RD]);
+            const float v = scorer.score(p, 0, ring[d]);
+            const int s = s0 + 32 * tile + lane;
+            if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
+          }
         }
-        const float v = scorer.score(p, row_cur, cur);
-        const int s = s0 + 32 * tile + lane;
-        if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
-        cur = nxt;
-        row_cur = row_nxt;
       }
     }
   }
@@ -660,8 +672,8 @@ static hipError_t launch_one(const IndexerDecodeParams& p, size_t lds, hipStream
 
 int indexer_decode_max_q() { return kMaxDecodeQ; }
 
-size_t indexer_decode_lds_bytes(int maxq, int chunk_cap) {
-  return ((size_t)maxq * chunk_cap + kRadixBins) * 4;
+size_t indexer_decode_lds_bytes(int maxq, int chunk_cap, int stage_pages) {
+  return ((size_t)maxq * chunk_cap + kRadixBins + stage_pages) * 4;
 }
 
 hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t lds, int* blocks_per_cu) {
@@ -678,7 +690,7 @@ hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t ld
 
 hipError_t launch_indexer_decode(int dtype, int H, int D, int maxq, const IndexerDecodeParams& p,
                                  hipStream_t st) {
-  const size_t lds = indexer_decode_lds_bytes(maxq, p.chunk_cap);
+  const size_t lds = indexer_decode_lds_bytes(maxq, p.chunk_cap, p.stage_pages);
 #define DSA_PICK(DT_, H_, D_, Q_) \
   if (dtype == DT_ && H == H_ && D == D_ && maxq == Q_) return launch_one<DT_, H_, D_, Q_>(p, lds, st);
   DSA_INDEXER_DECODE_SHAPES(DSA_PICK)

@@ -31,11 +31,12 @@ struct IndexerDecodeParams {
   int32_t seq_base;        // index of bv's first sequence in the whole batch
   int32_t grid;            // workgroups launched
   int32_t chunk_cap;       // LDS score slots per query (keys)
+  int32_t stage_pages;     // LDS slots for the workgroup's block-table slice
 };
 
 size_t indexer_ws_bytes(int nseq, int nq, int grid);
 size_t indexer_ws_zero_bytes(int nseq, int nq);
-size_t indexer_decode_lds_bytes(int maxq, int chunk_cap);
+size_t indexer_decode_lds_bytes(int maxq, int chunk_cap, int stage_pages);
 hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t lds, int* blocks_per_cu);
 hipError_t launch_indexer_decode(int dtype, int H, int D, int maxq, const IndexerDecodeParams& p,
                                  hipStream_t st);

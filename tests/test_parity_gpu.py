@@ -154,6 +154,19 @@ def test_c5_multi_token_decode_small():
     _run_all_paths(case)
 
 
+@pytest.mark.parametrize("name", ["c4_decode_fp8", "c4_decode_mxfp8"])
+def test_multi_token_decode_quantised(name):
+    # several query tokens per sequence with the FP8 / MXFP8 indexer
+    case = case_to(make_case(name, 14, batch=2, seq_len_range=(3000, 6000), q_len=4), "cuda")
+    _run_all_paths(case)
+
+
+def test_multi_token_decode_f32_ragged():
+    # three query tokens per sequence on the f32 path, ragged pages
+    case = case_to(make_case("c1_tiny_f32", 13, batch=2, seq_len_range=(100, 250), q_len=3), "cuda")
+    _run_all_paths(case)
+
+
 def test_c2_full_size_sampled():
     """The full decode workload (32 sequences, contexts U[4096, 32768]) in the
     launch configuration the benchmark times, checked on sampled queries."""

@@ -99,17 +99,47 @@ def cpu_baseline(case, budget_s):
     for t in (case.k_pool, case.kv_pool, case.k_scale, case.block_table):
         if t is not None:
             od._np(t)
+    # seeded order over the workload's query tokens, repeated until the budget
+    # is spent (at least one token)
     done, t0 = 0, time.perf_counter()
     order = np.random.default_rng(0).permutation(len(qs))
-    for j in order:
-        oracle.run_query(case, *qs[j])
+    while True:
+        oracle.run_query(case, *qs[order[done % len(qs)]])
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {len(qs)} query tokens of the same workload (first seed), "
-                      f"{el:.1f} s, float64 NumPy, host cores available {len(os.sched_getaffinity(0))}"}
+            "sample": f"{done} query tokens ({done / len(qs):.1f} passes over the {len(qs)} of the same "
+                      f"workload, first seed, seeded order), {el:.1f} s, float64 NumPy, "
+                      f"host cores available {len(os.sched_getaffinity(0))}"}
+
+
+def prefill_line(torch, B, make_case, steps):
+    """The 32768-token causal prefill: fused call time and MFMA fractions."""
+    import numpy as np
+    case = make_case("c3_prefill_bf16", 3, device="cuda")
+    call = B.Call(case)
+    for op in (B.DSA_OP_FUSED_PREFILL, B.DSA_OP_INDEXER_TOPK, B.DSA_OP_SPARSE_ATTN):
+        call.workspace(op)
+    ms = time_calls(lambda s: call.fused_prefill(), steps, 1, torch)
+    idx = call.indexer_topk().clone()
+    ms_idx = time_calls(lambda s: call.indexer_topk(), steps, 1, torch)
+    ms_sfa = time_calls(lambda s: call.sparse_attn(idx), steps, 1, torch)
+    T = case.total_q
+    t = np.arange(T, dtype=np.int64)
+    rows = int(np.minimum(case.topk, t + 1).sum())
+    pairs = int(((t + 1) * (t + 1 > case.topk)).sum())   # queries that need scores
+    f_idx = 2 * case.h_i * case.d_i * pairs
+    f_sfa = 2 * case.h_s * (case.d_qk + case.d_v) * rows
+    peak = MFMA_PEAK_TFLOPS["bf16"] * 1e12
+    return {"workload": "c3_prefill_bf16: one sequence, 32768 query tokens, causal, bf16, k=2048",
+            "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+            "stages_ms": {"indexer_topk": ms_idx, "sparse_attn": ms_sfa},
+            "algorithmic_flops": {"indexer_per_head": f_idx, "sfa": f_sfa},
+            "mfma_frac": {"fused": (f_idx + f_sfa) / (ms * 1e-3) / peak,
+                          "indexer": f_idx / (ms_idx * 1e-3) / peak, "sfa": f_sfa / (ms_sfa * 1e-3) / peak},
+            "peak_tflops": MFMA_PEAK_TFLOPS["bf16"]}
 
 
 def main():
@@ -122,6 +152,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--no-ctx32k", dest="ctx32k", action="store_false",
                     help="skip the extra all-32k-context measurement")
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false",
+                    help="skip the 32k causal prefill measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -218,6 +250,8 @@ def main():
         line["ctx32k"] = {"us_per_step": ms32 * 1e3, "tokens_per_s": c32[0].case.total_q / (ms32 * 1e-3),
                           "step_hbm_frac": a32["fused_bytes"] / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del c32
+    if args.workload == "c2_decode_bf16" and args.prefill:
+        line["prefill_32k"] = prefill_line(torch, B, make_case, 3)
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -80,7 +80,7 @@ typedef struct {
   const void* scale;
   int32_t dtype;
   int32_t num_pages;
-  int32_t page_size;
+  int32_t page_size;           /* tokens per page: a power of two in [1, 4096]    */
   int32_t dim;
 } dsa_paged_cache;
 

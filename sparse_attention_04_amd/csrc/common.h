@@ -105,7 +105,8 @@ struct BatchView {
   const int32_t* cu_q;
   const int32_t* block_table;
   int32_t max_pages;
-  int32_t page_size;
+  int32_t page_size;       // a power of two
+  int32_t page_shift;      // log2(page_size)
   int32_t total_q;
 };
 

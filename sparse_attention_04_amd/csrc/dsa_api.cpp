@@ -65,7 +65,8 @@ dsa_status check_cache(const dsa_paged_cache* c, const char* name, int dim, int 
   if (!c->data) return fail(DSA_ERR_INVALID_ARG, "%s->data is NULL", name);
   if (c->dtype != dtype) return fail(DSA_ERR_INVALID_ARG, "%s->dtype %d differs from the query dtype %d", name, c->dtype, dtype);
   if (c->dim != dim) return fail(DSA_ERR_INVALID_ARG, "%s->dim %d differs from %d", name, c->dim, dim);
-  if (c->page_size < 1 || c->page_size > 4096) return fail(DSA_ERR_UNSUPPORTED, "%s->page_size %d outside [1, 4096]", name, c->page_size);
+  if (c->page_size < 1 || c->page_size > 4096 || (c->page_size & (c->page_size - 1)))
+    return fail(DSA_ERR_UNSUPPORTED, "%s->page_size %d is not a power of two in [1, 4096]", name, c->page_size);
   if (c->num_pages < 1) return fail(DSA_ERR_INVALID_ARG, "%s->num_pages must be >= 1", name);
   if ((int64_t)b->max_pages_per_seq * c->page_size < b->max_seq_len)
     return fail(DSA_ERR_INVALID_ARG, "max_pages_per_seq * page_size < max_seq_len");
@@ -121,6 +122,7 @@ BatchView view_of(const dsa_batch* b, int page_size) {
   v.block_table = b->block_table;
   v.max_pages = b->max_pages_per_seq;
   v.page_size = page_size;
+  v.page_shift = __builtin_ctz((unsigned)page_size);
   v.total_q = b->total_q;
   return v;
 }

@@ -293,14 +293,14 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
     int tot = 0;
     for (int b0 = 0; b0 < bv.batch; b0 += kWave) {
       const int b = b0 + lane;
-      const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) / P : 0;
+      const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) >> bv.page_shift : 0;
       tot += wave_sum(pg);
     }
     const int cap = (tot + (p.grid - bv.batch) - 1) / (p.grid - bv.batch);
     int acc = 0, found = 0;
     for (int b0 = 0; b0 < bv.batch && !found; b0 += kWave) {
       const int b = b0 + lane;
-      const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) / P : 0;
+      const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) >> bv.page_shift : 0;
       const int nb = (cap > 0) ? (pg + cap - 1) / cap : 0;
       // inclusive prefix of nb over the wave
       int inc = nb;
@@ -375,8 +375,9 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
   // ---- 2. scores of this page range, kept in LDS as orderable keys ----------
   // The workgroup's slice of the block table is staged in LDS first, so the
   // address of a tile is an LDS lookup rather than a dependent global load.
-  const int pg0 = s0 / P;
-  const int npg_loc = (s1 > s0) ? (s1 - 1) / P + 1 - pg0 : 0;
+  const int PS = bv.page_shift;
+  const int pg0 = s0 >> PS;
+  const int npg_loc = (s1 > s0) ? ((s1 - 1) >> PS) + 1 - pg0 : 0;
   const bool staged = npg_loc <= p.stage_pages;
   if (!staged && tid == 0) atomic_add_agent(W.err(), 4u);  // host sizing guarantees staging
   for (int i = tid; i < npg_loc && staged; i += kIdxThreads) s_bt[i] = bt[pg0 + i];
@@ -391,8 +392,8 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
     auto fetch = [&](int tile, Tile& t) {
       if (tile < ntiles) {
         const int s = min(s0 + 32 * tile + (lane & 31), s1 - 1);
-        const int page = staged ? s_bt[s / P - pg0] : bt[s / P];
-        scorer.load_tile(p, (int64_t)page * P + (s % P), t);
+        const int page = staged ? s_bt[(s >> PS) - pg0] : bt[s >> PS];
+        scorer.load_tile(p, ((int64_t)page << PS) + (s & (P - 1)), t);
       }
     };
     for (int q = 0; q < T && q < MAXQ; q++) {

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
   // the sequence's block-table row, staged once (page lookups stay on chip)
   {
     const int* btg = bv.block_table + (size_t)b * bv.max_pages;
-    const int npg = min((L + P - 1) / P, kMaxPages);
+    const int npg = min((L + P - 1) >> bv.page_shift, kMaxPages);
     for (int i = tid; i < npg; i += kPfThreads) s_bt[i] = btg[i];
   }
   __syncthreads();
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
           const bool real = r < kKT && c < (D * 2) / 16;
           int s = tile * kKT + (real ? r : 0);
           s = min(s, tmax);
-          const int64_t prow = (int64_t)bt[s / P] * P + (s % P);
+          const int64_t prow = ((int64_t)bt[s >> bv.page_shift] << bv.page_shift) + (s & (P - 1));
           const unsigned char* src = (const unsigned char*)p.k_data + prow * (D * 2) + (real ? c * 16 : 0);
           dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(buf + (wave + kPfWaves * k) * 1024)));
         }

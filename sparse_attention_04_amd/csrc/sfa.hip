@@ -12,7 +12,7 @@
 // bf16 kernel (H = 128, Dqk = 576, Dv = 512): a workgroup owns one query token,
 // all of its heads and a contiguous range of index slots.  Per tile of 32
 // slots it gathers the 32 latent rows through the block table into LDS (a
-// 3-deep ring), then every wave (32 heads) computes
+// 4-deep ring), then every wave (32 heads) computes
 //   S^T[row, head] = KV[row, :] . q[head, :]     (16x16x32 bf16 MFMAs, rows on M)
 // so that after the softmax weights are formed the probabilities already sit in the
 // B-operand layout of the second product
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
 
   for (int r = tid; r < nslots; r += kSfaBf16Threads) {
     const int pos = idx[r];
-    s_rows[r] = (pos >= 0) ? bt[pos / P] * P + (pos % P) : -1;
+    s_rows[r] = (pos >= 0) ? (bt[pos >> bv.page_shift] << bv.page_shift) + (pos & (P - 1)) : -1;
   }
   __syncthreads();
   int fallback = -1;
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(256) void sfa_f32_kernel(SfaParams p) {
     if (tid < TR) {
       const int slot = t0 + tid;
       const int pos = (slot < nslots) ? idx[slot] : -1;
-      s_row[tid] = (pos >= 0) ? bt[pos / P] * P + (pos % P) : -1;
+      s_row[tid] = (pos >= 0) ? (bt[pos >> bv.page_shift] << bv.page_shift) + (pos & (P - 1)) : -1;
     }
     __syncthreads();
     for (int e = tid; e < TR * DQK; e += 256) {

@@ -72,6 +72,7 @@ def test_workspace_size_positive_and_monotone():
     (lambda b, i, s: setattr(i, "head_dim", 64), B.DSA_ERR_UNSUPPORTED),
     (lambda b, i, s: setattr(i.k_cache.contents, "dtype", B.DSA_F32), B.DSA_ERR_INVALID_ARG),
     (lambda b, i, s: setattr(i.k_cache.contents, "page_size", 0), B.DSA_ERR_UNSUPPORTED),
+    (lambda b, i, s: setattr(i.k_cache.contents, "page_size", 48), B.DSA_ERR_UNSUPPORTED),
     (lambda b, i, s: setattr(b, "max_pages_per_seq", 1), B.DSA_ERR_INVALID_ARG),
     (lambda b, i, s: setattr(s, "v_dim", 256), B.DSA_ERR_UNSUPPORTED),
     (lambda b, i, s: setattr(s, "q_dtype", B.DSA_FP8_E4M3), B.DSA_ERR_UNSUPPORTED),

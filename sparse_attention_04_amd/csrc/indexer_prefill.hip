@@ -37,6 +37,7 @@ constexpr int kCap = 3072;          // candidate buffer entries per query
 constexpr int kRowPitch = 128 * 2 + 16;            // LDS bytes per key row (bf16, padded)
 constexpr int kTileBytes = 20 * 1024;              // 64 rows of kRowPitch, rounded to whole loads
 constexpr int kMaxPages = 4096;                    // block-table entries staged in LDS
+constexpr int kHistWords = 260;                    // per-wave select histogram (256 bins, a spare word, padding)
 
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
@@ -53,34 +54,76 @@ __device__ __forceinline__ int lane_rank(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-// Wave-level exact Top-`need` of a candidate list (keys[], pos[] of `count`
-// entries, in position order).  Four passes over 8-bit digits fix the
-// need-th largest key; entries above it are kept, and of the entries equal to
-// it the first ones in list order.  Compacts in place, stably, and returns the
-// need-th largest key.  hist: 256 words of this wave's LDS.
-__device__ uint32_t wave_select(uint32_t* keys, uint32_t* pos, int& count, int need, uint32_t* hist) {
-  const int lane = threadIdx.x & 63;
-  uint32_t prefix = 0, pmask = 0;
-  int rem = need;
-  bool whole_bin = false;
-  for (int pass = 0; pass < 4 && !whole_bin; pass++) {
-    const int shift = 24 - 8 * pass;
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) hist[4 * lane + j] = 0u;
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS writes of this wave done (lgkmcnt(0))
-    for (int i = lane; i < count; i += 64) {
-      const uint32_t x = keys[i];
-      if ((x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// Wave-level Top-`need` of a candidate list (keys[], pos[] of `count` > need
+// entries, in position order).  The keys and positions are held in registers
+// (lane l owns entries l, l + 64, ...).  Radix passes run over y = key -
+// min(key), starting at the highest bit in which the entries differ, so the
+// first 8-bit digit spreads the entries over the whole histogram rather than
+// piling them onto the one or two bins of a shared exponent.  Each pass finds
+// the bin that holds the need-th largest entry.
+//
+// EXACT: passes continue until exactly `need` entries remain; of entries equal
+// to the need-th largest key the first ones in list order are kept.  Otherwise
+// the select may stop as soon as the entries above and in the current bin are
+// at most need + kSelSlack: they always include the need best.
+// Compacts in place, stably, and returns the smallest kept key: a later
+// candidate must exceed it to enter the top `need` (equal keys at later
+// positions lose the tie).  hist: 260 words of this wave's LDS, 16-byte aligned.
+constexpr int kSelSlack = 256;
+template <bool EXACT>
+__device__ uint32_t wave_select(uint32_t* keys, uint32_t* pos, int& count, int need, uint32_t* hist) {
+  constexpr int R = kCap / 64;
+  const int lane = threadIdx.x & 63;
+  uint32_t kv[R], pv[R];
+#pragma unroll
+  for (int j = 0; j < R; j++) {   // entries at or past `count` are read but never used
+    kv[j] = keys[64 * j + lane];
+    pv[j] = pos[64 * j + lane];
+  }
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < R; j++) {
+    const bool in = 64 * j + lane < count;
+    mn = min(mn, in ? kv[j] : 0xFFFFFFFFu);
+    mx = max(mx, in ? kv[j] : 0u);
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+#pragma unroll
+  for (int j = 0; j < R; j++) kv[j] -= mn;
+  const uint32_t range = mx - mn;
+  int hi = range ? 31 - __builtin_clz(range) : -1;    // highest bit in which entries differ
+  // entries in the current region: (y & pmask) == prefix
+  uint32_t prefix = 0u, pmask = (hi >= 0) ? ~((2u << hi) - 1u) : 0xFFFFFFFFu;
+  int rem = need;            // entries still wanted from the region
+  int bincnt = count;        // entries in the region
+  bool whole = false, partial = false;
+  while (hi >= 0) {
+    const int lo = max(hi - 7, 0);
+    const uint32_t dmask = (2u << (hi - lo)) - 1u;
+    *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+      const bool m = (64 * j + lane < count) && (kv[j] & pmask) == prefix;
+      atomicAdd(&hist[m ? (kv[j] >> lo) & dmask : 256u], 1u);   // word 256 takes the rest
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     // lane l owns bins 4l .. 4l+3; suffix sums from the top bin down
-    uint32_t h[4];
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      h[j] = hist[4 * lane + j];
-      c += (int)h[j];
-    }
+    const uint4 hv = *(const uint4*)(hist + 4 * lane);
+    const uint32_t h[4] = {hv.x, hv.y, hv.z, hv.w};
+    const int c = (int)(h[0] + h[1] + h[2] + h[3]);
     int x = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -88,14 +131,14 @@ __device__ uint32_t wave_select(uint32_t* keys, uint32_t* pos, int& count, int n
       if (lane + o < 64) x += v;
     }
     const int above = x - c;   // entries in bins above this lane's four
-    int bin = -1, binabove = 0, bincnt = 0;
+    int bin = -1, binabove = 0, bc = 0;
     if (above < rem && rem <= above + c) {
       int run = above;
       for (int j = 3; j >= 0; j--) {
         if (run + (int)h[j] >= rem) {
           bin = 4 * lane + j;
           binabove = run;
-          bincnt = (int)h[j];
+          bc = (int)h[j];
           break;
         }
         run += (int)h[j];
@@ -105,46 +148,47 @@ __device__ uint32_t wave_select(uint32_t* keys, uint32_t* pos, int& count, int n
     const int src = m ? (__ffsll((unsigned long long)m) - 1) : 0;
     bin = __shfl(bin, src);
     binabove = __shfl(binabove, src);
-    bincnt = __shfl(bincnt, src);
-    if (bin < 0) bin = 0;  // cannot happen for need <= count
+    bc = __shfl(bc, src);
+    if (bin < 0) bin = 0;  // cannot happen for need < count
     rem -= binabove;
-    prefix |= (uint32_t)bin << shift;
-    pmask |= 0xFFu << shift;
-    whole_bin = (bincnt == rem);
+    bincnt = bc;
+    prefix |= (uint32_t)bin << lo;
+    pmask |= dmask << lo;
+    hi = lo - 1;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // histogram read before the next clear
+    if (bincnt == rem) { whole = true; break; }
+    if (!EXACT && bincnt - rem <= kSelSlack) { partial = true; break; }
   }
-  // stable in-place compaction: above the prefix, or equal and among the
-  // first `rem` equal ones
+  const bool keep_all = whole || partial;
+  // stable in-place compaction (every read above precedes these writes)
   int out = 0, ties = 0;
-  for (int i0 = 0; i0 < count; i0 += 64) {
-    const int i = i0 + lane;
-    const uint32_t x = (i < count) ? keys[i] : 0u;
-    const uint32_t ps = (i < count) ? pos[i] : 0u;
-    const bool in = i < count;
-    const bool gt = in && (x & pmask) > prefix;
-    const bool eq = in && (x & pmask) == prefix;
-    const uint64_t me = __ballot(eq);
-    const bool keep = gt || (eq && (whole_bin || ties + lane_rank(me) < rem));
-    const uint64_t mk = __ballot(keep);
-    const int r = out + lane_rank(mk);
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // every lane has read before anyone writes
-    if (keep) {
-      keys[r] = x;
-      pos[r] = ps;
+  uint32_t kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < R; j++) {
+    if (64 * j < count) {
+      const bool in = 64 * j + lane < count;
+      const uint32_t ym = kv[j] & pmask;
+      const bool gt = in && ym > prefix;
+      const bool eq = in && ym == prefix;
+      const uint64_t me = __ballot(eq);
+      const bool keep = gt || (eq && (keep_all || ties + lane_rank(me) < rem));
+      const uint64_t mk = __ballot(keep);
+      const int r = out + lane_rank(mk);
+      if (keep) {
+        keys[r] = kv[j] + mn;
+        pos[r] = pv[j];
+        kmin = min(kmin, kv[j]);
+      }
+      out += __popcll(mk);
+      ties += __popcll(me);
     }
-    out += __popcll(mk);
-    ties += __popcll(me);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
   count = out;
-  // the need-th largest key is the smallest kept one
-  uint32_t mn = 0xFFFFFFFFu;
-  for (int i = lane; i < out; i += 64) mn = min(mn, keys[i]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-  return mn;
+  return wave_min_u32(kmin) + mn;
 }
 
-template <int H, int D>
+template <int H, int D, bool BIG_PAGE>
 __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerPrefillParams p) {
   static_assert(H == 64 && D == 128, "prefill indexer is compiled for 64 heads x 128");
   constexpr int MT = H / 32;        // M-tiles over heads
@@ -153,8 +197,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
   extern __shared__ __attribute__((aligned(16))) unsigned char pf_smem[];
   unsigned char* ring = pf_smem;                                              // 2 tiles
   uint32_t* cand = (uint32_t*)(pf_smem + 2 * kTileBytes);                     // [4][2][kCap]
-  uint32_t* hist = cand + kPfWaves * 2 * kCap;                                // [4][256]
-  int32_t* s_bt = (int32_t*)(hist + kPfWaves * 256);                          // [kMaxPages]
+  uint32_t* hist = cand + kPfWaves * 2 * kCap;                                // [4][kHistWords]
+  int32_t* s_bt = (int32_t*)(hist + kPfWaves * kHistWords);                   // [kMaxPages]
   __shared__ int s_unit[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -213,9 +257,23 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
   const int blocks[2] = {u, NB - 1 - u};
   const int nblk = (blocks[1] != blocks[0]) ? 2 : 1;
 
+  // per-lane source of each of this wave's LPW tile loads: LDS byte
+  // (wave + 4k) * 1024 + 16 * lane is row off / kRowPitch, 16-byte column
+  // (off % kRowPitch) / 16; padding bytes load row 0, column 0
+  int lrow[LPW], lcol[LPW];
+#pragma unroll
+  for (int k = 0; k < LPW; k++) {
+    const int off = (wave + kPfWaves * k) * 1024 + lane * 16;
+    const int r = off / kRowPitch, c = (off % kRowPitch) / 16;
+    const bool real = r < kKT && c < (D * 2) / 16;
+    lrow[k] = real ? r : 0;
+    lcol[k] = real ? c * 16 : 0;
+  }
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t* ckey = cand + (size_t)wave * 2 * kCap;
   uint32_t* cpos = ckey + kCap;
-  uint32_t* whist = hist + wave * 256;
+  uint32_t* whist = hist + wave * kHistWords;
 
   for (int bi = 0; bi < nblk; bi++) {
     const int q0 = blocks[bi] * kQBlock;
@@ -254,55 +312,74 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
       int count = 0;
       uint32_t thr = 0u;    // keys must exceed this to become candidates
       const int nt = (tmax + 1 + kKT - 1) / kKT;
+      // tile `tile`'s keys tile*64 .. tile*64+63 (rows past tmax repeat row
+      // tmax) go to ring buffer tile & 1: each wave issues LPW 1-KiB loads
       auto issue = [&](int tile) {
-        unsigned char* buf = ring + (tile & 1) * kTileBytes;
+        const int s0 = tile * kKT;
+        const int lim = tmax - s0;     // rows above lim repeat row lim
+        const uint32_t m0 = ring_lds + (uint32_t)(tile & 1) * kTileBytes + (uint32_t)wave_u * 1024u;
+        if constexpr (BIG_PAGE) {
+          // the whole tile lies in one page
+          const int64_t prow0 = ((int64_t)bt[s0 >> bv.page_shift] << bv.page_shift) + (s0 & (P - 1));
+          const unsigned char* base = (const unsigned char*)p.k_data + prow0 * (D * 2);
 #pragma unroll
-        for (int k = 0; k < LPW; k++) {
-          const int off = (wave + kPfWaves * k) * 1024 + lane * 16;
-          const int r = off / kRowPitch, c = (off % kRowPitch) / 16;
-          const bool real = r < kKT && c < (D * 2) / 16;
-          int s = tile * kKT + (real ? r : 0);
-          s = min(s, tmax);
-          const int64_t prow = ((int64_t)bt[s >> bv.page_shift] << bv.page_shift) + (s & (P - 1));
-          const unsigned char* src = (const unsigned char*)p.k_data + prow * (D * 2) + (real ? c * 16 : 0);
-          dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(buf + (wave + kPfWaves * k) * 1024)));
+          for (int k = 0; k < LPW; k++)
+            dma16(base + (min(lrow[k], lim) * (D * 2) + lcol[k]), m0 + k * kPfWaves * 1024u);
+        } else {
+          const unsigned char* src[LPW];
+#pragma unroll
+          for (int k = 0; k < LPW; k++) {
+            const int srow = s0 + min(lrow[k], lim);
+            const int64_t prow = ((int64_t)bt[srow >> bv.page_shift] << bv.page_shift) + (srow & (P - 1));
+            src[k] = (const unsigned char*)p.k_data + prow * (D * 2) + lcol[k];
+          }
+#pragma unroll
+          for (int k = 0; k < LPW; k++) dma16(src[k], m0 + k * kPfWaves * 1024u);
         }
       };
+      // 2-buffer ring: tile t + 1 is loaded while t is scored.  The barrier at
+      // the top of iteration t also tells that every wave is done with the
+      // buffer of tile t - 1, which tile t + 1 then overwrites.
       issue(0);
       for (int tile = 0; tile < nt; tile++) {
-        if (tile + 1 < nt) {
-          issue(tile + 1);
-          DSA_PF_WAIT_VMCNT(LPW);
-        } else {
-          DSA_PF_WAIT_VMCNT(0);
-        }
+        DSA_PF_WAIT_VMCNT(0);
         lds_barrier();
+        if (tile + 1 < nt) issue(tile + 1);
         const unsigned char* cur = ring + (tile & 1) * kTileBytes;
-        // ---- scores of the 64 keys of this tile for this wave's query
+        // ---- scores of the 64 keys of this tile for this wave's query: both
+        // 32-key N-tiles at once, so four independent accumulator chains
+        // keep the matrix unit busy
         float sc[2];
+        {
+          f32x16 acc[2][MT];
 #pragma unroll
-        for (int n = 0; n < 2; n++) {
-          f32x16 acc[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) acc[mt][e] = 0.f;
-          const unsigned char* kp = cur + (32 * n + (lane & 31)) * kRowPitch + (lane >> 5) * D;
-#pragma unroll
-          for (int kk = 0; kk < KS; kk++) {
-            const bf16x8 kb = *(const bf16x8*)(kp + 16 * kk);
+          for (int n = 0; n < 2; n++)
 #pragma unroll
             for (int mt = 0; mt < MT; mt++)
-              acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], kb, acc[mt], 0, 0, 0);
+#pragma unroll
+              for (int e = 0; e < 16; e++) acc[n][mt][e] = 0.f;
+          const unsigned char* kp = cur + (lane & 31) * kRowPitch + (lane >> 5) * D;
+#pragma unroll
+          for (int kk = 0; kk < KS; kk++) {
+            const bf16x8 kb0 = *(const bf16x8*)(kp + 16 * kk);
+            const bf16x8 kb1 = *(const bf16x8*)(kp + 32 * kRowPitch + 16 * kk);
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+              acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], kb0, acc[0][mt], 0, 0, 0);
+              acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], kb1, acc[1][mt], 0, 0, 0);
+            }
           }
-          float s = 0.f;
 #pragma unroll
-          for (int mt = 0; mt < MT; mt++)
+          for (int n = 0; n < 2; n++) {
+            float s = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[mt][i], s);
-          sc[n] = s + __shfl_xor(s, 32);
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+              for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[n][mt][i], s);
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+            sc[n] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);   // lanes l and l ^ 32 summed
+          }
         }
-        lds_barrier();   // the tile buffer may be refilled from here on
         // lane l takes key tile*64 + l: N-tile l/32, column l%32
         const int spos = tile * kKT + lane;
         const float v = (lane < 32) ? sc[0] : sc[1];
@@ -310,7 +387,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
         bool cnd = x > thr;
         uint64_t m = __ballot(cnd);
         if (count + __popcll(m) > kCap) {
-          thr = wave_select(ckey, cpos, count, K, whist);
+          thr = wave_select<false>(ckey, cpos, count, K, whist);
           cnd = x > thr;
           m = __ballot(cnd);
         }
@@ -323,7 +400,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
       }
       if (have_q && !all_keep) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
-        if (count > K) wave_select(ckey, cpos, count, K, whist);
+        if (count > K) wave_select<true>(ckey, cpos, count, K, whist);
         // count == K here (t + 1 > K keys were visible); positions ascend
         for (int i = lane; i < K; i += 64) row[i] = (i < count) ? (int32_t)cpos[i] : -1;
       }
@@ -335,7 +412,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
 }  // namespace
 
 size_t indexer_prefill_lds_bytes() {
-  return 2 * (size_t)kTileBytes + (size_t)kPfWaves * 2 * kCap * 4 + kPfWaves * 256 * 4 + kMaxPages * 4;
+  return 2 * (size_t)kTileBytes + (size_t)kPfWaves * 2 * kCap * 4 + kPfWaves * kHistWords * 4 + kMaxPages * 4;
 }
 
 int indexer_prefill_max_pages() { return kMaxPages; }
@@ -349,7 +426,8 @@ int indexer_prefill_grid(int total_q, int batch) {
 hipError_t launch_indexer_prefill(int dtype, int H, int D, const IndexerPrefillParams& p, hipStream_t st) {
   if (dtype != kBF16 || H != 64 || D != 128) return hipErrorInvalidValue;
   if (p.grid <= 0) return hipSuccess;
-  auto kern = indexer_prefill_kernel<64, 128>;
+  // pages of 64 tokens or more hold each 64-key tile whole
+  auto kern = p.bv.page_size >= kKT ? indexer_prefill_kernel<64, 128, true> : indexer_prefill_kernel<64, 128, false>;
   const size_t lds = indexer_prefill_lds_bytes();
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

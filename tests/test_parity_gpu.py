@@ -253,6 +253,13 @@ def test_chunked_prefill_after_cache():
     _run_prefill(case, _sample_prefill_queries(case, per_seq=25))
 
 
+def test_prefill_small_pages():
+    # 16-token pages: a 64-key tile spans four pages, each row looked up on its own
+    case = case_to(make_case("c3_prefill_bf16", 26, seq_len_range=(3100, 3100), q_len=900, page_size=16,
+                             topk=1024), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=30))
+
+
 def test_prefill_mixed_batch_zigzag_units():
     # sequences with different numbers of query blocks (odd, even, one) share a launch
     case = case_to(make_case("c3_prefill_bf16", 24, batch=3, seq_lens=[3000, 2100, 4100], q_lens=[130, 64, 257],

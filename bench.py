@@ -154,6 +154,8 @@ def main():
                     help="skip the extra all-32k-context measurement")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false",
                     help="skip the 32k causal prefill measurement")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="print only the 32k causal prefill measurement (--steps calls per stage)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -168,6 +170,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     B.lib()
+    if args.only_prefill:
+        print(json.dumps(prefill_line(torch, B, make_case, args.steps)), flush=True)
+        return
     seed = 2
     cases = [make_case(args.workload, seed, device="cuda", value_seed=seed + 100 * r) for r in range(args.sets)]
     calls = [B.Call(c) for c in cases]

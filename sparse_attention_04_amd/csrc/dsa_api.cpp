@@ -130,18 +130,20 @@ BatchView view_of(const dsa_batch* b, int page_size) {
 // ------------------------------------------------------ workspace planning ---
 
 struct SfaPlan {
-  int splits, rows_per_split;
+  int splits, rows_per_split, hsplit;
   size_t part_o_bytes, part_ml_bytes;
 };
 
 SfaPlan plan_sfa(const dsa_batch* b, int H, int Dv, int topk, bool bf16) {
   SfaPlan pl{};
-  // A workgroup serves one (token, range of index slots) with all heads.
-  // With few tokens the slot ranges are split until about kSfaTargetWG
-  // workgroups exist.  Ranges are multiples of the row tile and hold at most
-  // kSfaMaxRows slots.
-  (void)bf16;
-  const int64_t units = std::max<int64_t>(1, (int64_t)b->total_q);
+  // A workgroup serves one (token, range of index slots) with all heads, or
+  // in launches with few tokens (decode, bf16) with half of them: two
+  // workgroups per token then share the heads, which halves the split
+  // partials and the q each workgroup loads.  The slot ranges are split
+  // until about kSfaTargetWG workgroups exist.  Ranges are multiples of the
+  // row tile and hold at most kSfaMaxRows slots.
+  pl.hsplit = (bf16 && (int64_t)b->total_q < kSfaTargetWG) ? 2 : 1;
+  const int64_t units = std::max<int64_t>(1, (int64_t)b->total_q * pl.hsplit);
   int splits = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(1, topk / 64), kSfaTargetWG / units));
   splits = std::max(splits, (topk + kSfaMaxRows - 1) / kSfaMaxRows);
   int rps = (int)align_up((size_t)((topk + splits - 1) / splits), kSfaRowTile);
@@ -319,6 +321,7 @@ dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx
   p.topk = topk;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
   p.splits = pl.splits;
+  p.hsplit = pl.hsplit;
   p.rows_per_split = pl.rows_per_split;
   // Launches with fewer query tokens than workgroup slots (decode) are bound
   // by memory and latency, so the matrix units can afford the weight

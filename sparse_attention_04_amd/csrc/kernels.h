@@ -73,6 +73,7 @@ struct SfaParams {
   int32_t topk;
   float scale_log2;        // softmax_scale * log2(e)
   int32_t splits;          // ranges of index slots per token
+  int32_t hsplit;          // workgroups sharing one token's heads (bf16: 1 or 2; grid y)
   int32_t precise_weights; // bf16: also multiply in the bf16 rounding residuals of the weights
   int32_t rows_per_split;  // multiple of the row tile
   void* out;               // splits == 1: final [total_q][H][Dv] in q dtype

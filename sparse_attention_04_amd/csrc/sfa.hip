@@ -101,13 +101,17 @@ __device__ __forceinline__ void lds_wait(s16x4& a, s16x4& b) {
 
 // bf16 SFA, H = 128, Dqk = 576, Dv = 512.
 //
-// A workgroup serves all 128 heads of one token for one range of index slots,
-// with 4 waves, one per SIMD, so each wave may use the whole register file.
-// Wave w owns the 32 heads 32w .. 32w+31 as two 16-head groups ht: q^T for
-// all 576 dims stays in registers (144 VGPRs) and the O^T accumulators for all
-// 512 columns (256) live in the accumulation registers.  Each K/V operand read
-// from LDS feeds both head groups, and a gathered row is brought on chip once
-// per token and range.
+// A workgroup serves 64 * HG heads of one token (all 128 with HG = 2; with
+// HG = 1 two workgroups share the token, grid y picking the half) for one
+// range of index slots, with 4 waves, one per SIMD, so each wave may use the
+// whole register file.  Wave w owns 16 * HG heads as HG groups ht of 16: q^T
+// for all 576 dims stays in registers (72 VGPRs per group) and the O^T
+// accumulators for all 512 columns (128 per group) live in the accumulation
+// registers.  Each K/V operand read from LDS feeds every head group of the
+// wave.  HG = 2 brings a gathered row on chip once per token and range;
+// HG = 1 (launches with few tokens) gathers it twice, with the two reads
+// close together on one XCD, and in return halves the split partials and the
+// q each workgroup loads.
 //
 // Per tile of 32 index slots:
 //   S^T[row, head] = KV[row, :] . q[head, :]     16x16x32 bf16 MFMAs, rows on M
@@ -139,7 +143,7 @@ struct SfaBf16Geom {
   static constexpr size_t lds_bytes(int rows) { return (size_t)NBUF * TILE + (size_t)rows * 4; }
 };
 
-template <int DQK, int DV, bool LO>
+template <int DQK, int DV, bool LO, int HG>
 __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams p) {
   using G = SfaBf16Geom<DQK, DV>;
   constexpr int ROWB = G::ROWB, PITCH = G::PITCH, TR = G::TR, TILE = G::TILE, NBUF = G::NBUF;
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
   // Optional phase clocks of the first workgroup's first wave, compiled in
   // only with DSA_SFA_PHASES (they cost registers the tile loop needs).
 #ifdef DSA_SFA_PHASES
-  const bool prof = p.dbg && blockIdx.x == 0 && blockIdx.z == 0 && tid == 0;
+  const bool prof = p.dbg && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0;
   unsigned long long ph[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   unsigned long long tprev = prof ? __builtin_amdgcn_s_memtime() : 0;
 #define DSA_PHASE(i)                                             \
@@ -229,20 +233,27 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
 
   // q^T as the B operand of S^T = KV q^T (16x16x32): for head group ht, lane l
   // holds head 32*wave + 16*ht + l%16 and dims 32*k + 8*(l/16) .. +7 of K-step k.
-  const int head0 = 32 * wave + l16;
-  bf16x8 qb[2][KS];
+  // heads of this workgroup: 64 * HG starting at 64 * HG * blockIdx.y; wave w
+  // holds HG groups of 16
+  const int head0 = 64 * HG * blockIdx.y + 16 * HG * wave + l16;
+  bf16x8 qb[HG][KS];
 #pragma unroll
-  for (int ht = 0; ht < 2; ht++) {
+  for (int ht = 0; ht < HG; ht++) {
     const bf16x8* qs = (const bf16x8*)((const uint16_t*)p.q + ((size_t)g * H + head0 + 16 * ht) * DQK);
 #pragma unroll
     for (int k = 0; k < KS; k++) qb[ht][k] = qs[4 * k + grp];
   }
-  f32x4 o[2][MV];
+  f32x4 o[HG][MV];
 #pragma unroll
-  for (int ht = 0; ht < 2; ht++)
+  for (int ht = 0; ht < HG; ht++)
 #pragma unroll
     for (int i = 0; i < MV; i++) o[ht][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[HG], l_run[HG];
+#pragma unroll
+  for (int ht = 0; ht < HG; ht++) {
+    m_run[ht] = -INFINITY;
+    l_run[ht] = 0.f;
+  }
   // Every compiler-visible load is complete before the tile loop, so the
   // compiler's own waits never count the loop's asm-issued tile loads.  (This
   // also waits for the first tiles, which the first iterations need anyway.)
@@ -270,11 +281,11 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     const unsigned char* cur = sfa_smem + (tile % NBUF) * TILE;
 
     // ---- S^T[row, head]: two 16-row M-tiles x two 16-head groups
-    f32x4 s[2][2];
+    f32x4 s[2][HG];
 #pragma unroll
     for (int rt = 0; rt < 2; rt++)
 #pragma unroll
-      for (int ht = 0; ht < 2; ht++) s[rt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < HG; ht++) s[rt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
       // K-step k reads dims 32k + 8*grp .. +7 of rows l%16 and 16 + l%16;
       // QD steps are in flight at a time
@@ -291,7 +302,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
         constexpr int sl = k % QD;
         lds_wait<2 * (k + QD <= KS ? QD - 1 : KS - 1 - k)>(a[sl][0], a[sl][1]);
 #pragma unroll
-        for (int ht = 0; ht < 2; ht++) {
+        for (int ht = 0; ht < HG; ht++) {
           s[0][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][0], qb[ht][k], s[0][ht], 0, 0, 0);
           s[1][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][1], qb[ht][k], s[1][ht], 0, 0, 0);
         }
@@ -312,9 +323,9 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     // by less than ~150 (overflow there shows up as a non-finite output); terms
     // more than ~80 below it are flushed and negligible next to the first
     // maximum's own weight.  The normalised result does not depend on m_ref.
-    bf16x8 phi[2], plo[2];
+    bf16x8 phi[HG], plo[HG];
 #pragma unroll
-    for (int ht = 0; ht < 2; ht++) {
+    for (int ht = 0; ht < HG; ht++) {
       float z[8];
       float mt = -INFINITY;
 #pragma unroll
@@ -376,7 +387,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
                           v[sl][1][0], v[sl][1][1], v[sl][1][2], v[sl][1][3]};
         const bf16x8 am = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
-        for (int ht = 0; ht < 2; ht++) {
+        for (int ht = 0; ht < HG; ht++) {
           o[ht][mv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, phi[ht], o[ht][mv], 0, 0, 0);
           if constexpr (LO) o[ht][mv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, plo[ht], o[ht][mv], 0, 0, 0);
         }
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
 
   // ---- epilogue: o[ht][mv][i] holds head head0 + 16*ht, v = 16*mv + 4*grp + i
 #pragma unroll
-  for (int ht = 0; ht < 2; ht++) {
+  for (int ht = 0; ht < HG; ht++) {
     float l = l_run[ht];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
@@ -586,17 +597,21 @@ hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hip
   if (p.bv.total_q == 0) return hipSuccess;
   if (dtype == kBF16 && H == 128 && Dqk == 576 && Dv == 512) {
     if (p.rows_per_split > kSfaMaxRows) return hipErrorInvalidValue;
-    const void* kern = p.precise_weights ? (const void*)sfa_bf16_kernel<576, 512, true>
-                                         : (const void*)sfa_bf16_kernel<576, 512, false>;
+    // (precise weights, head groups of 16 per wave): 64 * HG heads per workgroup
+    const void* kern = nullptr;
+    if (p.precise_weights)
+      kern = (p.hsplit == 2) ? (const void*)sfa_bf16_kernel<576, 512, true, 1> : (const void*)sfa_bf16_kernel<576, 512, true, 2>;
+    else
+      kern = (p.hsplit == 2) ? (const void*)sfa_bf16_kernel<576, 512, false, 1> : (const void*)sfa_bf16_kernel<576, 512, false, 2>;
+    if (p.hsplit != 1 && p.hsplit != 2) return hipErrorInvalidValue;
     const size_t lds = SfaBf16Geom<576, 512>::lds_bytes(p.rows_per_split);
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int chunk = (p.bv.total_q + 7) / 8;
-    const dim3 grid(8 * chunk, 1, p.splits);
-    if (p.precise_weights)
-      hipLaunchKernelGGL((sfa_bf16_kernel<576, 512, true>), grid, dim3(kSfaBf16Threads), lds, st, p);
-    else
-      hipLaunchKernelGGL((sfa_bf16_kernel<576, 512, false>), grid, dim3(kSfaBf16Threads), lds, st, p);
+    const dim3 grid(8 * chunk, p.hsplit, p.splits);
+    void* args[] = {(void*)&p};
+    e = hipLaunchKernel(kern, grid, dim3(kSfaBf16Threads), args, lds, st);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
   }
   if (dtype == kF32 && H == 8 && Dqk == 80 && Dv == 64) {

@@ -118,6 +118,7 @@ struct MfmaScorer<kBF16, H, D> {
 #pragma unroll
     for (int kk = 0; kk < KS; kk++) t.v[kk] = src[kk];
   }
+
   __device__ float score(const IndexerDecodeParams& p, int64_t row, const Tile& t) const {
     f32x16 acc[MT];
 #pragma unroll
@@ -184,6 +185,7 @@ struct MfmaScorerF8 {
     }
   }
   struct Tile { i32x8 v[KS]; uint32_t sc; };
+
   __device__ void load_tile(const IndexerDecodeParams& p, int64_t row, Tile& t) const {
     const int lane = threadIdx.x & 63, h = lane >> 5;
     const uint8_t* kr = (const uint8_t*)p.k_data + row * D;
@@ -389,35 +391,45 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
     constexpr int kAhead = (DT == kFP8 || DT == kMX) ? 4 : 2;
     constexpr int RD = kAhead + 1;
     const int ntiles = (nloc + 31) / 32;
-    auto fetch = [&](int tile, Tile& t) {
-      if (tile < ntiles) {
-        const int s = min(s0 + 32 * tile + (lane & 31), s1 - 1);
-        const int page = staged ? s_bt[(s >> PS) - pg0] : bt[s >> PS];
-        scorer.load_tile(p, ((int64_t)page << PS) + (s & (P - 1)), t);
-      }
-    };
-    for (int q = 0; q < T && q < MAXQ; q++) {
-      if (s_state[q] != kActive) continue;
-      const int t = L - T + q;
-      scorer.load_query(p, tok0 + q);
-      uint32_t* scq = sc + (size_t)q * p.chunk_cap;
-      Tile ring[RD];
+    // STAGED: the page table slice is in LDS (always, by the host's sizing);
+    // the other instance is the fallback that reads it from memory.  Kept as
+    // two loops so the staged one's lookups stay LDS loads: a pointer that
+    // may point to either compiles to flat loads, which count as memory loads,
+    // so the wait for a page id would drain the whole tile ring.
+    auto score_range = [&](auto staged_c) {
+      constexpr bool STAGED = decltype(staged_c)::value;
+      auto page_of = [&](int s) { return STAGED ? s_bt[(s >> PS) - pg0] : bt[s >> PS]; };
+      auto fetch = [&](int tile, Tile& t) {
+        if (tile < ntiles) {
+          const int s = min(s0 + 32 * tile + (lane & 31), s1 - 1);
+          scorer.load_tile(p, ((int64_t)page_of(s) << PS) + (s & (P - 1)), t);
+        }
+      };
+      for (int q = 0; q < T && q < MAXQ; q++) {
+        if (s_state[q] != kActive) continue;
+        const int t = L - T + q;
+        scorer.load_query(p, tok0 + q);
+        uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+        Tile ring[RD];
 #pragma unroll
-      for (int d = 0; d < RD - 1; d++) fetch(wave + d * kIdxWaves, ring[d]);
-      for (int base = wave; base < ntiles; base += RD * kIdxWaves) {
+        for (int d = 0; d < RD - 1; d++) fetch(wave + d * kIdxWaves, ring[d]);
+        for (int base = wave; base < ntiles; base += RD * kIdxWaves) {
 #pragma unroll
-        for (int d = 0; d < RD; d++) {
-          const int tile = base + d * kIdxWaves;
-          if (tile < ntiles) {
-            // refill the slot of the previous tile with the one kAhead later
-            fetch(tile + kAhead * kIdxWaves, ring[(d + RD - 1) % RD]);
-            const float v = scorer.score(p, 0, ring[d]);
-            const int s = s0 + 32 * tile + lane;
-            if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
+          for (int d = 0; d < RD; d++) {
+            const int tile = base + d * kIdxWaves;
+            if (tile < ntiles) {
+              // refill the slot of the previous tile with the one kAhead later
+              fetch(tile + kAhead * kIdxWaves, ring[(d + RD - 1) % RD]);
+              const float v = scorer.score(p, 0, ring[d]);
+              const int s = s0 + 32 * tile + lane;
+              if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
+            }
           }
         }
       }
-    }
+    };
+    if (staged) score_range(std::true_type{});
+    else score_range(std::false_type{});
   }
   __syncthreads();
   DSA_STAMP(2);
@@ -638,6 +650,7 @@ struct MfmaScorer<kF32, H, D> {
     }
   }
   struct Tile { float k[D]; };
+
   __device__ void load_tile(const IndexerDecodeParams& p, int64_t row, Tile& t) const {
     const float* src = (const float*)p.k_data + row * D;
 #pragma unroll

@@ -446,28 +446,46 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p, int H) {
   const int c0 = (threadIdx.x & 63) * CPT;
   const int S = p.splits;
   if (h >= H) return;
-  float mx = -INFINITY;
-  for (int j = 0; j < S; j++) mx = fmaxf(mx, p.part_ml[((size_t)g * S + j) * H + h]);
+  // Splits go in groups of 4 whose log-sum-exps and partials are all loaded
+  // before any is used (one memory round trip per group); the running
+  // maximum rescales what earlier groups accumulated.
+  float mx = -INFINITY, den = 0.f;
   float acc[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; c++) acc[c] = 0.f;
-  float den = 0.f;
-  for (int j = 0; j < S; j++) {
-    const float l = p.part_ml[((size_t)g * S + j) * H + h];
-    if (l == -INFINITY) continue;
-    const float wj = exp2f(l - mx);
-    den += wj;
-    const float* src = p.part_o + (((size_t)g * S + j) * H + h) * DV + c0;
-    if constexpr (CPT % 4 == 0) {
+  for (int j0 = 0; j0 < S; j0 += 4) {
+    float l[4];
+    float v[4][CPT];
 #pragma unroll
-      for (int c = 0; c < CPT; c += 4) {
-        const f32x4 v = *(const f32x4*)(src + c);
-        acc[c] += wj * v[0]; acc[c + 1] += wj * v[1]; acc[c + 2] += wj * v[2]; acc[c + 3] += wj * v[3];
+    for (int u = 0; u < 4; u++) {
+      const int j = min(j0 + u, S - 1);   // past the end: reloads the last split, masked below
+      l[u] = (j0 + u < S) ? p.part_ml[((size_t)g * S + j) * H + h] : -INFINITY;
+      const float* src = p.part_o + (((size_t)g * S + j) * H + h) * DV + c0;
+      if constexpr (CPT % 4 == 0) {
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4) {
+          const f32x4 t = *(const f32x4*)(src + c);
+          v[u][c] = t[0]; v[u][c + 1] = t[1]; v[u][c + 2] = t[2]; v[u][c + 3] = t[3];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPT; c++) v[u][c] = src[c];
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < CPT; c++) acc[c] += wj * src[c];
     }
+    const float mn = fmaxf(fmaxf(mx, fmaxf(l[0], l[1])), fmaxf(l[2], l[3]));
+    if (mn == -INFINITY) continue;          // no selected row so far
+    const float sc = exp2f(mx - mn);        // 0 while mx is still -inf
+    den *= sc;
+#pragma unroll
+    for (int c = 0; c < CPT; c++) acc[c] *= sc;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const float wj = (l[u] == -INFINITY) ? 0.f : exp2f(l[u] - mn);
+      den += wj;
+#pragma unroll
+      for (int c = 0; c < CPT; c++) acc[c] += wj * v[u][c];
+    }
+    mx = mn;
   }
   const float inv = (den > 0.f) ? 1.f / den : 0.f;
   if constexpr (BF16OUT && CPT % 4 == 0) {

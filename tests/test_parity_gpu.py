@@ -189,6 +189,79 @@ def test_c2_full_size_sampled():
         assert row.max() < case.seq_lens_host[tok]
 
 
+def _check_rows_valid(case, idx_h):
+    """Every row holds n = min(k, t + 1) distinct positions in [0, t], then -1."""
+    for b in range(case.batch):
+        L, T = int(case.seq_lens_host[b]), int(case.q_lens_host[b])
+        for i in range(T):
+            t = L - T + i
+            n = min(case.topk, t + 1)
+            row = idx_h[case.token(b, i)]
+            g = row[:n]
+            assert np.all(row[n:] == -1), (b, i)
+            assert g.min() >= 0 and g.max() <= t, (b, i)
+            assert len(np.unique(g)) == n, (b, i)
+
+
+@pytest.mark.parametrize("name", ["c4_decode_fp8", "c4_decode_mxfp8"])
+def test_c4_full_size_sampled(name):
+    """The quantised-indexer decode at full size (64 sequences, contexts
+    U[16384, 65536], 1 % outliers at +-20) in the launch configuration the
+    benchmark uses, checked on sampled queries and on the properties of every
+    row."""
+    _say(f"{name} full size: generating on device")
+    case = make_case(name, 4, device="cuda")
+    call = B.Call(case)
+    _say(f"{name} full size: fused_decode")
+    out, lse, idx = call.fused_decode()
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    qs = _queries(case, limit=3)
+    for (b, i) in qs:
+        _say(f"{name} full size: oracle query b={b} i={i}")
+        check_topk_row(idx_h[case.token(b, i)], oracle.run_query(case, b, i), case.topk)
+    _check_sfa_on(case, out, qs, idx_h)
+    _check_rows_valid(case, idx_h)
+
+
+def test_c5_chunked_prefill_full_size_sampled():
+    """8 sequences of 131072 cached tokens, the last 8192 of each a new chunk
+    (t = 122880 + i), at full size, checked on sampled queries (first and last
+    chunk tokens among them) and on the properties of every row."""
+    _say("c5 chunked prefill full size: generating on device")
+    case = make_case("c5_chunk_prefill", 5, device="cuda")
+    call = B.Call(case)
+    _say("c5 chunked prefill full size: fused_prefill")
+    out, lse, idx = call.fused_prefill()
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    T = int(case.q_lens_host[0])
+    qs = [(0, 0), (7, T - 1)] + [q for q in _queries(case, limit=2) if q not in ((0, 0), (7, T - 1))]
+    for (b, i) in qs:
+        _say(f"c5 chunked prefill full size: oracle query b={b} i={i}")
+        check_topk_row(idx_h[case.token(b, i)], oracle.run_query(case, b, i), case.topk)
+    _check_sfa_on(case, out, qs, idx_h)
+    _check_rows_valid(case, idx_h)
+
+
+def test_c5_decode4_full_size_sampled():
+    """4-token decode at 131072 tokens (8 sequences, causal among the 4 new
+    tokens) at full size, checked on sampled queries and every row."""
+    _say("c5 decode4 full size: generating on device")
+    case = make_case("c5_decode4", 5, device="cuda")
+    call = B.Call(case)
+    _say("c5 decode4 full size: fused_decode")
+    out, lse, idx = call.fused_decode()
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    qs = [(0, 0), (3, 3)] + [q for q in _queries(case, limit=2) if q not in ((0, 0), (3, 3))]
+    for (b, i) in qs:
+        _say(f"c5 decode4 full size: oracle query b={b} i={i}")
+        check_topk_row(idx_h[case.token(b, i)], oracle.run_query(case, b, i), case.topk)
+    _check_sfa_on(case, out, qs, idx_h)
+    _check_rows_valid(case, idx_h)
+
+
 def test_fused_equals_composition():
     case = case_to(make_case("c2_decode_bf16", 8, batch=3, seq_len_range=(3000, 5000)), "cuda")
     call = B.Call(case)

@@ -142,6 +142,41 @@ def prefill_line(torch, B, make_case, steps):
             "peak_tflops": MFMA_PEAK_TFLOPS["bf16"]}
 
 
+def config_line(torch, B, make_case, name, steps, warmup, sets):
+    """One more workload of the scope table: fused-call time and its rate
+    against the roof that bounds it (HBM for decode, MFMA for prefill)."""
+    cases = [make_case(name, 5 if name.startswith("c5") else 4, device="cuda", value_seed=r + 1)
+             for r in range(sets)]
+    calls = [B.Call(c) for c in cases]
+    prefill = cases[0].max_q_len > 4
+    op = B.DSA_OP_FUSED_PREFILL if prefill else B.DSA_OP_FUSED_DECODE
+    for c in calls:
+        c.workspace(op)
+    R = len(calls)
+    fn = (lambda s: calls[s % R].fused_prefill()) if prefill else (lambda s: calls[s % R].fused_decode())
+    ms = time_calls(fn, steps, warmup, torch)
+    a = algorithmic(cases[0])
+    out = {"workload": f"{name}: {CONFIGS_EXTRA[name]}", "ms_per_call": ms,
+           "tokens_per_s": cases[0].total_q / (ms * 1e-3), "value_sets_rotated": R}
+    if prefill:
+        peak = MFMA_PEAK_TFLOPS["bf16"] * 1e12
+        out["mfma_frac"] = (a["indexer_flops"] + a["sfa_flops"]) / (ms * 1e-3) / peak
+    else:
+        out["algorithmic_bytes"] = a["fused_bytes"]
+        out["step_hbm_frac"] = a["fused_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    del calls, cases
+    torch.cuda.empty_cache()
+    return out
+
+
+CONFIGS_EXTRA = {
+    "c4_decode_fp8": "decode, 64 sequences, contexts U[16384, 65536], FP8 indexer, 1 % outliers",
+    "c4_decode_mxfp8": "decode, 64 sequences, contexts U[16384, 65536], MXFP8 indexer, 1 % outliers",
+    "c5_chunk_prefill": "chunked prefill, 8 sequences, 8192 new tokens after 122880 cached",
+    "c5_decode4": "4-token decode, 8 sequences at 131072 tokens",
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +189,8 @@ def main():
                     help="skip the extra all-32k-context measurement")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false",
                     help="skip the 32k causal prefill measurement")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="skip the C4 and C5 measurements")
     ap.add_argument("--only-prefill", action="store_true",
                     help="print only the 32k causal prefill measurement (--steps calls per stage)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -257,6 +294,10 @@ def main():
         del c32
     if args.workload == "c2_decode_bf16" and args.prefill:
         line["prefill_32k"] = prefill_line(torch, B, make_case, 3)
+    if args.workload == "c2_decode_bf16" and args.extra:
+        line["other_configs"] = {
+            n: config_line(torch, B, make_case, n, *((3, 1, 1) if n == "c5_chunk_prefill" else (50, 5, 2)))
+            for n in CONFIGS_EXTRA}
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -26,7 +26,11 @@ What is computed (the method as the pages state it):
     on top of multi-head latent attention ([P1] sec. 1; [P3] sec. 1);
   * paged caches are read through a block table ([P4] sec. 3.2 "efficient paged
     addressing"; [P1] sec. 2 "directly reads paged KV cache");
-  * MXFP8: every 32 elements share one scale ([P1] sec. 3; [P2] sec. 4.2).
+  * MXFP8: every 32 elements share one scale ([P1] sec. 3; [P2] sec. 4.2);
+  * the SFA KV cache may be stored in FP8 with one scale per token, head and
+    tile of 128 elements ([P1] sec. 3, "FP8 Block Quantization for SFA KV
+    Cache"; [P2] sec. 4.3 and its table; [P3] quantisation item 2; [P4] sec. 4
+    and its table).
 
 Readings where the pages are silent (each is listed in the design notes):
   * no activation on per-head scores; the weighted combination is a sum over
@@ -36,7 +40,11 @@ Readings where the pages are silent (each is listed in the design notes):
   * query i of a sequence with T_b new tokens and L_b cached keys sits at
     t = L_b - T_b + i;
   * SFA uses the absorbed (MQA) MLA form: one latent row per position shared by
-    every head; logits over all qk dims, V = the first d_v dims of the row.
+    every head; logits over all qk dims, V = the first d_v dims of the row;
+  * in that form the latent row is the one "head" of the FP8 KV cache: a row of
+    576 = 512 latent + 64 rope elements is 5 tiles, the last one 64 long (a row
+    shorter than 128 is one tile); each scale is an fp32 that multiplies the
+    decoded e4m3 values of its tile.
 
 Every function here is pinned by tests that do not retype its formula
 (brute-force loops, library routines, closed forms and invariants).
@@ -86,6 +94,9 @@ def decode_e8m0(bits) -> np.ndarray:
     return np.where(e == 255, np.nan, v)
 
 
+KV_TILE = 128   # elements per scale tile of an FP8 SFA KV row
+
+
 def decode_values(raw, dtype: str, scale=None, group: int = 32) -> np.ndarray:
     """Storage -> float64 for one tensor slice whose last axis is the element axis.
 
@@ -96,6 +107,10 @@ def decode_values(raw, dtype: str, scale=None, group: int = 32) -> np.ndarray:
                    head for queries)
     dtype 'mxfp8': raw e4m3 bytes; ``scale`` holds one e8m0 byte per group of
                    ``group`` consecutive elements ([P1] sec. 3, [P2] sec. 4.2)
+    dtype 'fp8_t128': raw e4m3 bytes; ``scale`` [..., ceil(D / 128)] holds one
+                   fp32 per tile of KV_TILE consecutive elements, the last tile
+                   possibly shorter ([P1] sec. 3, [P2] sec. 4.3: the SFA KV
+                   cache is quantised per token, head and tile of 128)
     """
     if dtype == "f32":
         return np.asarray(raw, np.float32).astype(np.float64)
@@ -110,6 +125,12 @@ def decode_values(raw, dtype: str, scale=None, group: int = 32) -> np.ndarray:
         shp = v.shape
         v = v.reshape(*shp[:-1], shp[-1] // group, group) * sc[..., None]
         return v.reshape(shp)
+    if dtype == "fp8_t128":
+        v = decode_e4m3(raw)
+        sc = np.asarray(scale, np.float64)
+        tile_of = np.arange(v.shape[-1]) // KV_TILE     # element c -> its tile
+        assert sc.shape[-1] == -(-v.shape[-1] // KV_TILE)
+        return v * sc[..., tile_of]
     raise ValueError(dtype)
 
 
@@ -205,8 +226,12 @@ def sfa_query(case, b: int, i: int, idx) -> tuple:
     """SFA for query i of sequence b over logical positions ``idx``."""
     tok = case.token(b, i)
     bt = _np(case.block_table[b])
+    kv_dtype = getattr(case, "kv_dtype", None) or case.sfa_dtype
+    kv_scale = getattr(case, "kv_scale", None)
     rows = decode_values(paged_rows(_np(case.kv_pool), bt, case.page_size, np.asarray(idx)),
-                         case.sfa_dtype)
+                         kv_dtype,
+                         None if kv_scale is None
+                         else paged_rows(_np(kv_scale), bt, case.page_size, np.asarray(idx)))
     q = decode_values(_np(case.q_s[tok]), case.sfa_dtype)
     return sparse_attention(q, rows, case.d_v, case.softmax_scale)
 

@@ -12,7 +12,10 @@ Optimization on Ascend CANN, section 2): a query, a paged K cache read through a
 block table, per-head weights, a Top-K size and per-sequence lengths.  The
 quantised storage formats follow the layered-quantisation sections of the same
 pages (MXFP8 with groups of 32 elements sharing one scale; FP8 with one fp32
-scale per token for keys and per token and head for queries).
+scale per token for keys and per token and head for queries; the SFA KV cache
+optionally in FP8 with one fp32 scale per tile of 128 elements of each row,
+"Adapting and Optimizing Inference for a New Model Architecture on Ascend",
+section 4.3).
 
 Recipe (fixed, documented):
   * every tensor has its own torch generator seeded from
@@ -21,7 +24,9 @@ Recipe (fixed, documented):
     (a different stream of numbers, still seeded and deterministic);
   * values are drawn in float32 and rounded to bf16 with round-to-nearest-even;
   * FP8 scale = amax / 448 (amax == 0 -> 1), elements x / scale rounded to
-    nearest-even and saturated to +-448 (OCP e4m3fn);
+    nearest-even and saturated to +-448 (OCP e4m3fn); amax is taken per row,
+    or per tile of 128 elements (the last tile of a row may be shorter) for the
+    tiled KV format;
   * MX scale exponent E = floor(log2 amax) - 8 clamped to e8m0's range, elements
     x * 2^-E saturated to +-448 (OCP MX v1.0 rule for e4m3 elements);
   * the tail of every sequence's last page, and one spare page that all unused
@@ -39,9 +44,11 @@ import torch
 
 # Storage dtype names used across the package.
 F32, BF16, FP8, MXFP8 = "f32", "bf16", "fp8", "mxfp8"
+FP8T = "fp8_t128"    # SFA KV rows: e4m3 bytes + one fp32 scale per 128-element tile
 
 E4M3_MAX = 448.0
 MX_GROUP = 32
+KV_TILE = 128
 
 # Tensor ids for per-tensor seeding (fixed: changing them changes every case).
 _TID = dict(seq_lens=1, pages=2, q_i=3, k_i=4, w=5, q_s=6, kv=7,
@@ -70,7 +77,9 @@ class Case:
       k_pool    [num_pages][P][D_I]  f32 / bf16 / uint8 (e4m3 bits)
       k_scale   None | f32 [num_pages][P] | uint8 [num_pages][P][D_I/32]
       q_s       [sum T][H_S][D_qk]   f32 / bf16
-      kv_pool   [num_pages][P][D_qk] f32 / bf16 (V = the first D_v columns)
+      kv_pool   [num_pages][P][D_qk] f32 / bf16, or uint8 (e4m3 bits) when
+                kv_dtype is fp8_t128 (V = the first D_v columns)
+      kv_scale  None | f32 [num_pages][P][ceil(D_qk / 128)] (fp8_t128)
     """
     name: str
     seed: int
@@ -102,6 +111,13 @@ class Case:
     # host copies of the small integer metadata (always on the CPU)
     seq_lens_host: np.ndarray = None
     q_lens_host: np.ndarray = None
+    # storage of the latent KV rows: sfa_dtype (None), or fp8_t128 with kv_scale
+    kv_dtype: Optional[str] = None
+    kv_scale: Optional[torch.Tensor] = None
+
+    def __post_init__(self):
+        if self.kv_dtype is None:
+            self.kv_dtype = self.sfa_dtype
 
     @property
     def total_q(self) -> int:
@@ -142,6 +158,21 @@ def quant_fp8_rows(x: torch.Tensor):
     amax = x.abs().amax(dim=-1)
     scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).float()
     return encode_e4m3(x / scale.unsqueeze(-1)), scale
+
+
+def quant_fp8_tiles(x: torch.Tensor, tile: int = KV_TILE):
+    """FP8 with one scale per tile of ``tile`` consecutive elements along the
+    last dim (the last tile may be shorter):
+    x [..., D] -> (bits uint8 [..., D], scale f32 [..., ceil(D / tile)])."""
+    x = x.float()
+    D = x.shape[-1]
+    nt = -(-D // tile)
+    xp = torch.nn.functional.pad(x, (0, nt * tile - D))
+    g = xp.reshape(*x.shape[:-1], nt, tile)
+    amax = g.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).float()
+    bits = encode_e4m3(g / scale.unsqueeze(-1)).reshape(*x.shape[:-1], nt * tile)[..., :D]
+    return bits.contiguous(), scale
 
 
 def quant_mx_rows(x: torch.Tensor):
@@ -194,6 +225,12 @@ PRESETS = {
     "c5_chunk_prefill": dict(batch=8, seq_len_range=(131072, 131072), q_len=8192, page_size=64,
                              h_i=64, d_i=128, topk=2048, idx_dtype=BF16, w_div=64.0,
                              h_s=128, d_qk=576, d_v=512, scale_dim=192, sfa_dtype=BF16, sfa_mult=1.0),
+    # The decode of c2_decode_bf16 with the SFA KV cache in FP8, one scale per
+    # tile of 128 elements of each latent row.
+    "c2_decode_fp8kv": dict(batch=32, seq_len_range=(4096, 32768), q_len=1, page_size=64,
+                            h_i=64, d_i=128, topk=2048, idx_dtype=BF16, w_div=64.0,
+                            h_s=128, d_qk=576, d_v=512, scale_dim=192, sfa_dtype=BF16, sfa_mult=0.1,
+                            kv_dtype=FP8T),
     # Long context: 4-token multi-query decode at 131072 tokens.
     "c5_decode4": dict(batch=8, seq_len_range=(131072, 131072), q_len=4, page_size=64,
                        h_i=64, d_i=128, topk=2048, idx_dtype=BF16, w_div=64.0,
@@ -222,6 +259,8 @@ def _encode(x: torch.Tensor, dtype: str):
         return quant_fp8_rows(x)
     if dtype == MXFP8:
         return quant_mx_rows(x)
+    if dtype == FP8T:
+        return quant_fp8_tiles(x)
     raise ValueError(dtype)
 
 
@@ -296,7 +335,8 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", value_seed: Optiona
     chunk = 1 << 16
 
     def storage_dtype(dt):
-        return {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.uint8, MXFP8: torch.uint8}[dt]
+        return {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.uint8, MXFP8: torch.uint8,
+                FP8T: torch.uint8}[dt]
 
     # 3. indexer q
     g, og = _gen(vseed, "q_i", dev), _gen(vseed, "out_q_i", dev)
@@ -322,12 +362,18 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", value_seed: Optiona
     for r0 in range(0, total_q, qrows):
         r1 = min(total_q, r0 + qrows)
         q_s[r0:r1] = _encode(_randn((r1 - r0, h_s, d_qk), g, dev, mult, outl, og), sdt)[0]
-    # 7. latent KV rows
-    kv_pool = torch.empty((num_pages, P, d_qk), dtype=storage_dtype(sdt), device=dev)
-    kv_pool.fill_(float("nan"))
+    # 7. latent KV rows (stored in sfa_dtype, or as FP8 tiles)
+    kdt = p.get("kv_dtype", sdt)
+    assert kdt == sdt or kdt == FP8T
+    kv_pool = torch.empty((num_pages, P, d_qk), dtype=storage_dtype(kdt), device=dev)
+    kv_pool.fill_(_poison_value(kv_pool))
+    kv_scale = None
+    if kdt == FP8T:
+        kv_scale = torch.full((num_pages, P, -(-d_qk // KV_TILE)), float("nan"),
+                              dtype=torch.float32, device=dev)
     g, og = _gen(vseed, "kv", dev), _gen(vseed, "out_kv", dev)
-    _fill_pool(kv_pool, None, lambda n: _randn((n, d_qk), g, dev, mult, outl, og),
-               n_keys, phys_t, sdt, chunk)
+    _fill_pool(kv_pool, kv_scale, lambda n: _randn((n, d_qk), g, dev, mult, outl, og),
+               n_keys, phys_t, kdt, chunk)
 
     cu_q = np.concatenate([[0], np.cumsum(q_lens)])
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a).astype(np.int32)).to(dev)
@@ -342,6 +388,7 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", value_seed: Optiona
         h_s=h_s, d_qk=d_qk, d_v=d_v, softmax_scale=1.0 / math.sqrt(p["scale_dim"]),
         sfa_dtype=sdt, q_s=q_s, kv_pool=kv_pool,
         seq_lens_host=seq_lens.astype(np.int32), q_lens_host=q_lens.astype(np.int32),
+        kv_dtype=kdt, kv_scale=kv_scale,
     )
 
 

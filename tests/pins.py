@@ -182,3 +182,48 @@ def pin_bf16(fn):
     x = torch.cat([x, torch.tensor([0.0, -0.0, 1.0, -2.5, 3.0e38], dtype=torch.bfloat16)])
     bits = x.view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(np.asarray(fn(bits)), x.to(torch.float64).numpy())
+
+
+# ------------------------------------------------------ FP8 tile-128 rows ---
+
+def read_golden_tile_row(path):
+    """The hand-worked FP8 tile-128 row: (bytes uint8 [D], scales [T], expected [D])."""
+    dim, scales, elems = None, None, []
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        f = line.split()
+        if f[0] == "dim":
+            dim = int(f[1])
+        elif f[0] == "scales":
+            scales = np.array([float(x) for x in f[1:]])
+        elif f[0] == "elem":
+            elems.append((int(f[1]), int(f[2], 16), float(f[3])))
+    raw = np.zeros(dim, np.uint8)
+    want = np.zeros(dim)
+    for i, byte, val in elems:
+        raw[i] = byte
+        want[i] = val
+    return raw, scales, want
+
+
+def pin_tile_decode(decode, golden_path):
+    """decode(raw, 'fp8_t128', scale) against (1) the hand-worked golden row and
+    (2) torch's float8_e4m3fn cast with each tile's scale spread by
+    repeat_interleave, on rows whose tiles differ in magnitude by 10^4 steps
+    (576 = 512 + 64: five tiles, the last short; 80: one short tile)."""
+    raw, sc, want = read_golden_tile_row(golden_path)
+    got = np.asarray(decode(raw[None], "fp8_t128", sc[None]))[0]
+    assert got.shape == want.shape and np.array_equal(got, want), (got, want)
+    r = _rng(77)
+    for D in (576, 80, 256):
+        T = -(-D // 128)
+        b = r.integers(0, 256, (5, D)).astype(np.uint8)
+        b[(b & 0x7F) == 0x7F] = 0x38                       # no NaN patterns
+        s = (10.0 ** (4 * np.arange(T)))[None] * r.uniform(0.5, 2.0, (5, T))
+        lib = torch.from_numpy(b).view(torch.float8_e4m3fn).double()
+        spread = torch.repeat_interleave(torch.from_numpy(s), 128, dim=1)[:, :D]
+        want = (lib * spread).numpy()
+        got = np.asarray(decode(b, "fp8_t128", s))
+        assert np.array_equal(got, want), D

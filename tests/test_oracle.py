@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import pins
-from sparse_attention_04_amd.inputs import make_case, quant_fp8_rows, quant_mx_rows
+from sparse_attention_04_amd.inputs import make_case, quant_fp8_rows, quant_fp8_tiles, quant_mx_rows
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -78,6 +78,32 @@ def test_input_quantisers_within_e4m3_error():
     # group amax lands in [256, 512) before saturation at 448 (OCP MX rule)
     g = np.abs(x.numpy()).reshape(50, 4, 32).max(-1) / 2.0 ** (e.numpy().astype(np.int64) - 127)
     assert np.all((g >= 256) & (g < 512))
+
+
+def test_fp8_tile128_decode_pins():
+    """The SFA KV cache's FP8 rows: one scale per tile of 128 elements."""
+    pins.pin_tile_decode(oracle.decode_values, os.path.join(GOLDEN, "kv_fp8_tile128.txt"))
+
+
+def test_tile_quantiser_within_e4m3_error():
+    """The input module's tile encoder: every tile's largest magnitude maps to
+    448 (so decodes to itself up to fp32 rounding of the scale) and every
+    element is within half an e4m3 ulp, whatever the other tiles hold."""
+    r = np.random.default_rng(11)
+    x = r.standard_normal((40, 576)).astype(np.float32)
+    x *= (10.0 ** (np.arange(576) // 128 - 2)).astype(np.float32)   # tiles 1e-2 .. 1e2
+    x[7, 130] = 0.0
+    x[8, 512:] = 0.0                                                # an all-zero tile
+    bits, sc = quant_fp8_tiles(torch.from_numpy(x))
+    assert bits.shape == (40, 576) and sc.shape == (40, 5)
+    back = oracle.decode_values(bits.numpy(), "fp8_t128", sc.numpy())
+    tile_sc = np.repeat(sc.numpy().astype(np.float64), 128, axis=1)[:, :576]
+    err = np.abs(back - x)
+    assert np.all(err <= np.maximum(np.abs(x) * 2 ** -4, tile_sc * 2 ** -10) + 1e-30)
+    amax = np.abs(x[:, :512]).reshape(40, 4, 128).max(-1)
+    assert np.allclose(np.abs(back[:, :512]).reshape(40, 4, 128).max(-1), amax, rtol=1e-6)
+    assert np.allclose(np.abs(back[:, 512:]).max(-1), np.abs(x[:, 512:]).max(-1), rtol=1e-6)
+    assert np.all(back[8, 512:] == 0.0) and sc[8, 4] == 1.0
 
 
 # -------------------------------------------------------------- scores ---
@@ -150,6 +176,34 @@ def test_case_poison_never_reached():
     # the poisoned tail exists
     last = c.block_table[0, (250 - 1) // 16]
     assert torch.isnan(c.k_pool[last, 250 % 16:]).all()
+
+
+def test_fp8_kv_case_wiring():
+    """SFA over an FP8 tile-128 KV cache: the oracle's paged gather of rows and
+    of their tile scales agrees with a route through torch's e4m3 cast and a
+    per-element scale spread by repeat_interleave; poisoned pool entries
+    (NaN scales, 0x7F bytes) are never reached."""
+    c = make_case("c2_decode_fp8kv", 4, batch=2, seq_len_range=(300, 700), topk=64)
+    assert c.kv_dtype == "fp8_t128" and c.kv_pool.dtype == torch.uint8
+    assert c.kv_scale.shape == (c.num_pages, c.page_size, 5)
+    for b in range(2):
+        idx = np.sort(np.random.default_rng(b).choice(int(c.seq_lens_host[b]), 64, replace=False))
+        out, lse = oracle.sfa_query(c, b, 0, idx)
+        assert np.isfinite(out).all() and np.isfinite(lse).all()
+        bt = c.block_table[b].long()
+        pos = torch.from_numpy(idx)
+        pg, off = bt[pos // c.page_size], pos % c.page_size
+        raw = c.kv_pool[pg, off].view(torch.float8_e4m3fn).double()
+        spread = torch.repeat_interleave(c.kv_scale[pg, off].double(), 128, dim=1)[:, :576]
+        rows = (raw * spread).numpy()
+        q = c.q_s[c.token(b, 0)].float().double().numpy()
+        o2, l2 = oracle.sparse_attention(q, rows, c.d_v, c.softmax_scale)
+        assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+    # the pool's unused rows are poisoned
+    last = c.block_table[0, (int(c.seq_lens_host[0]) - 1) // 64]
+    tail = int(c.seq_lens_host[0]) % 64
+    if tail:
+        assert (c.kv_pool[last, tail:] == 0x7F).all() and torch.isnan(c.kv_scale[last, tail:]).all()
 
 
 # -------------------------------------------------------------- zigzag ---
@@ -238,6 +292,29 @@ def _mutant_attn_v_from_tail(q, rows, d_v, scale):
 
 def _mutant_attn_sign(q, rows, d_v, scale):
     return oracle.sparse_attention(q, rows, d_v, -scale)
+
+
+def _mutant_tile_divides(raw, dtype, scale=None, group=32):
+    v = oracle.decode_e4m3(raw)
+    sc = np.asarray(scale, np.float64)
+    return v / sc[..., np.arange(v.shape[-1]) // 128]
+
+
+def _mutant_tile_64(raw, dtype, scale=None, group=32):
+    v = oracle.decode_e4m3(raw)
+    sc = np.asarray(scale, np.float64)
+    t = np.minimum(np.arange(v.shape[-1]) // 64, sc.shape[-1] - 1)
+    return v * sc[..., t]
+
+
+def _mutant_tile_first_scale(raw, dtype, scale=None, group=32):
+    return oracle.decode_e4m3(raw) * np.asarray(scale, np.float64)[..., :1]
+
+
+@pytest.mark.parametrize("mutant", [_mutant_tile_divides, _mutant_tile_64, _mutant_tile_first_scale])
+def test_tile_pin_catches_planted_mistakes(mutant):
+    with pytest.raises(AssertionError):
+        pins.pin_tile_decode(mutant, os.path.join(GOLDEN, "kv_fp8_tile128.txt"))
 
 
 def _mutant_e4m3_bias(t=None):

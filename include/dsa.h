@@ -61,7 +61,10 @@ typedef enum {
   DSA_F32 = 0,         /* float32                                                */
   DSA_BF16 = 1,        /* bfloat16                                               */
   DSA_FP8_E4M3 = 2,    /* OCP e4m3fn bytes + one float32 scale per row           */
-  DSA_MXFP8_E4M3 = 3   /* OCP e4m3fn bytes + one e8m0 scale byte per 32 elements */
+  DSA_MXFP8_E4M3 = 3,  /* OCP e4m3fn bytes + one e8m0 scale byte per 32 elements */
+  DSA_FP8_E4M3_TILE128 = 4  /* OCP e4m3fn bytes + one float32 scale per tile of 128
+                               consecutive elements of a row (the last tile of a
+                               row may be shorter): the SFA KV cache format      */
 } dsa_dtype;
 
 typedef enum {
@@ -74,6 +77,12 @@ typedef enum {
 /* A paged pool: data [num_pages][page_size][dim] elements of `dtype`.
  * scale: DSA_FP8_E4M3   -> float32 [num_pages][page_size] (one per token)
  *        DSA_MXFP8_E4M3 -> uint8 e8m0 [num_pages][page_size][dim / 32]
+ *        DSA_FP8_E4M3_TILE128 -> float32 [num_pages][page_size][ceil(dim / 128)]
+ *                          (element c of a row is byte c times scale c / 128;
+ *                          per token, head and tile of 128: "Adapting and
+ *                          Optimizing Inference for a New Model Architecture on
+ *                          Ascend", sec. 4.3; one head, the latent row, in the
+ *                          absorbed MLA form)
  *        otherwise NULL.                                                      */
 typedef struct {
   const void* data;
@@ -114,8 +123,10 @@ typedef struct {
 } dsa_indexer_args;
 
 /* SFA operands (absorbed MLA form: one latent row per position, shared by all heads).
- * q        device [total_q][n_heads][qk_dim] of q_dtype (== kv_cache->dtype, F32 or BF16)
- * kv_cache paged pool with dim == qk_dim; V is the first v_dim columns of a row.
+ * q        device [total_q][n_heads][qk_dim] of q_dtype (F32 or BF16)
+ * kv_cache paged pool with dim == qk_dim, dtype == q_dtype or
+ *          DSA_FP8_E4M3_TILE128 (rows decoded with their tile scales);
+ *          V is the first v_dim columns of a row.
  * Logits are softmax_scale * q_h . row over all qk_dim columns.                */
 typedef struct {
   const void* q;
@@ -127,9 +138,11 @@ typedef struct {
   const dsa_paged_cache* kv_cache;
 } dsa_sfa_args;
 
-/* Bytes of workspace the call needs (0 is possible).  Pointer fields are not
- * read; only the scalars are.  `topk` for DSA_OP_SPARSE_ATTN comes from
- * idx->topk when idx is given, else 2048. Returns 0 for an invalid op.        */
+/* Bytes of workspace the call needs (0 is possible).  Device pointers are not
+ * read; the scalars are, and sfa->kv_cache->dtype when sfa->kv_cache is not
+ * NULL (an FP8 KV cache changes the work split).  `topk` for
+ * DSA_OP_SPARSE_ATTN comes from idx->topk when idx is given, else 2048.
+ * Returns 0 for an invalid op.                                                */
 size_t dsa_workspace_size(int32_t op, const dsa_batch* batch,
                           const dsa_indexer_args* idx, const dsa_sfa_args* sfa);
 

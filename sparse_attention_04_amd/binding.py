@@ -17,10 +17,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = range(5)
-DSA_F32, DSA_BF16, DSA_FP8_E4M3, DSA_MXFP8_E4M3 = range(4)
+DSA_F32, DSA_BF16, DSA_FP8_E4M3, DSA_MXFP8_E4M3, DSA_FP8_E4M3_TILE128 = range(5)
 DSA_OP_INDEXER_TOPK, DSA_OP_SPARSE_ATTN, DSA_OP_FUSED_DECODE, DSA_OP_FUSED_PREFILL = range(4)
 
-DTYPE_CODE = {"f32": DSA_F32, "bf16": DSA_BF16, "fp8": DSA_FP8_E4M3, "mxfp8": DSA_MXFP8_E4M3}
+DTYPE_CODE = {"f32": DSA_F32, "bf16": DSA_BF16, "fp8": DSA_FP8_E4M3, "mxfp8": DSA_MXFP8_E4M3,
+              "fp8_t128": DSA_FP8_E4M3_TILE128}
 
 EXPORTED = ("dsa_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_fused_decode",
             "dsa_fused_prefill", "dsa_status_string", "dsa_last_error")
@@ -151,7 +152,9 @@ class Call:
         self.iargs = dsa_indexer_args(_ptr(c.q_i), idt, _ptr(c.q_i_scale), _ptr(c.w), c.h_i, c.d_i, c.topk,
                                       ctypes.pointer(self.k_cache))
         sdt = DTYPE_CODE[c.sfa_dtype]
-        self.kv_cache = dsa_paged_cache(_ptr(c.kv_pool), None, sdt, c.num_pages, c.page_size, c.d_qk)
+        kdt = DTYPE_CODE[getattr(c, "kv_dtype", None) or c.sfa_dtype]
+        self.kv_cache = dsa_paged_cache(_ptr(c.kv_pool), _ptr(getattr(c, "kv_scale", None)), kdt,
+                                        c.num_pages, c.page_size, c.d_qk)
         self.sargs = dsa_sfa_args(_ptr(c.q_s), sdt, c.h_s, c.d_qk, c.d_v, float(c.softmax_scale),
                                   ctypes.pointer(self.kv_cache))
         dev = c.q_s.device

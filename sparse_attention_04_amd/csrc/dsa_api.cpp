@@ -59,11 +59,14 @@ dsa_status check_batch(const dsa_batch* b) {
   return DSA_OK;
 }
 
+// `dtype` is the query dtype; with allow_tile8 the cache may instead hold
+// FP8 tile-128 rows (the SFA KV cache).
 dsa_status check_cache(const dsa_paged_cache* c, const char* name, int dim, int dtype,
-                       const dsa_batch* b) {
+                       const dsa_batch* b, bool allow_tile8 = false) {
   if (!c) return fail(DSA_ERR_INVALID_ARG, "%s is NULL", name);
   if (!c->data) return fail(DSA_ERR_INVALID_ARG, "%s->data is NULL", name);
-  if (c->dtype != dtype) return fail(DSA_ERR_INVALID_ARG, "%s->dtype %d differs from the query dtype %d", name, c->dtype, dtype);
+  if (c->dtype != dtype && !(allow_tile8 && c->dtype == DSA_FP8_E4M3_TILE128))
+    return fail(DSA_ERR_INVALID_ARG, "%s->dtype %d differs from the query dtype %d", name, c->dtype, dtype);
   if (c->dim != dim) return fail(DSA_ERR_INVALID_ARG, "%s->dim %d differs from %d", name, c->dim, dim);
   if (c->page_size < 1 || c->page_size > 4096 || (c->page_size & (c->page_size - 1)))
     return fail(DSA_ERR_UNSUPPORTED, "%s->page_size %d is not a power of two in [1, 4096]", name, c->page_size);
@@ -72,7 +75,8 @@ dsa_status check_cache(const dsa_paged_cache* c, const char* name, int dim, int 
     return fail(DSA_ERR_INVALID_ARG, "max_pages_per_seq * page_size < max_seq_len");
   if ((int64_t)c->num_pages * c->page_size >= (1ll << 31))
     return fail(DSA_ERR_UNSUPPORTED, "%s holds 2^31 rows or more", name);
-  const bool need_scale = (dtype == DSA_FP8_E4M3 || dtype == DSA_MXFP8_E4M3);
+  const bool need_scale = (c->dtype == DSA_FP8_E4M3 || c->dtype == DSA_MXFP8_E4M3 ||
+                           c->dtype == DSA_FP8_E4M3_TILE128);
   if (need_scale && !c->scale) return fail(DSA_ERR_INVALID_ARG, "%s->scale is NULL for a quantised dtype", name);
   return DSA_OK;
 }
@@ -102,7 +106,7 @@ dsa_status check_sfa(const dsa_batch* b, const dsa_sfa_args* a) {
     return fail(DSA_ERR_UNSUPPORTED, "sfa shape (dtype %d, heads %d, qk %d, v %d) is not compiled in; supported: f32 8x80/64, bf16 128x576/512",
                 a->q_dtype, a->n_heads, a->qk_dim, a->v_dim);
   if (!(a->softmax_scale > 0.f) || !(a->softmax_scale < 1e30f)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  return check_cache(a->kv_cache, "kv_cache", a->qk_dim, a->q_dtype, b);
+  return check_cache(a->kv_cache, "kv_cache", a->qk_dim, a->q_dtype, b, true);
 }
 
 int dt_kernel(int d) {
@@ -134,15 +138,17 @@ struct SfaPlan {
   size_t part_o_bytes, part_ml_bytes;
 };
 
-SfaPlan plan_sfa(const dsa_batch* b, int H, int Dv, int topk, bool bf16) {
+SfaPlan plan_sfa(const dsa_batch* b, int H, int Dv, int topk, bool bf16, bool kv8) {
   SfaPlan pl{};
   // A workgroup serves one (token, range of index slots) with all heads, or
   // in launches with few tokens (decode, bf16) with half of them: two
   // workgroups per token then share the heads, which halves the split
-  // partials and the q each workgroup loads.  The slot ranges are split
+  // partials and the q each workgroup loads.  Over an FP8 KV cache the
+  // workgroups always take half of the heads (the registers of the per-tile
+  // scale products do not fit next to all 128).  The slot ranges are split
   // until about kSfaTargetWG workgroups exist.  Ranges are multiples of the
   // row tile and hold at most kSfaMaxRows slots.
-  pl.hsplit = (bf16 && (int64_t)b->total_q < kSfaTargetWG) ? 2 : 1;
+  pl.hsplit = (bf16 && (kv8 || (int64_t)b->total_q < kSfaTargetWG)) ? 2 : 1;
   const int64_t units = std::max<int64_t>(1, (int64_t)b->total_q * pl.hsplit);
   int splits = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(1, topk / 64), kSfaTargetWG / units));
   splits = std::max(splits, (topk + kSfaMaxRows - 1) / kSfaMaxRows);
@@ -312,11 +318,14 @@ dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx
                    void* out, float* lse, unsigned char* ws, hipStream_t st) {
   if (b->total_q == 0) return DSA_OK;
   const bool bf16 = (a->q_dtype == DSA_BF16);
-  const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, bf16);
+  const bool kv8 = (a->kv_cache->dtype == DSA_FP8_E4M3_TILE128);
+  const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, bf16, kv8);
   SfaParams p{};
   p.bv = view_of(b, a->kv_cache->page_size);
   p.q = a->q;
   p.kv = a->kv_cache->data;
+  p.kv8 = kv8 ? 1 : 0;
+  p.kv_scale = p.kv8 ? (const float*)a->kv_cache->scale : nullptr;
   p.idx = idx;
   p.topk = topk;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
@@ -342,7 +351,8 @@ dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx
 }
 
 size_t sfa_bytes(const dsa_batch* b, const dsa_sfa_args* a, int topk) {
-  const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, a->q_dtype == DSA_BF16);
+  const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, a->q_dtype == DSA_BF16,
+                             a->kv_cache && a->kv_cache->dtype == DSA_FP8_E4M3_TILE128);
   return pl.part_o_bytes + pl.part_ml_bytes + kProfileBytes;
 }
 

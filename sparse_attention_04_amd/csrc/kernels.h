@@ -68,7 +68,9 @@ hipError_t launch_indexer_prefill(int dtype, int H, int D, const IndexerPrefillP
 struct SfaParams {
   BatchView bv;
   const void* q;           // [total_q][H][Dqk]
-  const void* kv;          // [num_pages][P][Dqk]
+  const void* kv;          // [num_pages][P][Dqk] in the q dtype, or e4m3 bytes with kv8
+  const float* kv_scale;   // kv8: f32 [num_pages][P][ceil(Dqk / 128)], one per tile of 128
+  int32_t kv8;             // rows are FP8 e4m3 with per-tile scales
   const int32_t* idx;      // [total_q][topk]
   int32_t topk;
   float scale_log2;        // softmax_scale * log2(e)

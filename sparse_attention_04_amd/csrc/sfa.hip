@@ -19,6 +19,17 @@
 //   O^T[v, head] += V^T[v, row] P^T[row, head]   (V^T read with ds_read_b64_tr_b16).
 // Slots holding -1 are masked.  With several slot ranges per token, each range
 // writes a normalised partial and its log-sum-exp, merged by sfa_combine.
+//
+// FP8 KV cache (e4m3 bytes, one fp32 scale per token and tile of 128 elements
+// of the latent row: Adapting and Optimizing Inference for a New Model
+// Architecture on Ascend, sec. 4.3): the gather brings the 576-byte rows and
+// their five scales into an LDS staging ring, and the workgroup converts each
+// tile of rows once into the bf16 tile layout above.  The conversion is exact
+// (every e4m3 value is a bf16 value) and leaves the scales out; they enter in
+// fp32: S^T is accumulated per 128-column tile and each partial is multiplied
+// by its rows' scales before it is summed, and the softmax weights are
+// multiplied by the scale of each 128-column V tile before they are rounded
+// into the PV product's operand.
 #include "common.h"
 #include "kernels.h"
 
@@ -52,6 +63,11 @@ __device__ __forceinline__ void lds_barrier() {
 // the kernel orders them itself with explicit vmcnt waits and barriers.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+
+// The 4-byte form (64 lanes fill lds_base .. +255 in lane order).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -143,16 +159,48 @@ struct SfaBf16Geom {
   static constexpr size_t lds_bytes(int rows) { return (size_t)NBUF * TILE + (size_t)rows * 4; }
 };
 
-template <int DQK, int DV, bool LO, int HG>
+// FP8 rows: a staging ring of NBUF tiles of TR raw rows (no pad: the rows are
+// only read row-wise, by the dequantising pass) plus their scales, and two
+// bf16 tiles in the layout above for the matrix products.
+template <int DQK, int DV>
+struct SfaKv8Geom {
+  using B = SfaBf16Geom<DQK, DV>;
+  static constexpr int TR = B::TR, NW = B::NW;
+  static constexpr int NT = (DQK + 127) / 128;           // scale tiles per row (5)
+  static constexpr int STG = TR * DQK;                   // staging bytes per tile (18432)
+  static constexpr int RLOADS = STG / 1024;              // 1-KiB row loads per tile (18)
+  static constexpr int SLOADS = (TR * NT * 4 + 255) / 256;  // 256-byte scale loads per tile (3)
+  static constexpr int SBYTES = SLOADS * 256;            // LDS bytes of one tile's scales
+  static constexpr int LOADS = RLOADS + SLOADS;          // 21
+  static constexpr int LPW = (LOADS + NW - 1) / NW;      // loads of wave 0 per tile (6)
+  static constexpr int NBUF = 4;                         // staged tiles in flight
+  static constexpr int UNITS = TR * DQK / 8;             // 8-element units dequantised per tile
+  static_assert(STG % 1024 == 0 && DQK % 16 == 0, "row loads tile the staging buffer");
+  static_assert(LOADS % NW == 1, "wave 0 issues one load more than the others");
+  static_assert(UNITS % kSfaBf16Threads == 0, "dequantising units split evenly");
+  static constexpr int SCOPY = TR * NT * 4;              // scale table of one converted tile (640)
+  static_assert(SCOPY % 16 == 0, "scale tables copy in 16-byte pieces");
+  // [2 bf16 tiles][2 scale tables][NBUF staged tiles][NBUF staged scale tables][row table]
+  static constexpr size_t tscale_off() { return 2 * (size_t)B::TILE; }
+  static constexpr size_t stage_off() { return tscale_off() + 2 * (size_t)SCOPY; }
+  static constexpr size_t scale_off() { return stage_off() + (size_t)NBUF * STG; }
+  static constexpr size_t rows_off() { return scale_off() + (size_t)NBUF * SBYTES; }
+  static constexpr size_t lds_bytes(int rows) { return rows_off() + (size_t)rows * 4; }
+};
+
+template <int DQK, int DV, bool LO, int HG, bool KV8>
 __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams p) {
   using G = SfaBf16Geom<DQK, DV>;
-  constexpr int ROWB = G::ROWB, PITCH = G::PITCH, TR = G::TR, TILE = G::TILE, NBUF = G::NBUF;
-  constexpr int NW = G::NW, LPW = G::LPW;
+  using G8 = SfaKv8Geom<DQK, DV>;
+  constexpr int ROWB = G::ROWB, PITCH = G::PITCH, TR = G::TR, TILE = G::TILE;
+  constexpr int NBUF = KV8 ? G8::NBUF : G::NBUF;
+  constexpr int NW = G::NW, LPW = KV8 ? G8::LPW : G::LPW;
   constexpr int KS = DQK / 32;               // QK^T K-steps of 32 (18)
   constexpr int MV = DV / 16;                // PV M-tiles of 16 columns (32)
+  static_assert(DQK % 32 == 0 && (!KV8 || DV % 128 == 0), "FP8 scale tiles cover whole K-steps and M-tiles");
   constexpr int H = 128;
   extern __shared__ __attribute__((aligned(16))) unsigned char sfa_smem[];
-  int32_t* s_rows = (int32_t*)(sfa_smem + NBUF * TILE);   // [rows_per_split]
+  int32_t* s_rows = (int32_t*)(sfa_smem + (KV8 ? G8::rows_off() : (size_t)NBUF * TILE));  // [rows_per_split]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, l16 = lane & 15;
@@ -203,6 +251,76 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
   // LPW loads, the others LPW - 1); lanes that land on a pad or past row 31
   // load chunk 0 of the tile's row 0.
   const int nld = (wave == 0) ? LPW : LPW - 1;
+  // FP8 rows: load c (< G8::LOADS) of a tile is issued by wave c % NW.  Loads
+  // below RLOADS fill staging bytes 1024c .. +1023 (rows are 16-byte
+  // multiples, so a lane's 16 bytes never straddle two rows); the others fill
+  // the tile's scale table s[t][r] (t < NT, r < TR) 64 floats at a time, lanes
+  // past the table loading a row's first scale into the pad.
+  auto issue8 = [&](int tile) {
+    const int slot = tile % NBUF;
+    const uint32_t stg = lds_addr(sfa_smem + G8::stage_off() + (size_t)slot * G8::STG);
+    const uint32_t scl = lds_addr(sfa_smem + G8::scale_off() + (size_t)slot * G8::SBYTES);
+    int lo = lane * 16;
+    asm volatile("" : "+v"(lo));
+    int rows[LPW];
+    const unsigned char* src[LPW];
+#pragma unroll
+    for (int k = 0; k < LPW; k++) {
+      const int c = wave + NW * k;
+      int r, col;
+      if (c < G8::RLOADS) {
+        const int off = c * 1024 + lo;
+        r = off / DQK;
+        col = off - r * DQK;
+      } else {
+        const int e = (c - G8::RLOADS) * 64 + lane;
+        const bool real = e < TR * G8::NT;
+        r = real ? e % TR : 0;
+        col = real ? 4 * (e / TR) : 0;
+      }
+      const int slot_r = tile * TR + r;
+      rows[k] = (slot_r < nslots && k < nld) ? s_rows[slot_r] : -1;
+      const int row = (rows[k] < 0) ? fallback : rows[k];
+      src[k] = (c < G8::RLOADS) ? (const unsigned char*)p.kv + (size_t)row * DQK + col
+                                : (const unsigned char*)p.kv_scale + (size_t)row * (4 * G8::NT) + col;
+    }
+#pragma unroll
+    for (int k = 0; k < LPW; k++) {
+      if (k < LPW - 1 || wave == 0) {
+        const int c = wave + NW * k;
+        if (c < G8::RLOADS)
+          dma16(src[k], __builtin_amdgcn_readfirstlane(stg + c * 1024));
+        else
+          dma4(src[k], __builtin_amdgcn_readfirstlane(scl + (c - G8::RLOADS) * 256));
+      }
+    }
+  };
+  // Convert staged tile `tile` into bf16 buffer tile & 1: each thread turns
+  // UNITS / 256 runs of 8 bytes into 8 bf16 values (exact; scale 1), and the
+  // tile's scale table moves next to the buffer (the staging slot is reloaded
+  // before the tile's products run).
+  auto convert8 = [&](int tile) {
+    const int slot = tile % NBUF;
+    const unsigned char* stg = sfa_smem + G8::stage_off() + (size_t)slot * G8::STG;
+    unsigned char* dst = sfa_smem + (size_t)(tile & 1) * TILE;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int j = 0; j < G8::UNITS / kSfaBf16Threads; j++) {
+      const int u = tid + kSfaBf16Threads * j;
+      const int r = u / (DQK / 8), cu = u - r * (DQK / 8);
+      const uint2 raw = *(const uint2*)(stg + r * DQK + 8 * cu);
+      const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
+      const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true);
+      const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, false);
+      const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, true);
+      const bf16x8 v = {a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+      *(bf16x8*)(dst + r * PITCH + 16 * cu) = v;
+    }
+    if (tid < G8::SCOPY / 16) {
+      const u32x4 sv = *(const u32x4*)(sfa_smem + G8::scale_off() + (size_t)slot * G8::SBYTES + 16 * tid);
+      *(u32x4*)(sfa_smem + G8::tscale_off() + (size_t)(tile & 1) * G8::SCOPY + 16 * tid) = sv;
+    }
+  };
   auto issue = [&](int tile) {
     unsigned char* buf = sfa_smem + (tile % NBUF) * TILE;
     // recomputed per tile (cheap ALU) rather than held in registers across
@@ -229,7 +347,11 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     }
   };
   // the first tiles' loads overlap the q load below
-  for (int t = 0; t < NBUF - 1 && t < ntiles; t++) issue(t);
+  if constexpr (KV8) {
+    for (int t = 0; t < NBUF && t < ntiles; t++) issue8(t);
+  } else {
+    for (int t = 0; t < NBUF - 1 && t < ntiles; t++) issue(t);
+  }
 
   // q^T as the B operand of S^T = KV q^T (16x16x32): for head group ht, lane l
   // holds head 32*wave + 16*ht + l%16 and dims 32*k + 8*(l/16) .. +7 of K-step k.
@@ -258,27 +380,49 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
   // compiler's own waits never count the loop's asm-issued tile loads.  (This
   // also waits for the first tiles, which the first iterations need anyway.)
   __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (KV8) {
+    // every wave's loads of the first tiles have landed
+    if (ntiles > 0) {
+      lds_barrier();
+      convert8(0);
+    }
+  }
   DSA_PHASE(1);
 
   for (int tile = 0; tile < ntiles; tile++) {
-    // this wave's loads of the tile have landed; up to NBUF - 2 younger tiles
-    // may still be in flight
-    const int later = min(NBUF - 2, ntiles - 1 - tile);
-    if (wave == 0) {
-      if (later >= 2) DSA_WAIT_VMCNT(2 * LPW); else if (later == 1) DSA_WAIT_VMCNT(LPW); else DSA_WAIT_VMCNT(0);
-    } else {
-      if (later >= 2) DSA_WAIT_VMCNT(2 * (LPW - 1)); else if (later == 1) DSA_WAIT_VMCNT(LPW - 1); else DSA_WAIT_VMCNT(0);
+    // bf16: this wave's loads of the tile have landed; up to NBUF - 2 younger
+    // tiles may still be in flight.  FP8: the same for the next tile, which
+    // this iteration dequantises.
+    const int ahead = KV8 ? tile + 1 : tile;
+    if (ahead < ntiles) {
+      const int later = min(NBUF - 2, ntiles - 1 - ahead);
+      if (wave == 0) {
+        if (later >= 2) DSA_WAIT_VMCNT(2 * LPW); else if (later == 1) DSA_WAIT_VMCNT(LPW); else DSA_WAIT_VMCNT(0);
+      } else {
+        if (later >= 2) DSA_WAIT_VMCNT(2 * (LPW - 1)); else if (later == 1) DSA_WAIT_VMCNT(LPW - 1); else DSA_WAIT_VMCNT(0);
+      }
     }
     // rows of this tile that hold a selected position (bit r)
     const int rslot = tile * TR + (lane & 31);
     const uint32_t valid = (uint32_t)__ballot(lane < 32 && rslot < nslots && s_rows[rslot] >= 0);
     DSA_PHASE(2);
-    // every wave's loads of this tile are in LDS, and every wave is done with
-    // the previous tile, whose buffer the next load refills
+    // bf16: every wave's loads of this tile are in LDS, and every wave is done
+    // with the previous tile, whose buffer the next load refills.  FP8: this
+    // tile's bf16 values are written, the next tile's raw rows are in LDS,
+    // and every wave is done with the previous tile's bf16 buffer (which the
+    // next dequantisation overwrites) and with this tile's staging slot
+    // (which the next load refills).
     lds_barrier();
-    if (tile + NBUF - 1 < ntiles) issue(tile + NBUF - 1);
+    const unsigned char* cur;
+    if constexpr (KV8) {
+      if (tile + NBUF < ntiles) issue8(tile + NBUF);
+      if (tile + 1 < ntiles) convert8(tile + 1);
+      cur = sfa_smem + (size_t)(tile & 1) * TILE;
+    } else {
+      if (tile + NBUF - 1 < ntiles) issue(tile + NBUF - 1);
+      cur = sfa_smem + (tile % NBUF) * TILE;
+    }
     DSA_PHASE(3);
-    const unsigned char* cur = sfa_smem + (tile % NBUF) * TILE;
 
     // ---- S^T[row, head]: two 16-row M-tiles x two 16-head groups
     f32x4 s[2][HG];
@@ -286,6 +430,26 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     for (int rt = 0; rt < 2; rt++)
 #pragma unroll
       for (int ht = 0; ht < HG; ht++) s[rt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // FP8: scales of this lane's rows 16 rt + 4 grp + i (i < 4) for every
+    // 128-column tile t, and the per-tile partial products (two sets, so a
+    // tile's partial is folded in while the next tile's products run)
+    constexpr int NTS = KV8 ? G8::NT : 1;
+    f32x4 scv[NTS][2];
+    f32x4 pa[KV8 ? 2 : 1][2][HG];
+    if constexpr (KV8) {
+      const float* ts = (const float*)(sfa_smem + G8::tscale_off() + (size_t)(tile & 1) * G8::SCOPY);
+#pragma unroll
+      for (int t = 0; t < NTS; t++)
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++) scv[t][rt] = *(const f32x4*)(ts + t * TR + 16 * rt + 4 * grp);
+    }
+    auto fold = [&](auto T) {
+      constexpr int t = decltype(T)::value;
+#pragma unroll
+      for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+        for (int ht = 0; ht < HG; ht++) s[rt][ht] += scv[t][rt] * pa[t & 1][rt][ht];
+    };
     {
       // K-step k reads dims 32k + 8*grp .. +7 of rows l%16 and 16 + l%16;
       // QD steps are in flight at a time
@@ -301,16 +465,30 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
         constexpr int k = decltype(K)::value;
         constexpr int sl = k % QD;
         lds_wait<2 * (k + QD <= KS ? QD - 1 : KS - 1 - k)>(a[sl][0], a[sl][1]);
+        if constexpr (KV8) {
+          // K-steps 4t .. 4t + 3 make up column tile t
+          constexpr int par = (k / 4) & 1;
+          constexpr f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ht = 0; ht < HG; ht++) {
-          s[0][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][0], qb[ht][k], s[0][ht], 0, 0, 0);
-          s[1][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][1], qb[ht][k], s[1][ht], 0, 0, 0);
+          for (int ht = 0; ht < HG; ht++) {
+            pa[par][0][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][0], qb[ht][k], (k % 4 == 0) ? zero : pa[par][0][ht], 0, 0, 0);
+            pa[par][1][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][1], qb[ht][k], (k % 4 == 0) ? zero : pa[par][1][ht], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int ht = 0; ht < HG; ht++) {
+            s[0][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][0], qb[ht][k], s[0][ht], 0, 0, 0);
+            s[1][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][1], qb[ht][k], s[1][ht], 0, 0, 0);
+          }
         }
         if constexpr (k + QD < KS) {
           a[sl][0] = lds_read_b128<64 * (k + QD)>(ra);
           a[sl][1] = lds_read_b128<16 * PITCH + 64 * (k + QD)>(ra);
         }
+        // the previous tile's partial, one K-step after its last product
+        if constexpr (KV8 && k % 4 == 1 && k >= 5) fold(std::integral_constant<int, k / 4 - 1>{});
       });
+      if constexpr (KV8) fold(std::integral_constant<int, (KS - 1) / 4>{});
     }
     DSA_PHASE(4);
 
@@ -324,6 +502,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     // more than ~80 below it are flushed and negligible next to the first
     // maximum's own weight.  The normalised result does not depend on m_ref.
     bf16x8 phi[HG], plo[HG];
+    float pwv[KV8 ? HG : 1][8];   // FP8: the fp32 weights, scaled per V tile below
 #pragma unroll
     for (int ht = 0; ht < HG; ht++) {
       float z[8];
@@ -345,6 +524,11 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
 #pragma unroll
       for (int e = 0; e < 8; e++) {
         const float pw = none ? 0.f : __builtin_amdgcn_exp2f(z[e] - m_run[ht]);
+        if constexpr (KV8) {
+          pwv[ht][e] = pw;
+          psum += pw;
+          continue;
+        }
         const __bf16 hi = (__bf16)pw;
         phi[ht][e] = hi;
         if constexpr (LO) {
@@ -381,6 +565,19 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
       static_for<0, MV>([&](auto M) {
         constexpr int mv = decltype(M)::value;
         constexpr int sl = mv % PD;
+        if constexpr (KV8 && mv % 8 == 0) {
+          // V columns 128 tv .. +127: weight of row r times that row's scale
+          constexpr int tv = mv / 8;
+#pragma unroll
+          for (int ht = 0; ht < HG; ht++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+              const float w = pwv[ht][e] * scv[tv][e >> 2][e & 3];
+              const __bf16 hi = (__bf16)w;
+              phi[ht][e] = hi;
+              if constexpr (LO) plo[ht][e] = (__bf16)(w - (float)hi);
+            }
+        }
         lds_wait<2 * (mv + PD <= MV ? PD - 1 : MV - 1 - mv)>(v[sl][0], v[sl][1]);
         typedef short s16x8 __attribute__((ext_vector_type(8)));
         const s16x8 av = {v[sl][0][0], v[sl][0][1], v[sl][0][2], v[sl][0][3],
@@ -508,9 +705,11 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p, int H) {
 
 // f32 SFA for small head counts and widths: one workgroup per (token, range),
 // scalar FMAs.  Thread (h, r) computes one logit per tile; thread (h, v) keeps
-// output columns.
-template <int H, int DQK, int DV>
+// output columns.  With KV8 the rows are FP8 bytes, each multiplied by the
+// fp32 scale of its tile of 128 elements as it is staged.
+template <int H, int DQK, int DV, bool KV8>
 __global__ __launch_bounds__(256) void sfa_f32_kernel(SfaParams p) {
+  constexpr int NT = (DQK + 127) / 128;
   constexpr int TR = 32;
   __shared__ float s_q[H][DQK];
   __shared__ float s_kv[TR][DQK + 1];
@@ -544,7 +743,15 @@ __global__ __launch_bounds__(256) void sfa_f32_kernel(SfaParams p) {
     for (int e = tid; e < TR * DQK; e += 256) {
       const int r = e / DQK, c = e % DQK;
       const int row = s_row[r];
-      s_kv[r][c] = (row >= 0) ? ((const float*)p.kv)[(size_t)row * DQK + c] : 0.f;
+      float x = 0.f;
+      if (row >= 0) {
+        if constexpr (KV8)
+          x = __builtin_amdgcn_cvt_f32_fp8((int)((const unsigned char*)p.kv)[(size_t)row * DQK + c], 0) *
+              p.kv_scale[(size_t)row * NT + c / 128];
+        else
+          x = ((const float*)p.kv)[(size_t)row * DQK + c];
+      }
+      s_kv[r][c] = x;
     }
     __syncthreads();
     for (int e = tid; e < H * TR; e += 256) {
@@ -611,18 +818,28 @@ __global__ __launch_bounds__(256) void sfa_f32_kernel(SfaParams p) {
 
 }  // namespace
 
+const void* pick_sfa_bf16(const SfaParams& p) {
+  // (precise weights, head groups of 16 per wave, FP8 rows): 64 * HG heads per
+  // workgroup; FP8 rows always with HG = 1 (two workgroups per token)
+  if (p.kv8)
+    return p.precise_weights ? (const void*)sfa_bf16_kernel<576, 512, true, 1, true>
+                             : (const void*)sfa_bf16_kernel<576, 512, false, 1, true>;
+  if (p.precise_weights)
+    return (p.hsplit == 2) ? (const void*)sfa_bf16_kernel<576, 512, true, 1, false>
+                           : (const void*)sfa_bf16_kernel<576, 512, true, 2, false>;
+  return (p.hsplit == 2) ? (const void*)sfa_bf16_kernel<576, 512, false, 1, false>
+                         : (const void*)sfa_bf16_kernel<576, 512, false, 2, false>;
+}
+
 hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hipStream_t st) {
   if (p.bv.total_q == 0) return hipSuccess;
   if (dtype == kBF16 && H == 128 && Dqk == 576 && Dv == 512) {
     if (p.rows_per_split > kSfaMaxRows) return hipErrorInvalidValue;
-    // (precise weights, head groups of 16 per wave): 64 * HG heads per workgroup
-    const void* kern = nullptr;
-    if (p.precise_weights)
-      kern = (p.hsplit == 2) ? (const void*)sfa_bf16_kernel<576, 512, true, 1> : (const void*)sfa_bf16_kernel<576, 512, true, 2>;
-    else
-      kern = (p.hsplit == 2) ? (const void*)sfa_bf16_kernel<576, 512, false, 1> : (const void*)sfa_bf16_kernel<576, 512, false, 2>;
     if (p.hsplit != 1 && p.hsplit != 2) return hipErrorInvalidValue;
-    const size_t lds = SfaBf16Geom<576, 512>::lds_bytes(p.rows_per_split);
+    if (p.kv8 && (!p.kv_scale || p.hsplit != 2)) return hipErrorInvalidValue;
+    const void* kern = pick_sfa_bf16(p);
+    const size_t lds = p.kv8 ? SfaKv8Geom<576, 512>::lds_bytes(p.rows_per_split)
+                             : SfaBf16Geom<576, 512>::lds_bytes(p.rows_per_split);
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int chunk = (p.bv.total_q + 7) / 8;
@@ -633,7 +850,11 @@ hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hip
     return hipGetLastError();
   }
   if (dtype == kF32 && H == 8 && Dqk == 80 && Dv == 64) {
-    hipLaunchKernelGGL((sfa_f32_kernel<8, 80, 64>), dim3(p.bv.total_q, 1, p.splits), dim3(256), 0, st, p);
+    if (p.kv8 && !p.kv_scale) return hipErrorInvalidValue;
+    if (p.kv8)
+      hipLaunchKernelGGL((sfa_f32_kernel<8, 80, 64, true>), dim3(p.bv.total_q, 1, p.splits), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((sfa_f32_kernel<8, 80, 64, false>), dim3(p.bv.total_q, 1, p.splits), dim3(256), 0, st, p);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

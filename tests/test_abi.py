@@ -77,6 +77,11 @@ def test_workspace_size_positive_and_monotone():
     (lambda b, i, s: setattr(s, "v_dim", 256), B.DSA_ERR_UNSUPPORTED),
     (lambda b, i, s: setattr(s, "q_dtype", B.DSA_FP8_E4M3), B.DSA_ERR_UNSUPPORTED),
     (lambda b, i, s: setattr(s, "softmax_scale", 0.0), B.DSA_ERR_INVALID_ARG),
+    # FP8 tile-128 rows are an SFA KV cache format only, and carry their scales
+    (lambda b, i, s: setattr(s.kv_cache.contents, "dtype", B.DSA_FP8_E4M3_TILE128), B.DSA_ERR_INVALID_ARG),
+    (lambda b, i, s: setattr(s, "q_dtype", B.DSA_FP8_E4M3_TILE128), B.DSA_ERR_UNSUPPORTED),
+    (lambda b, i, s: setattr(i, "q_dtype", B.DSA_FP8_E4M3_TILE128), B.DSA_ERR_INVALID_ARG),
+    (lambda b, i, s: setattr(s.kv_cache.contents, "dtype", B.DSA_FP8_E4M3), B.DSA_ERR_INVALID_ARG),
 ])
 def test_fused_decode_rejects_bad_arguments(mutate, expected):
     batch, ia, sa, keep = _structs()
@@ -119,3 +124,16 @@ def test_sparse_attn_argument_checks():
     st = B.lib().dsa_sparse_attn(ctypes.pointer(batch), ctypes.pointer(sa), ctypes.c_void_p(0x4000), 0,
                                  ctypes.c_void_p(0x2000), None, None, 0, None)
     assert st == B.DSA_ERR_INVALID_ARG
+
+
+def test_fp8_kv_cache_passes_validation():
+    """An FP8 tile-128 KV cache with its scale pool is accepted for bf16 and
+    f32 queries: the call gets as far as the workspace check."""
+    for kw in (dict(), dict(h_s=8, dqk=80, dv=64, sdt=B.DSA_F32, h_i=4, d_i=32, dt=B.DSA_F32, topk=64)):
+        batch, ia, sa, (kc, vc) = _structs(**kw)
+        vc.dtype = B.DSA_FP8_E4M3_TILE128
+        vc.scale = 0x5000
+        need = B.dsa_workspace_size(B.DSA_OP_FUSED_DECODE, batch, ia, sa)
+        st = B.lib().dsa_fused_decode(ctypes.pointer(batch), ctypes.pointer(ia), ctypes.pointer(sa),
+                                      ctypes.c_void_p(0x2000), None, None, ctypes.c_void_p(0x3000), need - 1, None)
+        assert st == B.DSA_ERR_WORKSPACE_TOO_SMALL, B.lib().dsa_last_error()

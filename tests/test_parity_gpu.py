@@ -53,6 +53,11 @@ def _check_indexer(case, call, idx, queries):
     return refs, diffs
 
 
+def _bar(case):
+    """Tolerance class of a case's SFA output: the fp8 bar for an FP8 KV cache."""
+    return "fp8" if case.kv_dtype == "fp8_t128" else case.sfa_dtype
+
+
 def _check_sfa_on(case, out, queries, idx_rows):
     """out rows vs the oracle's SFA run on the given index rows."""
     out_h = _host_out(out)
@@ -62,7 +67,7 @@ def _check_sfa_on(case, out, queries, idx_rows):
         sel = idx_rows[tok]
         sel = sel[sel >= 0]
         ref_o, _ = oracle.sfa_query(case, b, i, sel)
-        mx, rel = check_sfa(out_h[tok], ref_o, case.sfa_dtype)
+        mx, rel = check_sfa(out_h[tok], ref_o, _bar(case))
         worst = (max(worst[0], mx), max(worst[1], rel))
     return worst
 
@@ -87,7 +92,7 @@ def _run_all_paths(case, queries=None, fused=True):
     out_h, lse_h = _host_out(out), lse.cpu().numpy()
     for (b, i), ref in refs.items():
         tok = case.token(b, i)
-        check_sfa(out_h[tok], ref["out"], case.sfa_dtype)
+        check_sfa(out_h[tok], ref["out"], _bar(case))
         assert np.allclose(lse_h[tok], ref["lse"], atol=2e-3, rtol=1e-4), (lse_h[tok][:4], ref["lse"][:4])
     if fused:
         _say(f"{case.name}: fused_decode")
@@ -164,6 +169,32 @@ def test_multi_token_decode_quantised(name):
 def test_multi_token_decode_f32_ragged():
     # three query tokens per sequence on the f32 path, ragged pages
     case = case_to(make_case("c1_tiny_f32", 13, batch=2, seq_len_range=(100, 250), q_len=3), "cuda")
+    _run_all_paths(case)
+
+
+def test_c1_tiny_fp8kv():
+    # f32 queries over FP8 tile-128 rows of 80 elements (one short tile)
+    case = case_to(make_case("c1_tiny_f32", 14, batch=3, seq_len_range=(60, 250), kv_dtype="fp8_t128"), "cuda")
+    _run_all_paths(case)
+
+
+def test_c2_fp8kv_small():
+    # decode over an FP8 KV cache: head-split workgroups, split slot ranges
+    case = case_to(make_case("c2_decode_fp8kv", 31, batch=4, seq_len_range=(2500, 9000)), "cuda")
+    _run_all_paths(case)
+
+
+def test_c2_fp8kv_short_contexts_and_small_pages():
+    # index rows padded with -1 (masked rows, fallback loads), a context of one
+    # token, and 16-token pages
+    case = case_to(make_case("c2_decode_fp8kv", 32, batch=3, seq_lens=[1, 777, 2048], page_size=16), "cuda")
+    _run_all_paths(case)
+
+
+def test_c2_fp8kv_outliers():
+    # 20-sigma outliers: tiles whose scale is set by one large element
+    case = case_to(make_case("c2_decode_fp8kv", 33, batch=2, seq_len_range=(3000, 5000), outliers=0.01,
+                             sfa_mult=1.0), "cuda")
     _run_all_paths(case)
 
 
@@ -340,6 +371,14 @@ def test_prefill_mixed_batch_zigzag_units():
     _run_prefill(case, _sample_prefill_queries(case, per_seq=20))
 
 
+def test_prefill_fp8kv():
+    # causal prefill over an FP8 KV cache: the 128-head workgroups of large
+    # launches, ragged last query block and page
+    case = case_to(make_case("c3_prefill_bf16", 27, seq_len_range=(4133, 4133), q_len=4133,
+                             kv_dtype="fp8_t128"), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=30))
+
+
 def test_prefill_equal_scores():
     case = make_case("c3_prefill_bf16", 25, seq_len_range=(3500, 3500), q_len=300, topk=1024)
     case.k_pool[:] = case.k_pool[0, 0]
@@ -364,3 +403,22 @@ def test_c3_full_size_sampled():
     valid = idx_h >= 0
     assert np.array_equal(valid.sum(1), n)
     assert np.all(np.where(valid, idx_h <= t[:, None], True))
+
+
+def test_c2_fp8kv_full_size_sampled():
+    """The decode workload at full size (32 sequences, contexts U[4096, 32768])
+    with the SFA KV cache in FP8, in the configuration the benchmark times."""
+    _say("c2 fp8 KV full size: generating on device")
+    case = make_case("c2_decode_fp8kv", 6, device="cuda")
+    call = B.Call(case)
+    _say("c2 fp8 KV full size: fused_decode")
+    out, lse, idx = call.fused_decode()
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    qs = _queries(case, limit=4)
+    for (b, i) in qs:
+        ref = oracle.run_query(case, b, i)
+        check_topk_row(idx_h[case.token(b, i)], ref, case.topk)
+    mx, rel = _check_sfa_on(case, out, qs, idx_h)
+    _say(f"c2 fp8 KV full size: max abs excess {mx:.3g}, rel L2 {rel:.3g}")
+    _check_rows_valid(case, idx_h)

@@ -34,11 +34,13 @@ WORKLOADS = {
     "c4_decode_fp8": "decode, 64 sequences, contexts U[16384, 65536], FP8 indexer",
     "c4_decode_mxfp8": "decode, 64 sequences, contexts U[16384, 65536], MXFP8 indexer",
     "c5_decode4": "4-token decode, 8 sequences at 131072 tokens, bf16",
+    "c2_decode_fp8kv": "decode, 32 sequences, contexts U[4096, 32768], bf16, SFA KV cache FP8 "
+                       "(one fp32 scale per 128-element tile)",
 }
 
 
 def _el(dtype):
-    return {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[dtype]
+    return {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1, "fp8_t128": 1}[dtype]
 
 
 def algorithmic(case):
@@ -62,7 +64,8 @@ def algorithmic(case):
             pairs += t + 1
     # rows gathered once per sequence and step: the union over its queries is
     # bounded by the per-query count; for one query per sequence they coincide
-    gather = rows * case.d_qk * es
+    kv_scale = 4 * -(-case.d_qk // 128) if case.kv_dtype == "fp8_t128" else 0
+    gather = rows * (case.d_qk * _el(case.kv_dtype) + kv_scale)
     sfa_bytes = gather + tq * case.h_s * (case.d_qk + case.d_v) * es + tq * case.h_s * 4 + idx_b
     indexer_flops = 2 * case.h_i * case.d_i * pairs
     sfa_flops = 2 * case.h_s * (case.d_qk + case.d_v) * rows
@@ -174,6 +177,8 @@ CONFIGS_EXTRA = {
     "c4_decode_mxfp8": "decode, 64 sequences, contexts U[16384, 65536], MXFP8 indexer, 1 % outliers",
     "c5_chunk_prefill": "chunked prefill, 8 sequences, 8192 new tokens after 122880 cached",
     "c5_decode4": "4-token decode, 8 sequences at 131072 tokens",
+    "c2_decode_fp8kv": "decode, 32 sequences, contexts U[4096, 32768], SFA KV cache FP8 "
+                       "(one fp32 scale per 128-element tile)",
 }
 
 

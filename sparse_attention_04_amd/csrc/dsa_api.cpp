@@ -335,7 +335,7 @@ dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx
   // Launches with fewer query tokens than workgroup slots (decode) are bound
   // by memory and latency, so the matrix units can afford the weight
   // residuals; large prefill launches are bound by the matrix units and use
-  // bf16 weights (error <= 2^-9 max|V|).
+  // bf16 weights (each within 2^-8 relative).
   p.precise_weights = (int64_t)b->total_q < kSfaTargetWG ? 1 : 0;
   p.out = out;
   p.lse = lse;

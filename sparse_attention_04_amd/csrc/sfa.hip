@@ -29,7 +29,8 @@
 // fp32: S^T is accumulated per 128-column tile and each partial is multiplied
 // by its rows' scales before it is summed, and the softmax weights are
 // multiplied by the scale of each 128-column V tile before they are rounded
-// into the PV product's operand.
+// into the PV product's operand (the denominator then sums the fp32 weights,
+// as no single rounded set serves all four V tiles).
 #include "common.h"
 #include "kernels.h"
 
@@ -134,9 +135,10 @@ __device__ __forceinline__ void lds_wait(s16x4& a, s16x4& b) {
 //   softmax weights against a fixed reference (see below)
 //   O^T[v, head] += V^T[v, row] P^T[row, head]   V^T read with ds_read_b64_tr_b16
 // The weights leave the first product already in the B-operand layout of the
-// second, rounded to bf16, which bounds their contribution to the output
-// error by 2^-9 max|V|.  With LO the wave also multiplies in the rounding
-// residuals (a second bf16 part), so the weights enter to ~2^-17 relative; it
+// second, rounded to bf16 (each within 2^-8 relative; the denominator sums
+// the rounded weights, so the output stays a convex combination of rows).
+// With LO the wave also multiplies in the rounding residuals (a second bf16
+// part), so the weights enter to ~2^-16 relative; it
 // costs the PV product twice the MFMAs and is used where the launch is bound
 // by memory rather than by the matrix units (few query tokens).  Rows stream
 // through a 4-deep ring of LDS tiles filled by direct global->LDS loads; slots
@@ -174,10 +176,9 @@ struct SfaKv8Geom {
   static constexpr int LOADS = RLOADS + SLOADS;          // 21
   static constexpr int LPW = (LOADS + NW - 1) / NW;      // loads of wave 0 per tile (6)
   static constexpr int NBUF = 4;                         // staged tiles in flight
-  static constexpr int UNITS = TR * DQK / 8;             // 8-element units dequantised per tile
   static_assert(STG % 1024 == 0 && DQK % 16 == 0, "row loads tile the staging buffer");
   static_assert(LOADS % NW == 1, "wave 0 issues one load more than the others");
-  static_assert(UNITS % kSfaBf16Threads == 0, "dequantising units split evenly");
+  static_assert(kSfaBf16Threads % TR == 0, "whole threads per converted row");
   static constexpr int SCOPY = TR * NT * 4;              // scale table of one converted tile (640)
   static_assert(SCOPY % 16 == 0, "scale tables copy in 16-byte pieces");
   // [2 bf16 tiles][2 scale tables][NBUF staged tiles][NBUF staged scale tables][row table]
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     }
   };
   // Convert staged tile `tile` into bf16 buffer tile & 1: each thread turns
-  // UNITS / 256 runs of 8 bytes into 8 bf16 values (exact; scale 1), and the
+  // runs of 8 bytes of one row into 8 bf16 values (exact; scale 1), and the
   // tile's scale table moves next to the buffer (the staging slot is reloaded
   // before the tile's products run).
   auto convert8 = [&](int tile) {
@@ -304,10 +305,13 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     const unsigned char* stg = sfa_smem + G8::stage_off() + (size_t)slot * G8::STG;
     unsigned char* dst = sfa_smem + (size_t)(tile & 1) * TILE;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    // thread t takes row t / 8 and the 8-byte runs t % 8 + 8 j of it
+    constexpr int TPR = kSfaBf16Threads / TR;                 // threads per row (8)
+    static_assert((DQK / 8) % TPR == 0, "runs of a row split evenly");
+    const int r = tid / TPR;
 #pragma unroll
-    for (int j = 0; j < G8::UNITS / kSfaBf16Threads; j++) {
-      const int u = tid + kSfaBf16Threads * j;
-      const int r = u / (DQK / 8), cu = u - r * (DQK / 8);
+    for (int j = 0; j < (DQK / 8) / TPR; j++) {
+      const int cu = tid % TPR + TPR * j;
       const uint2 raw = *(const uint2*)(stg + r * DQK + 8 * cu);
       const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
       const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true);

@@ -30,8 +30,15 @@
 
 namespace dsa {
 
-constexpr int kIdxThreads = 256;
+// One workgroup of 8 waves per CU: the CU's waves share one key range (two
+// co-resident workgroups of 4 waves each finished up to 1.6x apart, the
+// younger one getting the smaller share of the CU), and half as many
+// workgroups take part in each sequence's radix barriers.
+constexpr int kIdxThreads = 512;
 constexpr int kIdxWaves = kIdxThreads / kWave;
+constexpr int kBinsPerThread = kRadixBins / kIdxThreads;
+static_assert(kMaxDecodeQ <= 4 && kIdxWaves % 4 == 0, "wave groups per decode query");
+static_assert(kRadixBins % kIdxThreads == 0, "histogram bins split evenly over the threads");
 
 // Workspace layout (uint32 words), see indexer_ws_words().
 //   [0, 64)                        header: error bits
@@ -269,7 +276,7 @@ enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3 };
   } while (0)
 
 template <int DT, int H, int D, int MAXQ>
-__global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerDecodeParams p) {
+__global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerDecodeParams p) {
   extern __shared__ uint32_t smem[];
   // dynamic LDS: sc[MAXQ][cap] | lhist[2048] | s_bt[stage_pages]
   uint32_t* sc = smem;
@@ -405,21 +412,28 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
           scorer.load_tile(p, ((int64_t)page_of(s) << PS) + (s & (P - 1)), t);
         }
       };
-      for (int q = 0; q < T && q < MAXQ; q++) {
-        if (s_state[q] != kActive) continue;
+      // Every query of the sequence is scored in the same sweep over the
+      // tiles, so each key is brought from memory once: the waves form QG
+      // groups, one per query (QG = 1 for one query, 2 for two, 4 for three
+      // or four), and the waves of a group take every (8 / QG)-th tile.  The
+      // waves that read the same tile do so close together, on one CU.
+      const int QG = (MAXQ == 1 || T <= 1) ? 1 : (T == 2) ? 2 : 4;
+      const int q = wave % QG;
+      if (q < T && q < MAXQ && s_state[q] == kActive) {
         const int t = L - T + q;
+        const int phase = wave / QG, stride = kIdxWaves / QG;
         scorer.load_query(p, tok0 + q);
         uint32_t* scq = sc + (size_t)q * p.chunk_cap;
         Tile ring[RD];
 #pragma unroll
-        for (int d = 0; d < RD - 1; d++) fetch(wave + d * kIdxWaves, ring[d]);
-        for (int base = wave; base < ntiles; base += RD * kIdxWaves) {
+        for (int d = 0; d < RD - 1; d++) fetch(phase + d * stride, ring[d]);
+        for (int base = phase; base < ntiles; base += RD * stride) {
 #pragma unroll
           for (int d = 0; d < RD; d++) {
-            const int tile = base + d * kIdxWaves;
+            const int tile = base + d * stride;
             if (tile < ntiles) {
               // refill the slot of the previous tile with the one kAhead later
-              fetch(tile + kAhead * kIdxWaves, ring[(d + RD - 1) % RD]);
+              fetch(tile + kAhead * stride, ring[(d + RD - 1) % RD]);
               const float v = scorer.score(p, 0, ring[d]);
               const int s = s0 + 32 * tile + lane;
               if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
@@ -470,12 +484,13 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
     for (int q = 0; q < T && q < MAXQ; q++) {
       if (s_state[q] != kActive) continue;
       const uint32_t* gh = W.hist(tok0 + q, pass);
-      // each thread owns 8 consecutive bins; suffix sums from the top bin down
-      uint32_t h8[8];
+      // each thread owns kBinsPerThread consecutive bins; suffix sums from
+      // the top bin down
+      uint32_t h8[kBinsPerThread];
       uint32_t csum = 0;
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        h8[e] = load_relaxed_agent(&gh[8 * tid + e]);
+      for (int e = 0; e < kBinsPerThread; e++) {
+        h8[e] = load_relaxed_agent(&gh[kBinsPerThread * tid + e]);
         csum += h8[e];
       }
       // suffix sums over threads: above[t] = sum of the counts of threads > t
@@ -498,12 +513,12 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(IndexerD
         s_bincnt = 0;
       }
       __syncthreads();
-      const int above = incl - (int)csum;  // bins above this thread's 8
+      const int above = incl - (int)csum;  // bins above this thread's own
       if (above < need && need <= above + (int)csum) {
         int run = above;
-        for (int e = 7; e >= 0; e--) {
+        for (int e = kBinsPerThread - 1; e >= 0; e--) {
           if (run + (int)h8[e] >= need) {
-            s_bin = 8 * tid + e;
+            s_bin = kBinsPerThread * tid + e;
             s_above = run;
             s_bincnt = (int)h8[e];
             break;

@@ -157,7 +157,11 @@ dsa_status dsa_indexer_topk(const dsa_batch* batch, const dsa_indexer_args* args
  *      (each row must hold at least one valid position <= the query's t).
  * out: device [total_q][n_heads][v_dim] in q_dtype.
  * lse: device float32 [total_q][n_heads] natural-log sum-exp of the scaled
- *      logits, or NULL.                                                       */
+ *      logits, or NULL.
+ * Launches that split index rows across workgroups (few query tokens) keep
+ * the normalised per-range results in fp16, so bf16 latent values must stay
+ * below 65504 in magnitude there (a larger one shows up as a non-finite
+ * output).                                                                    */
 dsa_status dsa_sparse_attn(const dsa_batch* batch, const dsa_sfa_args* args,
                            const int32_t* idx, int32_t topk, void* out, float* lse,
                            void* ws, size_t ws_bytes, void* stream);

@@ -157,7 +157,7 @@ SfaPlan plan_sfa(const dsa_batch* b, int H, int Dv, int topk, bool bf16, bool kv
   pl.splits = splits;
   pl.rows_per_split = rps;
   if (splits > 1) {
-    pl.part_o_bytes = align_up((size_t)b->total_q * splits * H * Dv * 4, 256);
+    pl.part_o_bytes = align_up((size_t)b->total_q * splits * H * Dv * (bf16 ? 2 : 4), 256);
     pl.part_ml_bytes = align_up((size_t)b->total_q * splits * H * 4, 256);
   }
   return pl;

@@ -80,7 +80,7 @@ struct SfaParams {
   int32_t rows_per_split;  // multiple of the row tile
   void* out;               // splits == 1: final [total_q][H][Dv] in q dtype
   float* lse;              // splits == 1: [total_q][H] (natural log) or null
-  float* part_o;           // splits > 1: [total_q][splits][H][Dv] f32
+  float* part_o;           // splits > 1: [total_q][splits][H][Dv], fp16 (bf16 kernel) or f32 (f32 kernel)
   float* part_ml;          // splits > 1: [total_q][splits][H] log2-sum-exp of each range
   unsigned long long* dbg; // optional: per-phase clock sums of workgroup 0, wave 0 (profiling)
 };

@@ -622,9 +622,15 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
       if (p.lse && grp == 0)
         p.lse[(size_t)g * H + head] = (l > 0.f) ? (m_run[ht] + log2f(l)) * 0.69314718055994531f : -INFINITY;
     } else {
-      float* po = p.part_o + (((size_t)g * p.splits + split) * H + head) * DV;
+      // normalised partials are convex combinations of V rows (|o| <= max|V|),
+      // kept in fp16: within 2^-11 relative, half the bytes of f32
+      typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+      _Float16* po = (_Float16*)p.part_o + (((size_t)g * p.splits + split) * H + head) * DV;
 #pragma unroll
-      for (int mv = 0; mv < MV; mv++) *(f32x4*)(po + 16 * mv + 4 * grp) = o[ht][mv] * inv;
+      for (int mv = 0; mv < MV; mv++) {
+        const f32x4 v = o[ht][mv] * inv;
+        *(f16x4*)(po + 16 * mv + 4 * grp) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+      }
       if (grp == 0)
         p.part_ml[((size_t)g * p.splits + split) * H + head] = (l > 0.f) ? m_run[ht] + log2f(l) : -INFINITY;
     }
@@ -639,6 +645,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
 
 // Merge the per-range partials of one token: weights 2^(lse_j - lse).  One
 // workgroup per (token, group of 4 heads); each thread owns DV/64 columns.
+// Partials are fp16 for the bf16 kernel (BF16OUT) and f32 otherwise.
 template <int DV, bool BF16OUT>
 __global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p, int H) {
   constexpr int CPT = DV / 64;  // columns per thread
@@ -661,6 +668,14 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p, int H) {
     for (int u = 0; u < 4; u++) {
       const int j = min(j0 + u, S - 1);   // past the end: reloads the last split, masked below
       l[u] = (j0 + u < S) ? p.part_ml[((size_t)g * S + j) * H + h] : -INFINITY;
+      if constexpr (BF16OUT) {
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        static_assert(CPT == 8, "one 16-byte load of fp16 partials per thread");
+        const f16x8 t = *(const f16x8*)((const _Float16*)p.part_o + (((size_t)g * S + j) * H + h) * DV + c0);
+#pragma unroll
+        for (int c = 0; c < 8; c++) v[u][c] = (float)t[c];
+        continue;
+      }
       const float* src = p.part_o + (((size_t)g * S + j) * H + h) * DV + c0;
       if constexpr (CPT % 4 == 0) {
 #pragma unroll

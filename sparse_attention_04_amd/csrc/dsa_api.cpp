@@ -140,15 +140,12 @@ struct SfaPlan {
 
 SfaPlan plan_sfa(const dsa_batch* b, int H, int Dv, int topk, bool bf16, bool kv8) {
   SfaPlan pl{};
-  // A workgroup serves one (token, range of index slots) with all heads, or
-  // in launches with few tokens (decode, bf16) with half of them: two
-  // workgroups per token then share the heads, which halves the split
-  // partials and the q each workgroup loads.  Over an FP8 KV cache the
-  // workgroups always take half of the heads (the registers of the per-tile
-  // scale products do not fit next to all 128).  The slot ranges are split
-  // until about kSfaTargetWG workgroups exist.  Ranges are multiples of the
-  // row tile and hold at most kSfaMaxRows slots.
-  pl.hsplit = (bf16 && (kv8 || (int64_t)b->total_q < kSfaTargetWG)) ? 2 : 1;
+  // A workgroup serves one (token, range of index slots) with all heads.
+  // Over an FP8 KV cache two workgroups share a token's heads (the registers
+  // of the per-tile scale products do not fit next to all 128).  The slot
+  // ranges are split until about kSfaTargetWG workgroups exist.  Ranges are
+  // multiples of the row tile and hold at most kSfaMaxRows slots.
+  pl.hsplit = (bf16 && kv8) ? 2 : 1;
   const int64_t units = std::max<int64_t>(1, (int64_t)b->total_q * pl.hsplit);
   int splits = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(1, topk / 64), kSfaTargetWG / units));
   splits = std::max(splits, (topk + kSfaMaxRows - 1) / kSfaMaxRows);

@@ -10,7 +10,8 @@
 // columns and V is the first Dv columns of the same row.
 //
 // bf16 kernel (H = 128, Dqk = 576, Dv = 512): a workgroup owns one query token,
-// all of its heads and a contiguous range of index slots.  Per tile of 32
+// all of its heads (half of them over an FP8 cache) and a contiguous range of
+// index slots.  Per tile of 32
 // slots it gathers the 32 latent rows through the block table into LDS (a
 // 4-deep ring), then every wave (32 heads) computes
 //   S^T[row, head] = KV[row, :] . q[head, :]     (16x16x32 bf16 MFMAs, rows on M)
@@ -118,17 +119,19 @@ __device__ __forceinline__ void lds_wait(s16x4& a, s16x4& b) {
 
 // bf16 SFA, H = 128, Dqk = 576, Dv = 512.
 //
-// A workgroup serves 64 * HG heads of one token (all 128 with HG = 2; with
-// HG = 1 two workgroups share the token, grid y picking the half) for one
-// range of index slots, with 4 waves, one per SIMD, so each wave may use the
-// whole register file.  Wave w owns 16 * HG heads as HG groups ht of 16: q^T
-// for all 576 dims stays in registers (72 VGPRs per group) and the O^T
-// accumulators for all 512 columns (128 per group) live in the accumulation
-// registers.  Each K/V operand read from LDS feeds every head group of the
-// wave.  HG = 2 brings a gathered row on chip once per token and range;
-// HG = 1 (launches with few tokens) gathers it twice, with the two reads
-// close together on one XCD, and in return halves the split partials and the
-// q each workgroup loads.
+// A workgroup serves 16 * NW * HG heads of one token for one range of index
+// slots, with NW waves of 16 * HG heads each (HG groups ht of 16).  Wave w
+// keeps q^T for all 576 dims in registers (72 VGPRs per group) and the O^T
+// accumulators for all 512 columns (128 per group).  Each K/V operand read
+// from LDS feeds every head group of the wave.  Configurations:
+//   * large launches (prefill): NW = 4, HG = 2, one wave per SIMD, so a wave
+//     may use the whole register file;
+//   * few query tokens (decode): NW = 8, HG = 1, two waves per SIMD, so one
+//     wave's products overlap the other's barrier and tile waits; the
+//     operand reads in flight are fewer to fit 256 registers per wave;
+//   * FP8 rows: NW = 4, HG = 1 (two workgroups per token, grid y).
+// All heads of a token in one workgroup bring a gathered row on chip once per
+// token and range.
 //
 // Per tile of 32 index slots:
 //   S^T[row, head] = KV[row, :] . q[head, :]     16x16x32 bf16 MFMAs, rows on M
@@ -143,21 +146,22 @@ __device__ __forceinline__ void lds_wait(s16x4& a, s16x4& b) {
 // by memory rather than by the matrix units (few query tokens).  Rows stream
 // through a 4-deep ring of LDS tiles filled by direct global->LDS loads; slots
 // holding -1 are masked.
-constexpr int kSfaBf16Threads = 256;
+constexpr int kSfaKv8Threads = 256;        // threads of the FP8-row configuration (4 waves)
 constexpr int kSfaMaxRows = 2048;          // index slots per workgroup (LDS row table)
 constexpr float kSfaRefMargin = 40.f;      // softmax reference above the first tile maximum (log2 units)
 
-template <int DQK, int DV>
+template <int DQK, int DV, int NW_ = 4>
 struct SfaBf16Geom {
   static constexpr int ROWB = DQK * 2;               // bytes of one latent row (1152)
   static constexpr int PITCH = ROWB + 32;            // LDS bytes per row (74 chunks of 16 B)
   static constexpr int TR = 32;                      // rows per tile
-  static constexpr int NW = kSfaBf16Threads / 64;    // 4 waves
+  static constexpr int NW = NW_;                     // waves
   static constexpr int LOADS = (TR * PITCH + 1023) / 1024;  // 1-KiB loads per tile (37)
   static constexpr int LPW = (LOADS + NW - 1) / NW;  // loads of wave 0 per tile (10)
   static constexpr int TILE = LOADS * 1024;          // LDS bytes per tile buffer
   static constexpr int NBUF = 4;                     // tiles in flight
-  static_assert(LOADS % NW == 1, "wave 0 issues one load more than the others");
+  static constexpr int NA = LOADS % NW;              // waves issuing LPW loads (the rest LPW - 1)
+  static_assert(NA != 0, "some waves issue one load more than the others");
   static constexpr size_t lds_bytes(int rows) { return (size_t)NBUF * TILE + (size_t)rows * 4; }
 };
 
@@ -178,7 +182,7 @@ struct SfaKv8Geom {
   static constexpr int NBUF = 4;                         // staged tiles in flight
   static_assert(STG % 1024 == 0 && DQK % 16 == 0, "row loads tile the staging buffer");
   static_assert(LOADS % NW == 1, "wave 0 issues one load more than the others");
-  static_assert(kSfaBf16Threads % TR == 0, "whole threads per converted row");
+  static_assert(kSfaKv8Threads % TR == 0, "whole threads per converted row");
   static constexpr int SCOPY = TR * NT * 4;              // scale table of one converted tile (640)
   static_assert(SCOPY % 16 == 0, "scale tables copy in 16-byte pieces");
   // [2 bf16 tiles][2 scale tables][NBUF staged tiles][NBUF staged scale tables][row table]
@@ -189,13 +193,15 @@ struct SfaKv8Geom {
   static constexpr size_t lds_bytes(int rows) { return rows_off() + (size_t)rows * 4; }
 };
 
-template <int DQK, int DV, bool LO, int HG, bool KV8>
-__global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams p) {
-  using G = SfaBf16Geom<DQK, DV>;
+template <int DQK, int DV, bool LO, int HG, bool KV8, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV, 1) void sfa_bf16_kernel(SfaParams p) {
+  using G = SfaBf16Geom<DQK, DV, NWV>;
   using G8 = SfaKv8Geom<DQK, DV>;
   constexpr int ROWB = G::ROWB, PITCH = G::PITCH, TR = G::TR, TILE = G::TILE;
   constexpr int NBUF = KV8 ? G8::NBUF : G::NBUF;
   constexpr int NW = G::NW, LPW = KV8 ? G8::LPW : G::LPW;
+  constexpr int NA = KV8 ? 1 : G::NA;        // waves issuing LPW loads per tile
+  constexpr int NT = 64 * NW;                // threads
   constexpr int KS = DQK / 32;               // QK^T K-steps of 32 (18)
   constexpr int MV = DV / 16;                // PV M-tiles of 16 columns (32)
   static_assert(DQK % 32 == 0 && (!KV8 || DV % 128 == 0), "FP8 scale tiles cover whole K-steps and M-tiles");
@@ -234,7 +240,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
   const int nslots = max(0, min(p.topk - slot0, p.rows_per_split));
   const int32_t* idx = p.idx + (size_t)g * p.topk + slot0;
 
-  for (int r = tid; r < nslots; r += kSfaBf16Threads) {
+  for (int r = tid; r < nslots; r += NT) {
     const int pos = idx[r];
     s_rows[r] = (pos >= 0) ? (bt[pos >> bv.page_shift] << bv.page_shift) + (pos & (P - 1)) : -1;
   }
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
   // 1024c .. +1023 of its buffer and is issued by wave c % NW (wave 0 issues
   // LPW loads, the others LPW - 1); lanes that land on a pad or past row 31
   // load chunk 0 of the tile's row 0.
-  const int nld = (wave == 0) ? LPW : LPW - 1;
+  const int nld = (wave < NA) ? LPW : LPW - 1;
   // FP8 rows: load c (< G8::LOADS) of a tile is issued by wave c % NW.  Loads
   // below RLOADS fill staging bytes 1024c .. +1023 (rows are 16-byte
   // multiples, so a lane's 16 bytes never straddle two rows); the others fill
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     }
 #pragma unroll
     for (int k = 0; k < LPW; k++) {
-      if (k < LPW - 1 || wave == 0) {
+      if (k < LPW - 1 || wave < NA) {
         const int c = wave + NW * k;
         if (c < G8::RLOADS)
           dma16(src[k], __builtin_amdgcn_readfirstlane(stg + c * 1024));
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     unsigned char* dst = sfa_smem + (size_t)(tile & 1) * TILE;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     // thread t takes row t / 8 and the 8-byte runs t % 8 + 8 j of it
-    constexpr int TPR = kSfaBf16Threads / TR;                 // threads per row (8)
+    constexpr int TPR = kSfaKv8Threads / TR;                  // threads per row (8)
     static_assert((DQK / 8) % TPR == 0, "runs of a row split evenly");
     const int r = tid / TPR;
 #pragma unroll
@@ -343,7 +349,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     }
 #pragma unroll
     for (int k = 0; k < LPW; k++) {
-      if (k < LPW - 1 || wave == 0) {
+      if (k < LPW - 1 || wave < NA) {
         const int row = (rows[k] < 0) ? fallback : rows[k];
         const unsigned char* src = (const unsigned char*)p.kv + (size_t)row * ROWB + cols[k];
         dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(buf + (wave + NW * k) * 1024)));
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
   // holds head 32*wave + 16*ht + l%16 and dims 32*k + 8*(l/16) .. +7 of K-step k.
   // heads of this workgroup: 64 * HG starting at 64 * HG * blockIdx.y; wave w
   // holds HG groups of 16
-  const int head0 = 64 * HG * blockIdx.y + 16 * HG * wave + l16;
+  const int head0 = 16 * NW * HG * blockIdx.y + 16 * HG * wave + l16;
   bf16x8 qb[HG][KS];
 #pragma unroll
   for (int ht = 0; ht < HG; ht++) {
@@ -400,7 +406,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     const int ahead = KV8 ? tile + 1 : tile;
     if (ahead < ntiles) {
       const int later = min(NBUF - 2, ntiles - 1 - ahead);
-      if (wave == 0) {
+      if (wave < NA) {
         if (later >= 2) DSA_WAIT_VMCNT(2 * LPW); else if (later == 1) DSA_WAIT_VMCNT(LPW); else DSA_WAIT_VMCNT(0);
       } else {
         if (later >= 2) DSA_WAIT_VMCNT(2 * (LPW - 1)); else if (later == 1) DSA_WAIT_VMCNT(LPW - 1); else DSA_WAIT_VMCNT(0);
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     {
       // K-step k reads dims 32k + 8*grp .. +7 of rows l%16 and 16 + l%16;
       // QD steps are in flight at a time
-      constexpr int QD = 4;
+      constexpr int QD = (NW == 8) ? 2 : 4;
       const uint32_t ra = lds_addr(cur) + l16 * PITCH + 16 * grp;
       bf16x8 a[QD][2];
       static_for<0, QD>([&](auto D) {
@@ -557,7 +563,7 @@ __global__ __launch_bounds__(kSfaBf16Threads, 1) void sfa_bf16_kernel(SfaParams 
     {
       // M-tile mv reads columns 16 mv .. +15 of rows r0 and 16 + r0; PD tiles
       // are in flight at a time
-      constexpr int PD = 6;
+      constexpr int PD = (NW == 8) ? 4 : 6;
       const int r0 = 4 * grp + (l16 >> 2);
       const uint32_t rv = lds_addr(cur) + r0 * PITCH + 8 * (l16 & 3);
       s16x4 v[PD][2];
@@ -837,25 +843,25 @@ __global__ __launch_bounds__(256) void sfa_f32_kernel(SfaParams p) {
 
 }  // namespace
 
+// (precise weights, head groups of 16 per wave, FP8 rows, waves): decode
+// (precise weights) runs 8 waves of 16 heads, prefill 4 waves of 32, FP8
+// rows 4 waves of 16 with two workgroups per token
+int sfa_bf16_waves(const SfaParams& p) { return (!p.kv8 && p.precise_weights) ? 8 : 4; }
 const void* pick_sfa_bf16(const SfaParams& p) {
-  // (precise weights, head groups of 16 per wave, FP8 rows): 64 * HG heads per
-  // workgroup; FP8 rows always with HG = 1 (two workgroups per token)
   if (p.kv8)
     return p.precise_weights ? (const void*)sfa_bf16_kernel<576, 512, true, 1, true>
                              : (const void*)sfa_bf16_kernel<576, 512, false, 1, true>;
-  if (p.precise_weights)
-    return (p.hsplit == 2) ? (const void*)sfa_bf16_kernel<576, 512, true, 1, false>
-                           : (const void*)sfa_bf16_kernel<576, 512, true, 2, false>;
-  return (p.hsplit == 2) ? (const void*)sfa_bf16_kernel<576, 512, false, 1, false>
-                         : (const void*)sfa_bf16_kernel<576, 512, false, 2, false>;
+  if (p.precise_weights) return (const void*)sfa_bf16_kernel<576, 512, true, 1, false, 8>;
+  return (const void*)sfa_bf16_kernel<576, 512, false, 2, false>;
 }
 
 hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hipStream_t st) {
   if (p.bv.total_q == 0) return hipSuccess;
   if (dtype == kBF16 && H == 128 && Dqk == 576 && Dv == 512) {
     if (p.rows_per_split > kSfaMaxRows) return hipErrorInvalidValue;
-    if (p.hsplit != 1 && p.hsplit != 2) return hipErrorInvalidValue;
-    if (p.kv8 && (!p.kv_scale || p.hsplit != 2)) return hipErrorInvalidValue;
+    // heads per workgroup x workgroups per token must cover the 128 heads
+    if (p.hsplit != (p.kv8 ? 2 : 1)) return hipErrorInvalidValue;
+    if (p.kv8 && !p.kv_scale) return hipErrorInvalidValue;
     const void* kern = pick_sfa_bf16(p);
     const size_t lds = p.kv8 ? SfaKv8Geom<576, 512>::lds_bytes(p.rows_per_split)
                              : SfaBf16Geom<576, 512>::lds_bytes(p.rows_per_split);
@@ -864,7 +870,7 @@ hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hip
     const int chunk = (p.bv.total_q + 7) / 8;
     const dim3 grid(8 * chunk, p.hsplit, p.splits);
     void* args[] = {(void*)&p};
-    e = hipLaunchKernel(kern, grid, dim3(kSfaBf16Threads), args, lds, st);
+    e = hipLaunchKernel(kern, grid, dim3(64 * sfa_bf16_waves(p)), args, lds, st);
     if (e != hipSuccess) return e;
     return hipGetLastError();
   }

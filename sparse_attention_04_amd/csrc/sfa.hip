@@ -124,11 +124,10 @@ __device__ __forceinline__ void lds_wait(s16x4& a, s16x4& b) {
 // keeps q^T for all 576 dims in registers (72 VGPRs per group) and the O^T
 // accumulators for all 512 columns (128 per group).  Each K/V operand read
 // from LDS feeds every head group of the wave.  Configurations:
-//   * large launches (prefill): NW = 4, HG = 2, one wave per SIMD, so a wave
-//     may use the whole register file;
-//   * few query tokens (decode): NW = 8, HG = 1, two waves per SIMD, so one
-//     wave's products overlap the other's barrier and tile waits; the
-//     operand reads in flight are fewer to fit 256 registers per wave;
+//   * bf16 rows: NW = 8, HG = 1, two waves per SIMD, so one wave's products
+//     overlap the other's barrier and tile waits; the operand reads in flight
+//     are fewer to fit 256 registers per wave (NW = 4 with HG = 2, one wave
+//     per SIMD, measured 8% slower in prefill and more in decode);
 //   * FP8 rows: NW = 4, HG = 1 (two workgroups per token, grid y).
 // All heads of a token in one workgroup bring a gathered row on chip once per
 // token and range.
@@ -843,16 +842,15 @@ __global__ __launch_bounds__(256) void sfa_f32_kernel(SfaParams p) {
 
 }  // namespace
 
-// (precise weights, head groups of 16 per wave, FP8 rows, waves): decode
-// (precise weights) runs 8 waves of 16 heads, prefill 4 waves of 32, FP8
-// rows 4 waves of 16 with two workgroups per token
-int sfa_bf16_waves(const SfaParams& p) { return (!p.kv8 && p.precise_weights) ? 8 : 4; }
+// (precise weights, head groups of 16 per wave, FP8 rows, waves): bf16 rows
+// run 8 waves of 16 heads, FP8 rows 4 waves of 16 with two workgroups per token
+int sfa_bf16_waves(const SfaParams& p) { return p.kv8 ? 4 : 8; }
 const void* pick_sfa_bf16(const SfaParams& p) {
   if (p.kv8)
     return p.precise_weights ? (const void*)sfa_bf16_kernel<576, 512, true, 1, true>
                              : (const void*)sfa_bf16_kernel<576, 512, false, 1, true>;
-  if (p.precise_weights) return (const void*)sfa_bf16_kernel<576, 512, true, 1, false, 8>;
-  return (const void*)sfa_bf16_kernel<576, 512, false, 2, false>;
+  return p.precise_weights ? (const void*)sfa_bf16_kernel<576, 512, true, 1, false, 8>
+                           : (const void*)sfa_bf16_kernel<576, 512, false, 1, false, 8>;
 }
 
 hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hipStream_t st) {

@@ -23,6 +23,10 @@
  *     memory comes from the caller's workspace `ws` of `ws_bytes` bytes, sized
  *     with dsa_workspace_size().  One workspace must not be used by two calls
  *     that may run concurrently.
+ *   Alignment: the workspace and the q, k_cache / kv_cache data and output
+ *     arrays are 16-byte aligned (the kernels move them 16 bytes at a time);
+ *     scale pools, head weights, lse, index rows, lengths and block tables
+ *     4-byte aligned.  A misaligned pointer is DSA_ERR_INVALID_ARG.
  *   Ordering: work is enqueued asynchronously on `stream` (a hipStream_t, NULL
  *     = the default stream); nothing is waited for.
  *   Errors: arguments are validated on the host before anything is enqueued;

@@ -44,11 +44,15 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ------------------------------------------------------------ validation ---
 
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 dsa_status check_batch(const dsa_batch* b) {
   if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is NULL");
   if (b->batch < 1) return fail(DSA_ERR_INVALID_ARG, "batch->batch must be >= 1 (got %d)", b->batch);
   if (!b->seq_lens || !b->cu_q || !b->block_table)
     return fail(DSA_ERR_INVALID_ARG, "batch->seq_lens, cu_q and block_table must be non-NULL");
+  if (!aligned(b->seq_lens, 4) || !aligned(b->cu_q, 4) || !aligned(b->block_table, 4))
+    return fail(DSA_ERR_INVALID_ARG, "batch arrays must be 4-byte aligned");
   if (b->max_pages_per_seq < 1) return fail(DSA_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
   if (b->total_q < 0 || b->max_q_len < 0 || b->max_seq_len < 0)
     return fail(DSA_ERR_INVALID_ARG, "negative total_q / max_q_len / max_seq_len");
@@ -65,6 +69,9 @@ dsa_status check_cache(const dsa_paged_cache* c, const char* name, int dim, int 
                        const dsa_batch* b, bool allow_tile8 = false) {
   if (!c) return fail(DSA_ERR_INVALID_ARG, "%s is NULL", name);
   if (!c->data) return fail(DSA_ERR_INVALID_ARG, "%s->data is NULL", name);
+  if (!aligned(c->data, 16)) return fail(DSA_ERR_INVALID_ARG, "%s->data must be 16-byte aligned", name);
+  if (c->dtype != DSA_MXFP8_E4M3 && !aligned(c->scale, 4))
+    return fail(DSA_ERR_INVALID_ARG, "%s->scale must be 4-byte aligned", name);
   if (c->dtype != dtype && !(allow_tile8 && c->dtype == DSA_FP8_E4M3_TILE128))
     return fail(DSA_ERR_INVALID_ARG, "%s->dtype %d differs from the query dtype %d", name, c->dtype, dtype);
   if (c->dim != dim) return fail(DSA_ERR_INVALID_ARG, "%s->dim %d differs from %d", name, c->dim, dim);
@@ -84,6 +91,8 @@ dsa_status check_cache(const dsa_paged_cache* c, const char* name, int dim, int 
 dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
   if (!a) return fail(DSA_ERR_INVALID_ARG, "indexer args are NULL");
   if (!a->q || !a->head_weights) return fail(DSA_ERR_INVALID_ARG, "indexer q / head_weights are NULL");
+  if (!aligned(a->q, 16) || !aligned(a->head_weights, 4) || (a->q_dtype == DSA_FP8_E4M3 && !aligned(a->q_scale, 4)))
+    return fail(DSA_ERR_INVALID_ARG, "indexer q must be 16-byte aligned, head_weights and fp8 q_scale 4-byte aligned");
   if (a->topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", a->topk);
   if (a->q_dtype < DSA_F32 || a->q_dtype > DSA_MXFP8_E4M3) return fail(DSA_ERR_INVALID_ARG, "unknown indexer dtype %d", a->q_dtype);
   const bool ok_shape = (a->q_dtype == DSA_F32 && a->n_heads == 4 && a->head_dim == 32) ||
@@ -99,6 +108,7 @@ dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
 dsa_status check_sfa(const dsa_batch* b, const dsa_sfa_args* a) {
   if (!a) return fail(DSA_ERR_INVALID_ARG, "sfa args are NULL");
   if (!a->q) return fail(DSA_ERR_INVALID_ARG, "sfa q is NULL");
+  if (!aligned(a->q, 16)) return fail(DSA_ERR_INVALID_ARG, "sfa q must be 16-byte aligned");
   if (a->q_dtype != DSA_F32 && a->q_dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "sfa dtype %d not supported (f32, bf16)", a->q_dtype);
   const bool ok_shape = (a->q_dtype == DSA_F32 && a->n_heads == 8 && a->qk_dim == 80 && a->v_dim == 64) ||
                         (a->q_dtype == DSA_BF16 && a->n_heads == 128 && a->qk_dim == 576 && a->v_dim == 512);
@@ -394,6 +404,7 @@ dsa_status dsa_indexer_topk(const dsa_batch* b, const dsa_indexer_args* a, int32
   if (s == DSA_OK) s = check_indexer(b, a);
   if (s != DSA_OK) return s;
   if (!idx_out) return fail(DSA_ERR_INVALID_ARG, "idx_out is NULL");
+  if (!aligned(idx_out, 4) || !aligned(ws, 16)) return fail(DSA_ERR_INVALID_ARG, "idx_out must be 4-byte, ws 16-byte aligned");
   const size_t need = dsa_workspace_size(DSA_OP_INDEXER_TOPK, b, a, nullptr);
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
   return run_indexer(b, a, idx_out, (uint32_t*)ws, (hipStream_t)stream);
@@ -406,6 +417,8 @@ dsa_status dsa_sparse_attn(const dsa_batch* b, const dsa_sfa_args* a, const int3
   if (s == DSA_OK) s = check_sfa(b, a);
   if (s != DSA_OK) return s;
   if (!idx || !out) return fail(DSA_ERR_INVALID_ARG, "idx / out is NULL");
+  if (!aligned(idx, 4) || !aligned(out, 16) || !aligned(lse, 4) || !aligned(ws, 16))
+    return fail(DSA_ERR_INVALID_ARG, "out and ws must be 16-byte, idx and lse 4-byte aligned");
   if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", topk);
   const size_t need = sfa_bytes(b, a, topk);
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -421,6 +434,8 @@ dsa_status dsa_fused_decode(const dsa_batch* b, const dsa_indexer_args* ia, cons
   if (s == DSA_OK) s = check_sfa(b, sa);
   if (s != DSA_OK) return s;
   if (!out) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
+  if (!aligned(out, 16) || !aligned(lse, 4) || !aligned(idx_out, 4) || !aligned(ws, 16))
+    return fail(DSA_ERR_INVALID_ARG, "out and ws must be 16-byte, lse and idx_out 4-byte aligned");
   if (ia->k_cache->page_size != sa->kv_cache->page_size)
     return fail(DSA_ERR_INVALID_ARG, "k_cache and kv_cache must share the page size (one block table)");
   const size_t need = dsa_workspace_size(DSA_OP_FUSED_DECODE, b, ia, sa);
@@ -443,6 +458,8 @@ dsa_status dsa_fused_prefill(const dsa_batch* b, const dsa_indexer_args* ia, con
   if (s == DSA_OK) s = check_sfa(b, sa);
   if (s != DSA_OK) return s;
   if (!out) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
+  if (!aligned(out, 16) || !aligned(lse, 4) || !aligned(idx_out, 4) || !aligned(ws, 16))
+    return fail(DSA_ERR_INVALID_ARG, "out and ws must be 16-byte, lse and idx_out 4-byte aligned");
   if (q_block != 64) return fail(DSA_ERR_UNSUPPORTED, "q_block must be 64 (got %d)", q_block);
   if (ia->k_cache->page_size != sa->kv_cache->page_size)
     return fail(DSA_ERR_INVALID_ARG, "k_cache and kv_cache must share the page size (one block table)");

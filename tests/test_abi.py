@@ -137,3 +137,26 @@ def test_fp8_kv_cache_passes_validation():
         st = B.lib().dsa_fused_decode(ctypes.pointer(batch), ctypes.pointer(ia), ctypes.pointer(sa),
                                       ctypes.c_void_p(0x2000), None, None, ctypes.c_void_p(0x3000), need - 1, None)
         assert st == B.DSA_ERR_WORKSPACE_TOO_SMALL, B.lib().dsa_last_error()
+
+
+@pytest.mark.parametrize("what", ["out", "ws", "q", "kv", "bt"])
+def test_misaligned_pointers_are_rejected(what):
+    """The kernels move q, cache rows, outputs and the workspace 16 bytes at a
+    time; a misaligned pointer is refused before anything is enqueued."""
+    batch, ia, sa, (kc, vc) = _structs()
+    out, ws = 0x2000, 0x3000
+    if what == "out":
+        out = 0x2008
+    elif what == "ws":
+        ws = 0x3004
+    elif what == "q":
+        sa.q = 0x1008
+    elif what == "kv":
+        vc.data = 0x1004
+    else:
+        batch.block_table = 0x1002
+    need = B.dsa_workspace_size(B.DSA_OP_FUSED_DECODE, batch, ia, sa)
+    st = B.lib().dsa_fused_decode(ctypes.pointer(batch), ctypes.pointer(ia), ctypes.pointer(sa),
+                                  ctypes.c_void_p(out), None, None, ctypes.c_void_p(ws), need, None)
+    assert st == B.DSA_ERR_INVALID_ARG, B.lib().dsa_last_error()
+    assert b"align" in B.lib().dsa_last_error()

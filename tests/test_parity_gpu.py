@@ -166,6 +166,15 @@ def test_multi_token_decode_quantised(name):
     _run_all_paths(case)
 
 
+def test_multi_token_decode_mixed_counts():
+    # 4, 2, 3 and 1 query tokens per sequence in one launch (one, two and
+    # four wave groups per sequence), with contexts just above k so that some
+    # queries of a sequence keep every visible position while others are scored
+    case = case_to(make_case("c5_decode4", 15, batch=4, seq_lens=[2050, 5000, 2049, 6000],
+                             q_lens=[4, 2, 3, 1]), "cuda")
+    _run_all_paths(case)
+
+
 def test_multi_token_decode_f32_ragged():
     # three query tokens per sequence on the f32 path, ragged pages
     case = case_to(make_case("c1_tiny_f32", 13, batch=2, seq_len_range=(100, 250), q_len=3), "cuda")

@@ -57,6 +57,13 @@ __device__ __forceinline__ void store_relaxed_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Workgroup barrier that waits only for this wave's LDS traffic, not for its
+// outstanding global loads (a plain __syncthreads() waits for every memory
+// operation, which would drain a load pipeline at each barrier).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Barrier among the `count` workgroups sharing `ctr` (all co-resident).  The
 // round-th call returns once count*round arrivals are seen.
 //

@@ -237,7 +237,7 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
       // a workgroup's keys span at most cap_pages pages (+1 when P does not
       // divide its range start, which the page-aligned assignment avoids)
       const int64_t stage_pages = cap_pages + 1;
-      const size_t lds = indexer_decode_lds_bytes(maxq, (int)std::min<int64_t>(cap_keys, 1 << 24),
+      const size_t lds = indexer_decode_lds_bytes(dt, maxq, (int)std::min<int64_t>(cap_keys, 1 << 24),
                                                   (int)std::min<int64_t>(stage_pages, 1 << 24));
       if (lds > kLdsMax) continue;
       int occ = 0;

@@ -39,6 +39,15 @@ constexpr int kIdxWaves = kIdxThreads / kWave;
 constexpr int kBinsPerThread = kRadixBins / kIdxThreads;
 static_assert(kMaxDecodeQ <= 4 && kIdxWaves % 4 == 0, "wave groups per decode query");
 static_assert(kRadixBins % kIdxThreads == 0, "histogram bins split evenly over the threads");
+// bf16 keys with three or four query tokens: 64-key steps whose quarter tiles
+// a wave holds in registers (one being staged, kXchgRing - 1 in flight), and
+// the two 16-KiB LDS slots they are shared through
+constexpr int kXchgRing = 8;
+constexpr int kXchgSlotWords = 64 * 128 * 2 / 4;
+
+__host__ __device__ constexpr size_t xchg_offset_words(int maxq, int chunk_cap, int stage_pages) {
+  return ((size_t)maxq * chunk_cap + kRadixBins + stage_pages + 3) / 4 * 4;
+}
 
 // Workspace layout (uint32 words), see indexer_ws_words().
 //   [0, 64)                        header: error bits
@@ -277,11 +286,13 @@ enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3 };
 
 template <int DT, int H, int D, int MAXQ>
 __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerDecodeParams p) {
-  extern __shared__ uint32_t smem[];
-  // dynamic LDS: sc[MAXQ][cap] | lhist[2048] | s_bt[stage_pages]
+  extern __shared__ __align__(16) uint32_t smem[];
+  // dynamic LDS: sc[MAXQ][cap] | lhist[2048] | s_bt[stage_pages] | xs (bf16,
+  // several queries: two 16-KiB slots of the shared key tiles, 16-B aligned)
   uint32_t* sc = smem;
   uint32_t* lhist = smem + (size_t)MAXQ * p.chunk_cap;
   int* s_bt = (int*)(lhist + kRadixBins);
+  u32x4* xs = (u32x4*)(smem + xchg_offset_words(MAXQ, p.chunk_cap, p.stage_pages));
   __shared__ int s_seqinfo[8];
   __shared__ int s_scan[kIdxThreads];
   __shared__ int s_rank[kIdxWaves + 1];
@@ -442,8 +453,78 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
         }
       }
     };
-    if (staged) score_range(std::true_type{});
-    else score_range(std::false_type{});
+    // Three or four query tokens (bf16): the four waves that score one 32-key
+    // tile for different queries each load a quarter of a 64-key step and the
+    // step is shared through LDS, so a wave's registers hold four times as
+    // many distinct keys in flight as when every wave loads the whole tile.
+    // Step c: 64 keys x 16 granules of 16 B; wave w loads LDS positions
+    // 128 w + 64 i + lane (i = 0, 1), position n*16 + g holding granule
+    // g ^ (n & 15) of key n, so the tile reads below hit 16 distinct bank
+    // groups per 16 lanes.  Two slots alternate, one barrier per step: a slot
+    // is rewritten two steps after it was read, across the barrier between.
+    bool shared_done = false;
+    if constexpr (DT == kBF16 && MAXQ == 4) {
+      static_assert(D == 128 && kIdxWaves == 8, "four queries x two 32-key halves of a 64-key step");
+      if (T >= 3 && staged && nloc > 0) {
+        constexpr int R = kXchgRing;
+        const int nsteps = (nloc + 63) / 64;
+        const int q = wave & 3, ph = wave >> 2;
+        const bool act = q < T && s_state[q] == kActive;
+        if (act) scorer.load_query(p, tok0 + q);
+        int key_i[2], seg_i[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+          const int pos = 128 * wave + 64 * i + lane;
+          key_i[i] = pos >> 4;
+          seg_i[i] = (pos & 15) ^ (key_i[i] & 15);
+        }
+        auto fetch = [&](int c, u32x4 (&r)[2]) {
+          c = min(c, nsteps - 1);  // past the end: reload the last step, unused
+#pragma unroll
+          for (int i = 0; i < 2; i++) {
+            const int s = min(s0 + 64 * c + key_i[i], s1 - 1);
+            const int64_t row = ((int64_t)s_bt[(s >> PS) - pg0] << PS) + (s & (P - 1));
+            r[i] = ((const u32x4*)((const uint16_t*)p.k_data + row * D))[seg_i[i]];
+          }
+        };
+        const int n = 32 * ph + (lane & 31);
+        const int rbase = 16 * n, rx = n & 15, rh = 8 * (lane >> 5);
+        const int t = L - T + q;
+        uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+        u32x4 rg[R][2];
+        // issued in step order (kept so by the scheduling barriers): the wait
+        // before each step's LDS store then leaves the later steps in flight
+#pragma unroll
+        for (int d = 0; d < R - 1; d++) {
+          fetch(d, rg[d]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int base = 0; base < nsteps; base += R) {
+#pragma unroll
+          for (int d = 0; d < R; d++) {
+            const int c = base + d;
+            u32x4* slot = xs + (c & 1) * (kXchgSlotWords / 4);
+            slot[128 * wave + lane] = rg[d][0];
+            slot[128 * wave + 64 + lane] = rg[d][1];
+            fetch(c + R - 1, rg[(d + R - 1) % R]);
+            lds_barrier();
+            if (act && c < nsteps) {
+              Tile tl;
+#pragma unroll
+              for (int kk = 0; kk < MfmaScorer<DT, H, D>::KS; kk++) tl.v[kk] = slot[rbase + ((rh + kk) ^ rx)];
+              const float v = scorer.score(p, 0, tl);
+              const int s = s0 + 64 * c + 32 * ph + lane;
+              if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
+            }
+          }
+        }
+        shared_done = true;
+      }
+    }
+    if (!shared_done) {
+      if (staged) score_range(std::true_type{});
+      else score_range(std::false_type{});
+    }
   }
   __syncthreads();
   DSA_STAMP(2);
@@ -701,8 +782,9 @@ static hipError_t launch_one(const IndexerDecodeParams& p, size_t lds, hipStream
 
 int indexer_decode_max_q() { return kMaxDecodeQ; }
 
-size_t indexer_decode_lds_bytes(int maxq, int chunk_cap, int stage_pages) {
-  return ((size_t)maxq * chunk_cap + kRadixBins + stage_pages) * 4;
+size_t indexer_decode_lds_bytes(int dtype, int maxq, int chunk_cap, int stage_pages) {
+  const size_t xchg = (dtype == kBF16 && maxq == 4) ? 2 * kXchgSlotWords : 0;
+  return (xchg_offset_words(maxq, chunk_cap, stage_pages) + xchg) * 4;
 }
 
 hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t lds, int* blocks_per_cu) {
@@ -719,7 +801,7 @@ hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t ld
 
 hipError_t launch_indexer_decode(int dtype, int H, int D, int maxq, const IndexerDecodeParams& p,
                                  hipStream_t st) {
-  const size_t lds = indexer_decode_lds_bytes(maxq, p.chunk_cap, p.stage_pages);
+  const size_t lds = indexer_decode_lds_bytes(dtype, maxq, p.chunk_cap, p.stage_pages);
 #define DSA_PICK(DT_, H_, D_, Q_) \
   if (dtype == DT_ && H == H_ && D == D_ && maxq == Q_) return launch_one<DT_, H_, D_, Q_>(p, lds, st);
   DSA_INDEXER_DECODE_SHAPES(DSA_PICK)

@@ -36,7 +36,7 @@ struct IndexerDecodeParams {
 
 size_t indexer_ws_bytes(int nseq, int nq, int grid);
 size_t indexer_ws_zero_bytes(int nseq, int nq);
-size_t indexer_decode_lds_bytes(int maxq, int chunk_cap, int stage_pages);
+size_t indexer_decode_lds_bytes(int dtype, int maxq, int chunk_cap, int stage_pages);
 hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t lds, int* blocks_per_cu);
 hipError_t launch_indexer_decode(int dtype, int H, int D, int maxq, const IndexerDecodeParams& p,
                                  hipStream_t st);

@@ -51,12 +51,6 @@ __device__ __forceinline__ int find_seq(const BatchView& bv, int tok) {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Workgroup barrier that waits only for this wave's LDS traffic, not for its
-// outstanding global->LDS tile loads (a plain __syncthreads() waits for every
-// memory operation, which would drain the load pipeline at each barrier).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // One 16-byte-per-lane global->LDS load (64 lanes fill lds_base .. +1 KiB in
 // lane order).  Issued through inline assembly so that the compiler's

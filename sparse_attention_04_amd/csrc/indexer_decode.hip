@@ -42,7 +42,7 @@ static_assert(kRadixBins % kIdxThreads == 0, "histogram bins split evenly over t
 // bf16 keys with three or four query tokens: 64-key steps whose quarter tiles
 // a wave holds in registers (one being staged, kXchgRing - 1 in flight), and
 // the two 16-KiB LDS slots they are shared through
-constexpr int kXchgRing = 8;
+constexpr int kXchgRing = 4;
 constexpr int kXchgSlotWords = 64 * 128 * 2 / 4;
 
 __host__ __device__ constexpr size_t xchg_offset_words(int maxq, int chunk_cap, int stage_pages) {
@@ -135,8 +135,8 @@ struct MfmaScorer<kBF16, H, D> {
     for (int kk = 0; kk < KS; kk++) t.v[kk] = src[kk];
   }
 
-  __device__ float score(const IndexerDecodeParams& p, int64_t row, const Tile& t) const {
-    f32x16 acc[MT];
+  // per-head products of the tile's 32 keys: acc[mt] = heads 32 mt .. +31
+  __device__ void mma(const Tile& t, f32x16 (&acc)[MT]) const {
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -148,12 +148,20 @@ struct MfmaScorer<kBF16, H, D> {
       for (int mt = 0; mt < MT; mt++)
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], b, acc[mt], 0, 0, 0);
     }
+  }
+  // head-weighted sum: lane n and lane n + 32 both return key n's score
+  __device__ float head_sum(const f32x16 (&acc)[MT]) const {
     float s = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
       for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[mt][i], s);
     return s + __shfl_xor(s, 32);
+  }
+  __device__ float score(const IndexerDecodeParams& p, int64_t row, const Tile& t) const {
+    f32x16 acc[MT];
+    mma(t, acc);
+    return head_sum(acc);
   }
 };
 
@@ -491,6 +499,12 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
         const int rbase = 16 * n, rx = n & 15, rh = 8 * (lane >> 5);
         const int t = L - T + q;
         uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+        auto store = [&](int c, float v) {
+          const int s = s0 + 64 * c + 32 * ph + lane;
+          if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
+        };
+        f32x16 pacc[MfmaScorer<DT, H, D>::MT];
+        int pc = -1;  // step whose products pacc holds, not yet summed
         u32x4 rg[R][2];
         // issued in step order (kept so by the scheduling barriers): the wait
         // before each step's LDS store then leaves the later steps in flight
@@ -508,16 +522,27 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
             slot[128 * wave + 64 + lane] = rg[d][1];
             fetch(c + R - 1, rg[(d + R - 1) % R]);
             lds_barrier();
-            if (act && c < nsteps) {
+            // The two waves on a SIMD (phases 0 and 1) would otherwise run
+            // their MFMAs together and then their head sums together; phase 1
+            // sums its previous step after this barrier instead, so one
+            // wave's VALU work overlaps the other's MFMAs.
+            if (act) {
               Tile tl;
+              if (c < nsteps) {
 #pragma unroll
-              for (int kk = 0; kk < MfmaScorer<DT, H, D>::KS; kk++) tl.v[kk] = slot[rbase + ((rh + kk) ^ rx)];
-              const float v = scorer.score(p, 0, tl);
-              const int s = s0 + 64 * c + 32 * ph + lane;
-              if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
+                for (int kk = 0; kk < MfmaScorer<DT, H, D>::KS; kk++) tl.v[kk] = slot[rbase + ((rh + kk) ^ rx)];
+              }
+              if (ph == 1 && pc >= 0) store(pc, scorer.head_sum(pacc));
+              pc = -1;
+              if (c < nsteps) {
+                scorer.mma(tl, pacc);
+                pc = c;
+              }
+              if (ph == 0 && pc >= 0) store(pc, scorer.head_sum(pacc));
             }
           }
         }
+        if (act && ph == 1 && pc >= 0) store(pc, scorer.head_sum(pacc));
         shared_done = true;
       }
     }

@@ -233,7 +233,8 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
     const int G = std::min(kMaxGrid, per_cu * di.cus);
     for (int nb = std::min(b->batch, G / 2); nb >= 1; nb = (nb > 1) ? nb / 2 : 0) {
       const int64_t cap_pages = ((int64_t)nb * std::max(1, maxp) + (G - nb) - 1) / (G - nb);
-      const int64_t cap_keys = cap_pages * P;
+      // rounded up to 8 keys: the kernel's selection sweeps read 8 scores at once
+      const int64_t cap_keys = (cap_pages * P + 7) / 8 * 8;
       // a workgroup's keys span at most cap_pages pages (+1 when P does not
       // divide its range start, which the page-aligned assignment avoids)
       const int64_t stage_pages = cap_pages + 1;

@@ -41,9 +41,11 @@ static_assert(kMaxDecodeQ <= 4 && kIdxWaves % 4 == 0, "wave groups per decode qu
 static_assert(kRadixBins % kIdxThreads == 0, "histogram bins split evenly over the threads");
 // bf16 keys with three or four query tokens: 64-key steps whose quarter tiles
 // a wave holds in registers (one being staged, kXchgRing - 1 in flight), and
-// the two 16-KiB LDS slots they are shared through
+// the two 16-KiB LDS slots they are shared through (the same 32 KiB later
+// hold the per-query radix histograms of every several-query kernel)
 constexpr int kXchgRing = 4;
 constexpr int kXchgSlotWords = 64 * 128 * 2 / 4;
+static_assert(2 * kXchgSlotWords >= kMaxDecodeQ * kRadixBins, "the exchange area holds one histogram per query");
 
 __host__ __device__ constexpr size_t xchg_offset_words(int maxq, int chunk_cap, int stage_pages) {
   return ((size_t)maxq * chunk_cap + kRadixBins + stage_pages + 3) / 4 * 4;
@@ -295,8 +297,9 @@ enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3 };
 template <int DT, int H, int D, int MAXQ>
 __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerDecodeParams p) {
   extern __shared__ __align__(16) uint32_t smem[];
-  // dynamic LDS: sc[MAXQ][cap] | lhist[2048] | s_bt[stage_pages] | xs (bf16,
-  // several queries: two 16-KiB slots of the shared key tiles, 16-B aligned)
+  // dynamic LDS: sc[MAXQ][cap] | lhist[2048] | s_bt[stage_pages] | xs (several
+  // queries, 32 KiB, 16-B aligned: while scoring bf16 keys, the two slots of
+  // the shared key steps; then one radix histogram per query)
   uint32_t* sc = smem;
   uint32_t* lhist = smem + (size_t)MAXQ * p.chunk_cap;
   int* s_bt = (int*)(lhist + kRadixBins);
@@ -306,7 +309,6 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
   __shared__ int s_rank[kIdxWaves + 1];
   __shared__ uint32_t s_prefix[MAXQ], s_pmask[MAXQ];
   __shared__ int s_need[MAXQ], s_state[MAXQ], s_take[MAXQ];
-  __shared__ int s_bin, s_above, s_bincnt;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const BatchView& bv = p.bv;
@@ -555,6 +557,13 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
   DSA_STAMP(2);
 
   // ---- 3. radix passes ------------------------------------------------------
+  // Every active query of the sequence goes through a pass together: one LDS
+  // histogram per query (the several-query kernels reuse the key-exchange
+  // area for them), one cross-workgroup barrier per pass, and the global bin
+  // loads of all queries in flight at once.
+  uint32_t* qhist = (MAXQ > 1) ? (uint32_t*)xs : lhist;
+  __shared__ int s_scanq[MAXQ][kIdxWaves];
+  __shared__ int s_binq[MAXQ], s_aboveq[MAXQ], s_bincntq[MAXQ];
   int round = 0;
   for (int pass = 0; pass < kMaxPasses; pass++) {
     bool act = false;
@@ -564,18 +573,33 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
     const uint32_t dmask = (pass < 2) ? 0x7FFu : 0x3FFu;
     for (int q = 0; q < T && q < MAXQ; q++) {
       if (s_state[q] != kActive) continue;
-      for (int i = tid; i < kRadixBins; i += kIdxThreads) lhist[i] = 0u;
-      __syncthreads();
+      for (int i = tid; i < kRadixBins / 4; i += kIdxThreads) ((u32x4*)(qhist + q * kRadixBins))[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    // each thread takes 8 consecutive keys per round (two 16-B LDS reads ahead
+    // of their atomics; chunk_cap is a multiple of 8, so the reads stay inside
+    // the buffer and keys past nloc are masked)
+    for (int q = 0; q < T && q < MAXQ; q++) {
+      if (s_state[q] != kActive) continue;
       const uint32_t pre = s_prefix[q], pm = s_pmask[q];
       const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
-      for (int i = tid; i < nloc; i += kIdxThreads) {
-        const uint32_t x = scq[i];
-        if (x != 0u && (x & pm) == pre) atomicAdd(&lhist[(x >> shift) & dmask], 1u);
+      uint32_t* h = qhist + q * kRadixBins;
+      for (int i0 = 8 * tid; i0 < nloc; i0 += 8 * kIdxThreads) {
+        const u32x4 va = *(const u32x4*)(scq + i0);
+        const u32x4 vb = *(const u32x4*)(scq + i0 + 4);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const uint32_t x = (i0 + e < nloc) ? ((e < 4) ? va[e & 3] : vb[e & 3]) : 0u;
+          if (x != 0u && (x & pm) == pre) atomicAdd(&h[(x >> shift) & dmask], 1u);
+        }
       }
-      __syncthreads();
+    }
+    __syncthreads();
+    for (int q = 0; q < T && q < MAXQ; q++) {
+      if (s_state[q] != kActive) continue;
       uint32_t* gh = W.hist(tok0 + q, pass);
       for (int i = tid; i < kRadixBins; i += kIdxThreads) {
-        const uint32_t c = lhist[i];
+        const uint32_t c = qhist[q * kRadixBins + i];
         if (c) atomic_add_agent(&gh[i], c);
       }
       if (j == 0 && pass + 1 < kMaxPasses) {
@@ -587,62 +611,74 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
     round++;
     group_barrier(ctr, (uint32_t)(nb * round), W.err());
     DSA_STAMP(4 + 3 * pass);
-    for (int q = 0; q < T && q < MAXQ; q++) {
-      if (s_state[q] != kActive) continue;
-      const uint32_t* gh = W.hist(tok0 + q, pass);
-      // each thread owns kBinsPerThread consecutive bins; suffix sums from
-      // the top bin down
-      uint32_t h8[kBinsPerThread];
-      uint32_t csum = 0;
+    // each thread owns kBinsPerThread consecutive bins of every query; suffix
+    // sums from the top bin down
+    uint32_t h8[MAXQ][kBinsPerThread];
+    bool qa[MAXQ];
 #pragma unroll
-      for (int e = 0; e < kBinsPerThread; e++) {
-        h8[e] = load_relaxed_agent(&gh[kBinsPerThread * tid + e]);
-        csum += h8[e];
-      }
-      // suffix sums over threads: above[t] = sum of the counts of threads > t
-      int x = (int)csum;
+    for (int q = 0; q < MAXQ; q++) {
+      qa[q] = q < T && s_state[q] == kActive;
+      const uint32_t* gh = W.hist(tok0 + q, pass);
+#pragma unroll
+      for (int e = 0; e < kBinsPerThread; e++)
+        h8[q][e] = qa[q] ? load_relaxed_agent(&gh[kBinsPerThread * tid + e]) : 0u;
+    }
+    if (tid < MAXQ) {
+      s_binq[tid] = 0;
+      s_aboveq[tid] = 0;
+      s_bincntq[tid] = 0;
+    }
+    int xq[MAXQ];
+    uint32_t csq[MAXQ];
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) {
+      csq[q] = 0;
+#pragma unroll
+      for (int e = 0; e < kBinsPerThread; e++) csq[q] += h8[q][e];
+      // suffix sums over the wave: counts of this lane and the lanes above
+      int x = (int)csq[q];
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_down(x, o);
         if (lane + o < 64) x += v;
       }
-      if (lane == 0) s_scan[wave] = x;  // wave total
-      __syncthreads();
+      xq[q] = x;
+      if (lane == 0) s_scanq[q][wave] = x;  // wave total
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) {
+      if (!qa[q]) continue;
       int later = 0;
 #pragma unroll
-      for (int w = 0; w < kIdxWaves; w++) later += (w > wave) ? s_scan[w] : 0;
-      const int incl = x + later;       // this thread's bins and everything above
+      for (int w = 0; w < kIdxWaves; w++) later += (w > wave) ? s_scanq[q][w] : 0;
+      const int incl = xq[q] + later;            // this thread's bins and everything above
+      const int above = incl - (int)csq[q];      // bins above this thread's own
       const int need = s_need[q];
-      if (tid == 0) {
-        s_bin = 0;
-        s_above = 0;
-        s_bincnt = 0;
-      }
-      __syncthreads();
-      const int above = incl - (int)csum;  // bins above this thread's own
-      if (above < need && need <= above + (int)csum) {
+      if (above < need && need <= above + (int)csq[q]) {
         int run = above;
         for (int e = kBinsPerThread - 1; e >= 0; e--) {
-          if (run + (int)h8[e] >= need) {
-            s_bin = kBinsPerThread * tid + e;
-            s_above = run;
-            s_bincnt = (int)h8[e];
+          if (run + (int)h8[q][e] >= need) {
+            s_binq[q] = kBinsPerThread * tid + e;
+            s_aboveq[q] = run;
+            s_bincntq[q] = (int)h8[q][e];
             break;
           }
-          run += (int)h8[e];
+          run += (int)h8[q][e];
         }
       }
-      __syncthreads();
-      if (tid == 0) {
-        const int nneed = need - s_above;
-        s_need[q] = nneed;
-        s_prefix[q] |= ((uint32_t)s_bin) << shift;
-        s_pmask[q] |= dmask << shift;
-        if (s_bincnt == nneed) s_state[q] = kTakeBin;
-        else if (pass == kMaxPasses - 1) s_state[q] = kTiePass;
-      }
-      __syncthreads();
     }
+    __syncthreads();
+    if (tid < T && tid < MAXQ && s_state[tid] == kActive) {
+      const int q = tid;
+      const int nneed = s_need[q] - s_aboveq[q];
+      s_need[q] = nneed;
+      s_prefix[q] |= ((uint32_t)s_binq[q]) << shift;
+      s_pmask[q] |= dmask << shift;
+      if (s_bincntq[q] == nneed) s_state[q] = kTakeBin;
+      else if (pass == kMaxPasses - 1) s_state[q] = kTiePass;
+    }
+    __syncthreads();
     DSA_STAMP(5 + 3 * pass);
   }
   DSA_STAMP(12);
@@ -683,37 +719,67 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
 
   DSA_STAMP(13);
   // ---- 4. append this workgroup's selected positions ------------------------
+  // Queries whose boundary bin is taken whole: every key at or above it.  Each
+  // wave counts its keys of every such query, reserves its slots of all of
+  // them at once (lane q: one atomic for query q), then writes them.
+  {
+    bool tb[MAXQ];
+    int cnt[MAXQ];
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) {
+      tb[q] = q < T && s_state[q] == kTakeBin;
+      cnt[q] = 0;
+      if (!tb[q]) continue;
+      const uint32_t pre = s_prefix[q], pm = s_pmask[q];
+      const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+      // lane: 4 consecutive keys per round, one 16-B LDS read
+      int c = 0;
+      for (int i0 = 4 * kWave * wave; i0 < nloc; i0 += 4 * kIdxThreads) {
+        const int i = i0 + 4 * lane;
+        const u32x4 v = (i < nloc) ? *(const u32x4*)(scq + i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const uint32_t x = (i + e < nloc) ? v[e] : 0u;
+          c += (x != 0u && (x & pm) >= pre) ? 1 : 0;
+        }
+      }
+      cnt[q] = wave_sum(c);
+    }
+    int mine = 0;
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) mine = (lane == q) ? cnt[q] : mine;
+    int base_l = 0;
+    if (lane < MAXQ && mine) base_l = (int)atomic_add_agent(W.outcnt(tok0 + lane), (uint32_t)mine);
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) {
+      if (!tb[q]) continue;
+      const uint32_t pre = s_prefix[q], pm = s_pmask[q];
+      const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+      int32_t* row = p.idx_out + (size_t)(tok0 + q) * K;
+      int base = __shfl(base_l, q);
+      for (int i0 = 4 * kWave * wave; i0 < nloc; i0 += 4 * kIdxThreads) {
+        const int i = i0 + 4 * lane;
+        const u32x4 v = (i < nloc) ? *(const u32x4*)(scq + i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const uint32_t x = (i + e < nloc) ? v[e] : 0u;
+          const bool sel = x != 0u && (x & pm) >= pre;
+          const uint64_t m = __ballot(sel);
+          const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+          if (sel && base + r < K) row[base + r] = s0 + i + e;
+          base += __popcll(m);
+        }
+      }
+    }
+  }
   for (int q = 0; q < T && q < MAXQ; q++) {
     const int st = s_state[q];
-    if (st == kAll) continue;
+    if (st != kTiePass) continue;
     const uint32_t pre = s_prefix[q], pm = s_pmask[q];
     const int take = s_take[q];
     const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
     int32_t* row = p.idx_out + (size_t)(tok0 + q) * K;
     uint32_t* oc = W.outcnt(tok0 + q);
-    if (st == kTakeBin) {
-      // every key at or above the boundary bin: each wave counts its keys,
-      // reserves its slots with one atomic, then writes them
-      int cnt = 0;
-      for (int i0 = wave * kWave; i0 < nloc; i0 += kIdxThreads) {
-        const int i = i0 + lane;
-        const uint32_t x = (i < nloc) ? scq[i] : 0u;
-        cnt += __popcll(__ballot(x != 0u && (x & pm) >= pre));
-      }
-      int base = 0;
-      if (lane == 0 && cnt) base = (int)atomic_add_agent(oc, (uint32_t)cnt);
-      base = __shfl(base, 0);
-      for (int i0 = wave * kWave; i0 < nloc; i0 += kIdxThreads) {
-        const int i = i0 + lane;
-        const uint32_t x = (i < nloc) ? scq[i] : 0u;
-        const bool sel = x != 0u && (x & pm) >= pre;
-        const uint64_t m = __ballot(sel);
-        const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (sel && base + r < K) row[base + r] = s0 + i;
-        base += __popcll(m);
-      }
-      continue;
-    }
     // equal keys straddle the boundary: ties are taken in position order, so
     // rank them across the whole workgroup
     __shared__ int s_base;
@@ -808,7 +874,8 @@ static hipError_t launch_one(const IndexerDecodeParams& p, size_t lds, hipStream
 int indexer_decode_max_q() { return kMaxDecodeQ; }
 
 size_t indexer_decode_lds_bytes(int dtype, int maxq, int chunk_cap, int stage_pages) {
-  const size_t xchg = (dtype == kBF16 && maxq == 4) ? 2 * kXchgSlotWords : 0;
+  (void)dtype;
+  const size_t xchg = (maxq > 1) ? 2 * kXchgSlotWords : 0;
   return (xchg_offset_words(maxq, chunk_cap, stage_pages) + xchg) * 4;
 }
 

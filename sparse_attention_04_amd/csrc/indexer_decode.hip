@@ -720,9 +720,13 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
   DSA_STAMP(13);
   // ---- 4. append this workgroup's selected positions ------------------------
   // Queries whose boundary bin is taken whole: every key at or above it.  Each
-  // wave counts its keys of every such query, reserves its slots of all of
-  // them at once (lane q: one atomic for query q), then writes them.
+  // wave counts its keys of every such query; the workgroup reserves its slots
+  // with one atomic per query (all a sequence's workgroups add to the same
+  // counter, so fewer, larger reservations wait less on each other); then
+  // each wave writes its keys from its offset within the workgroup's range.
   {
+    __shared__ int s_wcnt[MAXQ][kIdxWaves];
+    __shared__ int s_wgbase[MAXQ];
     bool tb[MAXQ];
     int cnt[MAXQ];
 #pragma unroll
@@ -745,18 +749,27 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
       }
       cnt[q] = wave_sum(c);
     }
-    int mine = 0;
+    if (lane == 0) {
 #pragma unroll
-    for (int q = 0; q < MAXQ; q++) mine = (lane == q) ? cnt[q] : mine;
-    int base_l = 0;
-    if (lane < MAXQ && mine) base_l = (int)atomic_add_agent(W.outcnt(tok0 + lane), (uint32_t)mine);
+      for (int q = 0; q < MAXQ; q++) s_wcnt[q][wave] = cnt[q];
+    }
+    __syncthreads();
+    if (tid < MAXQ) {
+      int tot = 0;
+#pragma unroll
+      for (int w = 0; w < kIdxWaves; w++) tot += s_wcnt[tid][w];
+      s_wgbase[tid] = tot ? (int)atomic_add_agent(W.outcnt(tok0 + tid), (uint32_t)tot) : 0;
+    }
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < MAXQ; q++) {
       if (!tb[q]) continue;
       const uint32_t pre = s_prefix[q], pm = s_pmask[q];
       const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
       int32_t* row = p.idx_out + (size_t)(tok0 + q) * K;
-      int base = __shfl(base_l, q);
+      int base = s_wgbase[q];
+#pragma unroll
+      for (int w = 0; w < kIdxWaves; w++) base += (w < wave) ? s_wcnt[q][w] : 0;
       for (int i0 = 4 * kWave * wave; i0 < nloc; i0 += 4 * kIdxThreads) {
         const int i = i0 + 4 * lane;
         const u32x4 v = (i < nloc) ? *(const u32x4*)(scq + i) : u32x4{0u, 0u, 0u, 0u};

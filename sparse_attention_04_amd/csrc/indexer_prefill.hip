@@ -45,9 +45,6 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 #define DSA_PF_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
 __device__ __forceinline__ int lane_rank(uint64_t m) {

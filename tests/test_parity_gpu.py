@@ -175,6 +175,15 @@ def test_multi_token_decode_mixed_counts():
     _run_all_paths(case)
 
 
+def test_multi_token_decode_small_pages():
+    # bf16 keys, three and four query tokens over 16-token pages: every
+    # 64-key step of the shared-step scorer spans four pages, and contexts end
+    # inside a step
+    case = case_to(make_case("c5_decode4", 16, batch=3, seq_lens=[2100, 3333, 5001],
+                             q_lens=[4, 3, 4], page_size=16), "cuda")
+    _run_all_paths(case)
+
+
 def test_multi_token_decode_f32_ragged():
     # three query tokens per sequence on the f32 path, ragged pages
     case = case_to(make_case("c1_tiny_f32", 13, batch=2, seq_len_range=(100, 250), q_len=3), "cuda")

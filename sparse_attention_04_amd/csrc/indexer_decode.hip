@@ -151,13 +151,16 @@ struct MfmaScorer<kBF16, H, D> {
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], b, acc[mt], 0, 0, 0);
     }
   }
-  // head-weighted sum: lane n and lane n + 32 both return key n's score
+  // head-weighted sum: lane n and lane n + 32 both return key n's score.
+  // Four partial sums (entries i mod 4 of each M-tile), added pairwise, the
+  // same order as the prefill indexer's.
   __device__ float head_sum(const f32x16 (&acc)[MT]) const {
-    float s = 0.f;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-      for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[mt][i], s);
+      for (int i = 0; i < 16; i++) s4[i & 3] = fmaf(wr[mt][i], acc[mt][i], s4[i & 3]);
+    const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     return s + __shfl_xor(s, 32);
   }
   __device__ float score(const IndexerDecodeParams& p, int64_t row, const Tile& t) const {

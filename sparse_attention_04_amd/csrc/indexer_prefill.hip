@@ -368,11 +368,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
           }
 #pragma unroll
           for (int n = 0; n < 2; n++) {
-            float s = 0.f;
+            // four partial sums (entries i mod 4 of each M-tile), added
+            // pairwise: shorter dependency chains than one running sum; the
+            // decode indexer's bf16 scorer sums in the same order
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-              for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[n][mt][i], s);
+              for (int i = 0; i < 16; i++) s4[i & 3] = fmaf(wr[mt][i], acc[n][mt][i], s4[i & 3]);
+            const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
             const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
             sc[n] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);   // lanes l and l ^ 32 summed
           }

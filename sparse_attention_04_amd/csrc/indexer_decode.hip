@@ -244,11 +244,13 @@ struct MfmaScorerF8 {
         acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][kk], t.v[kk], acc[mt], 0, 0,
                                                                   0, sa[mt][kk], 0, sb);
     }
-    float s = 0.f;
+    // four partial sums added pairwise, as in the bf16 scorer
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-      for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[mt][i], s);
+      for (int i = 0; i < 16; i++) s4[i & 3] = fmaf(wr[mt][i], acc[mt][i], s4[i & 3]);
+    float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     s += __shfl_xor(s, 32);
     if constexpr (DT == kFP8) {
       // the key's per-token scale (lane l%32 loaded it for its own key)

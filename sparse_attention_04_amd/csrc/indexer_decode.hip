@@ -152,15 +152,14 @@ struct MfmaScorer<kBF16, H, D> {
     }
   }
   // head-weighted sum: lane n and lane n + 32 both return key n's score.
-  // Four partial sums (entries i mod 4 of each M-tile), added pairwise, the
-  // same order as the prefill indexer's.
+  // One running sum: here the sum overlaps the other wave's MFMAs, and four
+  // partial sums (the prefill indexer's order) measured slightly slower.
   __device__ float head_sum(const f32x16 (&acc)[MT]) const {
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    float s = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-      for (int i = 0; i < 16; i++) s4[i & 3] = fmaf(wr[mt][i], acc[mt][i], s4[i & 3]);
-    const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      for (int i = 0; i < 16; i++) s = fmaf(wr[mt][i], acc[mt][i], s);
     return s + __shfl_xor(s, 32);
   }
   __device__ float score(const IndexerDecodeParams& p, int64_t row, const Tile& t) const {
@@ -244,7 +243,7 @@ struct MfmaScorerF8 {
         acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][kk], t.v[kk], acc[mt], 0, 0,
                                                                   0, sa[mt][kk], 0, sb);
     }
-    // four partial sums added pairwise, as in the bf16 scorer
+    // four partial sums added pairwise (as in the prefill indexer)
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)

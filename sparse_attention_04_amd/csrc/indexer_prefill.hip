@@ -369,8 +369,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
 #pragma unroll
           for (int n = 0; n < 2; n++) {
             // four partial sums (entries i mod 4 of each M-tile), added
-            // pairwise: shorter dependency chains than one running sum; the
-            // decode indexer's bf16 scorer sums in the same order
+            // pairwise: shorter dependency chains than one running sum
             float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mt = 0; mt < MT; mt++)

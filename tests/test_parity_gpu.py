@@ -311,6 +311,27 @@ def test_c5_decode4_full_size_sampled():
     _check_rows_valid(case, idx_h)
 
 
+def test_multi_token_decode_sub_batches():
+    """Four query tokens for 32 sequences of about 56k tokens (bf16).  With all
+    32 in one launch a workgroup would hold about 8000 keys x 4 queries of
+    scores plus the 32 KiB key-exchange area, more than the LDS; the decode
+    planner then launches sub-batches of 16 sequences.  Sampled queries of
+    both halves, the SFA on them, and every row's properties."""
+    _say("multi-token sub-batches: generating on device")
+    case = make_case("c5_decode4", 17, device="cuda", batch=32, seq_len_range=(54000, 57000))
+    call = B.Call(case)
+    _say("multi-token sub-batches: fused_decode")
+    out, lse, idx = call.fused_decode()
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    qs = [(0, 0), (15, 3), (16, 0), (31, 3)]
+    for (b, i) in qs:
+        _say(f"multi-token sub-batches: oracle query b={b} i={i}")
+        check_topk_row(idx_h[case.token(b, i)], oracle.run_query(case, b, i), case.topk)
+    _check_sfa_on(case, out, qs, idx_h)
+    _check_rows_valid(case, idx_h)
+
+
 def test_fused_equals_composition():
     case = case_to(make_case("c2_decode_bf16", 8, batch=3, seq_len_range=(3000, 5000)), "cuda")
     call = B.Call(case)

@@ -321,8 +321,11 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
   DSA_STAMP(0);
 
   // ---- 1. which sequence / page range this workgroup owns ------------------
-  // pages_b = ceil(L_b / P); cap = ceil(sum pages / (grid - B)); sequence b
-  // gets ceil(pages_b / cap) workgroups of at most cap pages each.
+  // pages_b = ceil(L_b / P); sequence b gets ceil(pages_b / cap) workgroups of
+  // at most cap pages each, cap being the smallest with sum_b ceil(pages_b /
+  // cap) <= grid.  Binary search between ceil(sum pages / grid) and
+  // ceil(sum pages / (grid - B)), which always fits (each sequence's last
+  // workgroup wastes less than one) and is the bound the host sizes LDS by.
   if (tid < kWave) {
     int tot = 0;
     for (int b0 = 0; b0 < bv.batch; b0 += kWave) {
@@ -330,7 +333,21 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
       const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) >> bv.page_shift : 0;
       tot += wave_sum(pg);
     }
-    const int cap = (tot + (p.grid - bv.batch) - 1) / (p.grid - bv.batch);
+    int cap = (tot + (p.grid - bv.batch) - 1) / (p.grid - bv.batch);
+    if (tot > 0) {
+      int lo = (tot + p.grid - 1) / p.grid;
+      while (lo < cap) {  // uniform over the wave: every bound comes from a wave sum
+        const int mid = (lo + cap) / 2;
+        int wgs = 0;
+        for (int b0 = 0; b0 < bv.batch; b0 += kWave) {
+          const int b = b0 + lane;
+          const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) >> bv.page_shift : 0;
+          wgs += wave_sum((pg + mid - 1) / mid);
+        }
+        if (wgs <= p.grid) cap = mid;
+        else lo = mid + 1;
+      }
+    }
     int acc = 0, found = 0;
     for (int b0 = 0; b0 < bv.batch && !found; b0 += kWave) {
       const int b = b0 + lane;

@@ -558,7 +558,11 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
               if (ph == 1 && pc >= 0) store(pc, scorer.head_sum(pacc));
               pc = -1;
               if (c < nsteps) {
+                // the SIMD prefers this wave's MFMA issue over its partner's
+                // VALU work while the products are queued
+                __builtin_amdgcn_s_setprio(1);
                 scorer.mma(tl, pacc);
+                __builtin_amdgcn_s_setprio(0);
                 pc = c;
               }
               if (ph == 0 && pc >= 0) store(pc, scorer.head_sum(pacc));

@@ -41,14 +41,12 @@ static_assert(kMaxDecodeQ <= 4 && kIdxWaves % 4 == 0, "wave groups per decode qu
 static_assert(kRadixBins % kIdxThreads == 0, "histogram bins split evenly over the threads");
 // bf16 keys with three or four query tokens: 64-key steps whose quarter tiles
 // a wave holds in registers (one being staged, kXchgRing - 1 in flight), and
-// the two 16-KiB LDS slots they are shared through (the same 32 KiB later
-// hold the per-query radix histograms of every several-query kernel)
+// the two 16-KiB LDS slots they are shared through
 constexpr int kXchgRing = 4;
 constexpr int kXchgSlotWords = 64 * 128 * 2 / 4;
-static_assert(2 * kXchgSlotWords >= kMaxDecodeQ * kRadixBins, "the exchange area holds one histogram per query");
 
 __host__ __device__ constexpr size_t xchg_offset_words(int maxq, int chunk_cap, int stage_pages) {
-  return ((size_t)maxq * chunk_cap + kRadixBins + stage_pages + 3) / 4 * 4;
+  return ((size_t)maxq * chunk_cap + (size_t)maxq * kRadixBins + stage_pages + 3) / 4 * 4;
 }
 
 // Workspace layout (uint32 words), see indexer_ws_words().
@@ -301,12 +299,12 @@ enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3 };
 template <int DT, int H, int D, int MAXQ>
 __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerDecodeParams p) {
   extern __shared__ __align__(16) uint32_t smem[];
-  // dynamic LDS: sc[MAXQ][cap] | lhist[2048] | s_bt[stage_pages] | xs (several
-  // queries, 32 KiB, 16-B aligned: while scoring bf16 keys, the two slots of
-  // the shared key steps; then one radix histogram per query)
+  // dynamic LDS: sc[MAXQ][cap] | qhist[MAXQ][2048] (one radix histogram per
+  // query) | s_bt[stage_pages] | xs (bf16 with several queries: the two 16-KiB
+  // slots of the shared key steps, 16-B aligned)
   uint32_t* sc = smem;
-  uint32_t* lhist = smem + (size_t)MAXQ * p.chunk_cap;
-  int* s_bt = (int*)(lhist + kRadixBins);
+  uint32_t* qhist = smem + (size_t)MAXQ * p.chunk_cap;
+  int* s_bt = (int*)(qhist + MAXQ * kRadixBins);
   u32x4* xs = (u32x4*)(smem + xchg_offset_words(MAXQ, p.chunk_cap, p.stage_pages));
   __shared__ int s_seqinfo[8];
   __shared__ int s_scan[kIdxThreads];
@@ -432,6 +430,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
   const bool staged = npg_loc <= p.stage_pages;
   if (!staged && tid == 0) atomic_add_agent(W.err(), 4u);  // host sizing guarantees staging
   for (int i = tid; i < npg_loc && staged; i += kIdxThreads) s_bt[i] = bt[pg0 + i];
+  // the first radix pass's histograms fill while the keys are scored
+  for (int i = tid; i < MAXQ * kRadixBins / 4; i += kIdxThreads) ((u32x4*)qhist)[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
   {
     MfmaScorer<DT, H, D> scorer;
@@ -466,6 +466,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
         const int phase = wave / QG, stride = kIdxWaves / QG;
         scorer.load_query(p, tok0 + q);
         uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+        uint32_t* hq = qhist + q * kRadixBins;
         Tile ring[RD];
 #pragma unroll
         for (int d = 0; d < RD - 1; d++) fetch(phase + d * stride, ring[d]);
@@ -478,7 +479,11 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
               fetch(tile + kAhead * stride, ring[(d + RD - 1) % RD]);
               const float v = scorer.score(p, 0, ring[d]);
               const int s = s0 + 32 * tile + lane;
-              if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
+              if (lane < 32 && s < s1) {
+                const uint32_t x = (s <= t) ? float_key(v) : 0u;
+                scq[s - s0] = x;
+                if (x) atomicAdd(&hq[x >> 21], 1u);
+              }
             }
           }
         }
@@ -522,9 +527,14 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
         const int rbase = 16 * n, rx = n & 15, rh = 8 * (lane >> 5);
         const int t = L - T + q;
         uint32_t* scq = sc + (size_t)q * p.chunk_cap;
+        uint32_t* hq = qhist + q * kRadixBins;
         auto store = [&](int c, float v) {
           const int s = s0 + 64 * c + 32 * ph + lane;
-          if (lane < 32 && s < s1) scq[s - s0] = (s <= t) ? float_key(v) : 0u;
+          if (lane < 32 && s < s1) {
+            const uint32_t x = (s <= t) ? float_key(v) : 0u;
+            scq[s - s0] = x;
+            if (x) atomicAdd(&hq[x >> 21], 1u);
+          }
         };
         f32x16 pacc[MfmaScorer<DT, H, D>::MT];
         int pc = -1;  // step whose products pacc holds, not yet summed
@@ -583,10 +593,9 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
 
   // ---- 3. radix passes ------------------------------------------------------
   // Every active query of the sequence goes through a pass together: one LDS
-  // histogram per query (the several-query kernels reuse the key-exchange
-  // area for them), one cross-workgroup barrier per pass, and the global bin
-  // loads of all queries in flight at once.
-  uint32_t* qhist = (MAXQ > 1) ? (uint32_t*)xs : lhist;
+  // histogram per query (pass 0's filled while the keys were scored), one
+  // cross-workgroup barrier per pass, and the global bin loads of all queries
+  // in flight at once.
   __shared__ int s_scanq[MAXQ][kIdxWaves];
   __shared__ int s_binq[MAXQ], s_aboveq[MAXQ], s_bincntq[MAXQ];
   int round = 0;
@@ -596,7 +605,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
     if (!act) break;
     const int shift = (pass == 0) ? 21 : (pass == 1) ? 10 : 0;
     const uint32_t dmask = (pass < 2) ? 0x7FFu : 0x3FFu;
-    for (int q = 0; q < T && q < MAXQ; q++) {
+    // pass 0's histograms were filled while scoring
+    for (int q = 0; q < T && q < MAXQ && pass > 0; q++) {
       if (s_state[q] != kActive) continue;
       for (int i = tid; i < kRadixBins / 4; i += kIdxThreads) ((u32x4*)(qhist + q * kRadixBins))[i] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -604,7 +614,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
     // each thread takes 8 consecutive keys per round (two 16-B LDS reads ahead
     // of their atomics; chunk_cap is a multiple of 8, so the reads stay inside
     // the buffer and keys past nloc are masked)
-    for (int q = 0; q < T && q < MAXQ; q++) {
+    for (int q = 0; q < T && q < MAXQ && pass > 0; q++) {
       if (s_state[q] != kActive) continue;
       const uint32_t pre = s_prefix[q], pm = s_pmask[q];
       const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
@@ -912,8 +922,7 @@ static hipError_t launch_one(const IndexerDecodeParams& p, size_t lds, hipStream
 int indexer_decode_max_q() { return kMaxDecodeQ; }
 
 size_t indexer_decode_lds_bytes(int dtype, int maxq, int chunk_cap, int stage_pages) {
-  (void)dtype;
-  const size_t xchg = (maxq > 1) ? 2 * kXchgSlotWords : 0;
+  const size_t xchg = (dtype == kBF16 && maxq == 4) ? 2 * kXchgSlotWords : 0;
   return (xchg_offset_words(maxq, chunk_cap, stage_pages) + xchg) * 4;
 }
 

@@ -314,7 +314,8 @@ def test_c5_decode4_full_size_sampled():
 def test_multi_token_decode_sub_batches():
     """Four query tokens for 32 sequences of about 56k tokens (bf16).  With all
     32 in one launch a workgroup would hold about 8000 keys x 4 queries of
-    scores plus the 32 KiB key-exchange area, more than the LDS; the decode
+    scores, four histograms and the 32 KiB key-exchange area, more than the
+    LDS; the decode
     planner then launches sub-batches of 16 sequences.  Sampled queries of
     both halves, the SFA on them, and every row's properties."""
     _say("multi-token sub-batches: generating on device")

@@ -315,9 +315,9 @@ def test_multi_token_decode_sub_batches():
     """Four query tokens for 32 sequences of about 56k tokens (bf16).  With all
     32 in one launch a workgroup would hold about 8000 keys x 4 queries of
     scores, four histograms and the 32 KiB key-exchange area, more than the
-    LDS; the decode
-    planner then launches sub-batches of 16 sequences.  Sampled queries of
-    both halves, the SFA on them, and every row's properties."""
+    LDS; the decode planner then launches sub-batches of 16 sequences.
+    Sampled queries of both halves, the SFA on them, and every row's
+    properties."""
     _say("multi-token sub-batches: generating on device")
     case = make_case("c5_decode4", 17, device="cuda", batch=32, seq_len_range=(54000, 57000))
     call = B.Call(case)

@@ -352,9 +352,13 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", value_seed: Optiona
     g, og = _gen(vseed, "k_i", dev), _gen(vseed, "out_k_i", dev)
     _fill_pool(k_pool, k_scale, lambda n: _randn((n, d_i), g, dev, 1.0, outl, og),
                n_keys, phys_t, idt, chunk)
-    # 5. head weights U(0,1)/w_div
+    # 5. head weights U(0,1)/w_div, or U(-1,1)/w_div with w_signed (the
+    # weights are projections of the hidden state and may take either sign)
     g = _gen(vseed, "w", dev)
-    w = (torch.rand((total_q, h_i), generator=g, device=dev) / p["w_div"]).float()
+    u = torch.rand((total_q, h_i), generator=g, device=dev)
+    if p.get("w_signed", False):
+        u = 2.0 * u - 1.0
+    w = (u / p["w_div"]).float()
     # 6. SFA q
     g, og = _gen(vseed, "q_s", dev), _gen(vseed, "out_q_s", dev)
     q_s = torch.empty((total_q, h_s, d_qk), dtype=storage_dtype(sdt), device=dev)

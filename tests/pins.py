@@ -227,3 +227,84 @@ def pin_tile_decode(decode, golden_path):
         want = (lib * spread).numpy()
         got = np.asarray(decode(b, "fp8_t128", s))
         assert np.array_equal(got, want), D
+
+
+# ------------------------------------------------ whole indexer per query ---
+
+def _torch_e4m3(raw_bytes):
+    """e4m3 bytes -> float64 through torch's float8_e4m3fn cast (a library route)."""
+    t = torch.as_tensor(np.ascontiguousarray(raw_bytes, np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_e8m0(raw_byte):
+    """One e8m0 scale byte -> float through torch's float8_e8m0fnu cast."""
+    t = torch.tensor([int(raw_byte)], dtype=torch.uint8)
+    return float(t.view(torch.float8_e8m0fnu).to(torch.float64)[0])
+
+
+def _host(x):
+    t = x.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.to(torch.float64).numpy()
+    return t.numpy()
+
+
+def loop_indexer_query(case, b, i):
+    """The indexer for one query by explicit loops: every key position s <= t
+    is looked up in the block table one at a time, its bytes and scale(s) are
+    decoded with torch's FP8 / E8M0 casts, the query's scales are taken from
+    its own token's row, and the scores come from the pure-Python triple loop.
+    Returns (t, scores, kept positions, n-th largest score)."""
+    P = case.page_size
+    L, T = int(case.seq_lens_host[b]), int(case.q_lens_host[b])
+    t = L - T + i
+    tok = int(case.q_lens_host[:b].sum()) + i
+    dt = case.idx_dtype
+    bt = _host(case.block_table)[b]
+    kpool = case.k_pool.detach().cpu()
+    qraw = case.q_i.detach().cpu()[tok]
+    H, D = qraw.shape
+    if dt in ("fp8", "mxfp8"):
+        q = _torch_e4m3(qraw.numpy())
+        qs = _host(case.q_i_scale)[tok]
+        for h in range(H):
+            for d in range(D):
+                q[h, d] *= float(qs[h]) if dt == "fp8" else _torch_e8m0(qs[h, d // 32])
+    else:
+        q = _host(qraw).astype(np.float64)
+    keys = []
+    for s in range(t + 1):
+        page, off = int(bt[s // P]), s % P
+        row = kpool[page, off]
+        if dt in ("fp8", "mxfp8"):
+            k = _torch_e4m3(row.numpy())
+            sc = case.k_scale.detach().cpu()[page, off].numpy()
+            for d in range(D):
+                k[d] *= float(sc) if dt == "fp8" else _torch_e8m0(sc[d // 32])
+        else:
+            k = _host(row).astype(np.float64)
+        keys.append(k.tolist())
+    w = _host(case.w)[tok].astype(np.float64)
+    scores = brute_scores(q.tolist(), w.tolist(), keys)
+    keep = brute_topk(list(scores), case.topk)
+    kth = min(scores[p] for p in keep)        # the n-th largest: the smallest kept score
+    return t, scores, keep, kth
+
+
+def pin_indexer_query(fn, cases):
+    """fn(case, b, i) -> (t, scores, idx, kth) against the loop route above,
+    for every query of every case."""
+    for case in cases:
+        for b in range(case.batch):
+            for i in range(int(case.q_lens_host[b])):
+                t, scores, idx, kth = fn(case, b, i)
+                rt, rscores, rkeep, rkth = loop_indexer_query(case, b, i)
+                assert t == rt, (t, rt)
+                assert np.allclose(scores, rscores, rtol=1e-12, atol=1e-12), (case.name, b, i)
+                assert list(np.asarray(idx).tolist()) == rkeep, (case.name, b, i)
+                # kth is the n-th largest of fn's own scores (exactly: the
+                # smallest kept one), and the loop route's up to rounding
+                sc = np.asarray(scores)
+                assert kth == sc[np.asarray(idx)].min(), (case.name, b, i, kth)
+                assert np.isclose(kth, rkth, rtol=1e-12, atol=1e-12), (case.name, b, i, kth, rkth)

@@ -339,3 +339,62 @@ def test_pins_catch_planted_mistakes(pin, mutant):
 def test_codec_pin_catches_wrong_bias():
     with pytest.raises(AssertionError):
         pins.pin_e4m3_table(_mutant_e4m3_bias())
+
+
+# ------------------------------------------- quantised indexer per query ---
+
+def _small_quant_cases():
+    """Small FP8 and MXFP8 indexer cases (and a bf16 one): ragged contexts over
+    16-token pages in a permuted pool, 1 % outliers at +-20 before quantising,
+    signed head weights, several query tokens per sequence (so a wrong token's
+    scale row is a different row)."""
+    kw = dict(batch=2, seq_len_range=(40, 75), q_len=2, page_size=16, h_i=3, d_i=64, topk=16,
+              h_s=2, d_qk=16, d_v=8, scale_dim=16, w_signed=True)
+    return [make_case("c4_decode_fp8", 21, **kw), make_case("c4_decode_mxfp8", 22, **kw),
+            make_case("c2_decode_bf16", 23, **kw)]
+
+
+def test_indexer_query_quantised_against_loop_route():
+    """oracle.indexer_query (scores, Top-K and the n-th largest score) on FP8,
+    MXFP8 and bf16 cases against explicit per-position block-table lookups,
+    torch's float8_e4m3fn / float8_e8m0fnu casts and the pure-Python score
+    loop ([P2] sec. 4.2: MXFP8 with 32-element groups; [P1] sec. 3)."""
+    pins.pin_indexer_query(oracle.indexer_query, _small_quant_cases())
+
+
+def _mutant_query(scale_unpaged=False, q_scale_token=0, kth_shift=0):
+    """Copies of oracle.indexer_query with one planted mistake."""
+    od = oracle.dsa_oracle
+
+    def fn(case, b, i):
+        P = case.page_size
+        L, T = int(case.seq_lens_host[b]), int(case.q_lens_host[b])
+        t = od.query_position(L, T, i)
+        tok = case.token(b, i)
+        bt = od._np(case.block_table[b])
+        pos = np.arange(t + 1)
+        qs_tok = min(tok + q_scale_token, case.total_q - 1)
+        q = od.decode_values(od._np(case.q_i[tok]), case.idx_dtype,
+                             None if case.q_i_scale is None else od._np(case.q_i_scale[qs_tok]))
+        k_raw = od.paged_rows(od._np(case.k_pool), bt, P, pos)
+        if case.k_scale is None:
+            k_sc = None
+        elif scale_unpaged:       # logical position used as a pool row
+            flat = od._np(case.k_scale).reshape(-1, *case.k_scale.shape[2:])
+            k_sc = flat[pos]
+        else:
+            k_sc = od.paged_rows(od._np(case.k_scale), bt, P, pos)
+        keys = od.decode_values(k_raw, case.idx_dtype, k_sc)
+        scores = od.indexer_scores(q, od._np(case.w[tok]).astype(np.float64), keys)
+        idx = od.topk_select(scores, case.topk)
+        kth = np.sort(scores)[::-1][len(idx) - 1 + kth_shift]
+        return t, scores, idx, kth
+    return fn
+
+
+@pytest.mark.parametrize("mutant", [_mutant_query(scale_unpaged=True), _mutant_query(q_scale_token=1),
+                                    _mutant_query(kth_shift=1)],
+                         ids=["unpaged-key-scale", "next-token-q-scale", "kth-off-by-one"])
+def test_indexer_query_pin_catches_planted_mistakes(mutant):
+    with pytest.raises(AssertionError):
+        pins.pin_indexer_query(mutant, _small_quant_cases())

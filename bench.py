@@ -4,11 +4,11 @@
 A step is one call of dsa_fused_decode: the fused Lightning Indexer (per-head
 scores from the paged bf16 K cache, head-weighted sum, causal mask, Top-K) and
 Sparse Flash Attention over the selected latent rows, for a batch of 32
-sequences with contexts drawn uniformly from [4096, 32768] (one new token each),
-indexer 64 heads x 128, k = 2048, SFA 128 heads over 512 + 64 latent columns.
-Inputs are synthetic, seeded and resident in HBM; several value sets with the
-same layout are rotated so that the ~236 MB step does not sit in the 256 MB
-last-level cache between steps.
+sequences whose contexts are all 32768 tokens (one new token each), indexer 64
+heads x 128, k = 2048, SFA 128 heads over 512 + 64 latent columns.  Inputs are
+synthetic, seeded and resident in HBM; several value sets with the same layout
+are rotated so that the ~354 MB step does not sit in the 256 MB last-level
+cache between steps.
 
 Prints one JSON line (see the fields below).
 """
@@ -148,8 +148,8 @@ def prefill_line(torch, B, make_case, steps):
 def config_line(torch, B, make_case, name, steps, warmup, sets):
     """One more workload of the scope table: fused-call time and its rate
     against the roof that bounds it (HBM for decode, MFMA for prefill)."""
-    cases = [make_case(name, 5 if name.startswith("c5") else 4, device="cuda", value_seed=r + 1)
-             for r in range(sets)]
+    seed = 5 if name.startswith("c5") else 2 if name.startswith("c2") else 4
+    cases = [make_case(name, seed, device="cuda", value_seed=r + 1) for r in range(sets)]
     calls = [B.Call(c) for c in cases]
     prefill = cases[0].max_q_len > 4
     op = B.DSA_OP_FUSED_PREFILL if prefill else B.DSA_OP_FUSED_DECODE
@@ -173,6 +173,7 @@ def config_line(torch, B, make_case, name, steps, warmup, sets):
 
 
 CONFIGS_EXTRA = {
+    "c2_decode_bf16": "decode, 32 sequences, contexts U[4096, 32768], bf16",
     "c4_decode_fp8": "decode, 64 sequences, contexts U[16384, 65536], FP8 indexer, 1 % outliers",
     "c4_decode_mxfp8": "decode, 64 sequences, contexts U[16384, 65536], MXFP8 indexer, 1 % outliers",
     "c5_chunk_prefill": "chunked prefill, 8 sequences, 8192 new tokens after 122880 cached",
@@ -187,11 +188,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2_decode_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c2_decode_bf16_32k", choices=sorted(WORKLOADS))
     ap.add_argument("--sets", type=int, default=4, help="value sets rotated between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
-    ap.add_argument("--no-ctx32k", dest="ctx32k", action="store_false",
-                    help="skip the extra all-32k-context measurement")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false",
                     help="skip the 32k causal prefill measurement")
     ap.add_argument("--no-extra", dest="extra", action="store_false",
@@ -286,20 +285,10 @@ def main():
             "sfa": a["sfa_flops"] / (ms_sfa * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[case.sfa_dtype],
         },
     }
-    if args.workload == "c2_decode_bf16" and args.ctx32k:
-        # the same step with every context at 32768 tokens ("at 32k ctx")
-        c32 = [B.Call(make_case("c2_decode_bf16_32k", seed, device="cuda", value_seed=seed + 100 * r))
-               for r in range(args.sets)]
-        for c in c32:
-            c.workspace(B.DSA_OP_FUSED_DECODE)
-        ms32 = time_calls(lambda s: c32[s % len(c32)].fused_decode(), args.steps, args.warmup, torch)
-        a32 = algorithmic(c32[0].case)
-        line["ctx32k"] = {"us_per_step": ms32 * 1e3, "tokens_per_s": c32[0].case.total_q / (ms32 * 1e-3),
-                          "step_hbm_frac": a32["fused_bytes"] / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del c32
-    if args.workload == "c2_decode_bf16" and args.prefill:
+    headline = args.workload == "c2_decode_bf16_32k"
+    if headline and args.prefill:
         line["prefill_32k"] = prefill_line(torch, B, make_case, 3)
-    if args.workload == "c2_decode_bf16" and args.extra:
+    if headline and args.extra:
         line["other_configs"] = {
             n: config_line(torch, B, make_case, n, *((3, 1, 1) if n == "c5_chunk_prefill" else (50, 5, 2)))
             for n in CONFIGS_EXTRA}

@@ -391,12 +391,16 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
           cnd = x > thr;
           m = __ballot(cnd);
         }
+        // count + 64 <= kCap always holds here (see indexer_prefill_max_topk);
+        // the bound below only keeps a broken invariant inside the buffer
         if (cnd) {
           const int r = count + lane_rank(m);
-          ckey[r] = x;
-          cpos[r] = (uint32_t)spos;
+          if (r < kCap) {
+            ckey[r] = x;
+            cpos[r] = (uint32_t)spos;
+          }
         }
-        count += __popcll(m);
+        count = min(count + __popcll(m), kCap);
       }
       if (have_q && !all_keep) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -416,7 +420,12 @@ size_t indexer_prefill_lds_bytes() {
 }
 
 int indexer_prefill_max_pages() { return kMaxPages; }
-int indexer_prefill_max_topk() { return kCap - 64; }
+// A mid-query select may keep up to k + kSelSlack candidates, and the next
+// tile appends at most kKT more before the buffer is checked again, so the
+// buffer holds k + kSelSlack + kKT entries at most: k <= kCap - kSelSlack - kKT.
+constexpr int kMaxTopk = kCap - kSelSlack - kKT;
+static_assert(kMaxTopk == 2752, "prefill Top-K bound");
+int indexer_prefill_max_topk() { return kMaxTopk; }
 
 int indexer_prefill_grid(int total_q, int batch) {
   const int blocks = (total_q + kQBlock - 1) / kQBlock + batch;   // >= sum of ceil(T_b/64)

@@ -497,13 +497,15 @@ __global__ __launch_bounds__(64 * NWV, 1) void sfa_bf16_kernel(SfaParams p) {
 
     // ---- softmax weights for heads l%16 (+16 ht); this lane holds rows
     // 4*grp + i and 16 + 4*grp + i (i < 4) of each head group.
-    // Fixed reference: the first tile with a selected row sets m_ref to its
-    // maximum plus kSfaRefMargin (log2 units) and it never moves afterwards,
-    // so the accumulators are never rescaled.  Weights 2^(z - m_ref) stay in
-    // the normal fp32/bf16 range while a later logit exceeds that first maximum
-    // by less than ~150 (overflow there shows up as a non-finite output); terms
-    // more than ~80 below it are flushed and negligible next to the first
-    // maximum's own weight.  The normalised result does not depend on m_ref.
+    // Reference m_ref: the first tile with a selected row sets it to its
+    // maximum plus kSfaRefMargin (log2 units), so weights 2^(z - m_ref) are at
+    // most 2^-40 and the usual case never rescales.  A later tile whose
+    // maximum passes m_ref (a logit more than kSfaRefMargin above the first
+    // maximum) moves m_ref to that maximum plus the margin and rescales the
+    // accumulators by 2^(old - new) first, so no weight ever exceeds 1 and the
+    // sums stay finite whatever the order of the index rows.  Terms more than
+    // ~86 below the reference's maximum are flushed, negligible next to its own
+    // weight.  The normalised result does not depend on m_ref.
     bf16x8 phi[HG], plo[HG];
     float pwv[KV8 ? HG : 1][8];   // FP8: the fp32 weights, scaled per V tile below
 #pragma unroll
@@ -517,10 +519,19 @@ __global__ __launch_bounds__(64 * NWV, 1) void sfa_bf16_kernel(SfaParams p) {
         z[e] = ((valid >> r) & 1u) ? v * p.scale_log2 : -INFINITY;
         mt = fmaxf(mt, z[e]);
       }
+      // the head's maximum over the tile (its rows sit in the four lane groups)
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
       if (m_run[ht] == -INFINITY) {
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
         m_run[ht] = mt + kSfaRefMargin;     // still -inf if no row of the tile is selected
+      } else if (mt > m_run[ht]) {
+        // rare: move the reference up and rescale what was accumulated
+        const float m_new = mt + kSfaRefMargin;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[ht] - m_new);
+        l_run[ht] *= alpha;
+#pragma unroll
+        for (int mv = 0; mv < MV; mv++) o[ht][mv] *= alpha;
+        m_run[ht] = m_new;
       }
       const bool none = (m_run[ht] == -INFINITY);
       float psum = 0.f;

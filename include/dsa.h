@@ -23,6 +23,12 @@
  *     memory comes from the caller's workspace `ws` of `ws_bytes` bytes, sized
  *     with dsa_workspace_size().  One workspace must not be used by two calls
  *     that may run concurrently.
+ *   Workspace state: a workspace must be zero-filled before its first use
+ *     (hipMemsetAsync, or allocate it zeroed).  Every call that is enqueued
+ *     leaves the parts it relies on zero again when its kernels finish, so the
+ *     same workspace serves any later call of any shape without being cleared
+ *     (the decode indexer keeps its cross-workgroup counters and histograms
+ *     there and clears them itself, which saves a fill launch per call).
  *   Alignment: the workspace and the q, k_cache / kv_cache data and output
  *     arrays are 16-byte aligned (the kernels move them 16 bytes at a time);
  *     scale pools, head weights, lse, index rows, lengths and block tables
@@ -35,6 +41,13 @@
  *     the last failure.  Contents of device arrays (block-table entries, lengths)
  *     are preconditions: block_table entries < num_pages, seq_lens[b] <=
  *     max_pages_per_seq * page_size, 0 <= q_lens <= seq_lens, values finite.
+ *     The decode indexer's workgroups wait for each other with bounded waits
+ *     (its grid is sized to be resident as a whole; other work sharing the
+ *     device can keep part of it waiting).  If a
+ *     wait ever gives up, the affected queries' index rows are overwritten
+ *     with -1 (slot 0 included, which no valid row has), and a sticky error
+ *     bit is set in the workspace; with DSA_DEBUG=1 in the environment each
+ *     call synchronises after the indexer and returns DSA_ERR_HIP for it.
  *   Positions: sequence b has L_b = seq_lens[b] keys in the caches; its
  *     T_b = cu_q[b+1] - cu_q[b] query tokens are the LAST T_b positions, query
  *     i sitting at t = L_b - T_b + i.  Key position s of sequence b lives in

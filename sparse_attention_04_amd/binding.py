@@ -164,10 +164,16 @@ class Call:
         self._ws = {}
 
     def workspace(self, op):
+        """The call's workspace: zero-filled when allocated, as the ABI asks of
+        a workspace before its first use (calls leave it ready for the next)."""
         n = dsa_workspace_size(op, self.batch, self.iargs, self.sargs)
         if op not in self._ws or self._ws[op].numel() < n:
-            self._ws[op] = torch.empty(max(n, 1), dtype=torch.uint8, device=self.case.q_s.device)
+            self._ws[op] = torch.zeros(max(n, 1), dtype=torch.uint8, device=self.case.q_s.device)
         return self._ws[op], n
+
+    def use_workspace(self, op, ws):
+        """Run `op` with a caller-supplied (zero-filled before first use) workspace."""
+        self._ws[op] = ws
 
     def indexer_topk(self, stream=None):
         ws, n = self.workspace(DSA_OP_INDEXER_TOPK)

@@ -64,6 +64,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+__device__ __forceinline__ void store_agent_i32(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Barrier among the `count` workgroups sharing `ctr` (all co-resident).  The
 // round-th call returns once count*round arrivals are seen.
 //
@@ -73,9 +77,11 @@ __device__ __forceinline__ void lds_barrier() {
 // wave waits for its own outstanding memory operations to complete before the
 // workgroup arrives, and readers issue their loads after observing the count.
 // No cache write-back or invalidation is needed, which keeps a barrier round to
-// a few microseconds.  The wait is bounded: on timeout an error bit is set and
-// the workgroup continues, so the grid always drains.
-__device__ __forceinline__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+// a few microseconds.  The wait is bounded by `spin_limit` sleeps: on timeout
+// the error bit is set in `err`, the sequence's `failed` flag is raised and the
+// workgroup continues, so the grid always drains.
+__device__ __forceinline__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t* err, uint32_t* failed,
+                                              uint32_t spin_limit) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -83,8 +89,9 @@ __device__ __forceinline__ void group_barrier(uint32_t* ctr, uint32_t target, ui
     uint32_t spins = 0;
     while (load_relaxed_agent(ctr) < target) {
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
+      if (++spins > spin_limit) {
         atomic_add_agent(err, kErrBarrierTimeout);
+        atomic_add_agent(failed, 1u);
         break;
       }
     }

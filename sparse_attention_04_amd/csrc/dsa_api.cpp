@@ -11,6 +11,7 @@
 #include <cstring>
 #include <string>
 
+#include "api_internal.h"
 #include "kernels.h"
 
 using namespace dsa;
@@ -199,6 +200,14 @@ bool debug_mode() {
   return s && s[0] == '1';
 }
 
+// DSA_TEST_FORCE_TIMEOUT=1 (tests only): every cross-workgroup wait of the
+// decode indexer gives up after a few sleeps, as a failed co-residency would
+// make it, so the failure path can be checked while every kernel still ends.
+bool force_timeout_mode() {
+  const char* s = getenv("DSA_TEST_FORCE_TIMEOUT");
+  return s && s[0] == '1';
+}
+
 // DSA_PROFILE=1: kernels record per-phase clock sums of their first workgroup
 // in the last kProfileBytes of the workspace.
 constexpr size_t kProfileBytes = 256;
@@ -223,9 +232,7 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
   const int maxp = (b->max_seq_len + P - 1) / P;
   const int dt = dt_kernel(a->q_dtype);
 
-  hipError_t e = launch_zero(ws, indexer_ws_zero_bytes(b->batch, b->total_q) / 4, st);
-  if (e != hipSuccess) return hip_fail(e, "zero-fill launch");
-
+  hipError_t e = hipSuccess;
   // Pick the largest co-resident grid (2 or 1 workgroups per CU) and the
   // largest sub-batch whose per-workgroup score buffer fits in LDS.
   int grid = 0, chunk_cap = 0, sub = 0, stage = 0;
@@ -269,6 +276,13 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
   p.grid = grid;
   p.chunk_cap = chunk_cap;
   p.stage_pages = stage;
+  p.spin_limit = kSpinLimit;
+  p.barrier_slack = 0;
+  if (force_timeout_mode()) {
+    // test hook: no barrier can complete, and every wait gives up quickly
+    p.spin_limit = 64;
+    p.barrier_slack = 1u << 30;
+  }
   for (int b0 = 0; b0 < b->batch; b0 += sub) {
     const int nb = std::min(sub, b->batch - b0);
     p.bv = view_of(b, P);
@@ -286,7 +300,12 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
     uint32_t flags = 0;
     e = hipMemcpy(&flags, ws, 4, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "indexer (debug flags)");
-    if (flags) return fail(DSA_ERR_HIP, "indexer reported error bits 0x%x (bounded wait expired or LDS bound)", flags);
+    if (flags) {
+      const uint32_t zero = 0;
+      e = hipMemcpy(ws, &zero, 4, hipMemcpyHostToDevice);   // report each failure once
+      if (e != hipSuccess) return hip_fail(e, "indexer (debug flags reset)");
+      return fail(DSA_ERR_HIP, "indexer reported error bits 0x%x (bounded wait expired or LDS bound)", flags);
+    }
   }
   return DSA_OK;
 }
@@ -430,6 +449,16 @@ dsa_status dsa_fused_decode(const dsa_batch* b, const dsa_indexer_args* ia, cons
                             void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                             void* stream) {
   g_err.clear();
+  return dsa::fused_decode_impl(b, ia, sa, out, lse, idx_out, ws, ws_bytes, stream, false);
+}
+
+}  // extern "C"
+
+namespace dsa {
+
+dsa_status fused_decode_impl(const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa,
+                             void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                             void* stream, bool validate_only) {
   dsa_status s = check_batch(b);
   if (s == DSA_OK) s = check_indexer(b, ia);
   if (s == DSA_OK) s = check_sfa(b, sa);
@@ -439,6 +468,7 @@ dsa_status dsa_fused_decode(const dsa_batch* b, const dsa_indexer_args* ia, cons
     return fail(DSA_ERR_INVALID_ARG, "out and ws must be 16-byte, lse and idx_out 4-byte aligned");
   if (ia->k_cache->page_size != sa->kv_cache->page_size)
     return fail(DSA_ERR_INVALID_ARG, "k_cache and kv_cache must share the page size (one block table)");
+  if (validate_only) return DSA_OK;
   const size_t need = dsa_workspace_size(DSA_OP_FUSED_DECODE, b, ia, sa);
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
   unsigned char* w = (unsigned char*)ws;
@@ -449,6 +479,13 @@ dsa_status dsa_fused_decode(const dsa_batch* b, const dsa_indexer_args* ia, cons
   if (s != DSA_OK) return s;
   return run_sfa(b, sa, idx, ia->topk, out, lse, w + ib + align_up((size_t)b->total_q * ia->topk * 4, 256), st);
 }
+
+dsa_status set_error(dsa_status st, const char* msg) { return fail(st, "%s", msg); }
+void clear_error() { g_err.clear(); }
+
+}  // namespace dsa
+
+extern "C" {
 
 dsa_status dsa_fused_prefill(const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa,
                              int32_t q_block, void* out, float* lse, int32_t* idx_out, void* ws,

@@ -49,16 +49,22 @@ __host__ __device__ constexpr size_t xchg_offset_words(int maxq, int chunk_cap, 
   return ((size_t)maxq * chunk_cap + (size_t)maxq * kRadixBins + stage_pages + 3) / 4 * 4;
 }
 
-// Workspace layout (uint32 words), see indexer_ws_words().
-//   [0, 64)                        header: error bits
-//   [64, 64 + 32*B)                per sequence: barrier counter (own 128-B line)
-//   zeroed region ends here + per query {hist0[2048], outcnt (+31 pad)}
+// Workspace layout (uint32 words).  The whole region is zero when a call
+// starts and the call leaves it zero: the last workgroup of each sequence to
+// finish clears what the sequence's workgroups used (see the end of the
+// kernel), so no fill is needed between calls, whatever the batch shape.
+//   [0, 64)                        header: error bits (sticky), profiling stamps
+//   [64, 64 + 32*B)                per sequence, one 128-B line: barrier counter,
+//                                  exit counter, failure flag
+//   then per query {hist0[2048], outcnt (+31 pad)}
 //   then per query {hist1[2048], hist2[2048], tie[grid_pad]}
 struct WsLayout {
   uint32_t* base;
   int32_t nseq, nq, grid_pad;
   __host__ __device__ uint32_t* err() const { return base; }
   __host__ __device__ uint32_t* seq_ctr(int b) const { return base + 64 + 32 * b; }
+  __host__ __device__ uint32_t* seq_exit(int b) const { return seq_ctr(b) + 1; }
+  __host__ __device__ uint32_t* seq_failed(int b) const { return seq_ctr(b) + 2; }
   __host__ __device__ uint32_t* qa(int g) const { return base + 64 + 32 * nseq + (size_t)g * 2080; }
   __host__ __device__ uint32_t* hist(int g, int pass) const {
     if (pass == 0) return qa(g);
@@ -68,34 +74,14 @@ struct WsLayout {
   __host__ __device__ uint32_t* tie(int g) const {
     return base + 64 + 32 * nseq + (size_t)nq * 2080 + (size_t)g * (4096 + grid_pad) + 4096;
   }
-  __host__ __device__ size_t zero_words() const { return 64 + 32 * (size_t)nseq + (size_t)nq * 2080; }
   __host__ __device__ size_t total_words() const {
-    return zero_words() + (size_t)nq * (4096 + grid_pad);
+    return 64 + 32 * (size_t)nseq + (size_t)nq * 2080 + (size_t)nq * (4096 + grid_pad);
   }
 };
 
 size_t indexer_ws_bytes(int nseq, int nq, int grid) {
   WsLayout L{nullptr, nseq, nq, (grid + 31) / 32 * 32};
   return L.total_words() * 4;
-}
-
-size_t indexer_ws_zero_bytes(int nseq, int nq) {
-  WsLayout L{nullptr, nseq, nq, 0};
-  return L.zero_words() * 4;
-}
-
-__global__ void zero_words_kernel(uint32_t* p, size_t n) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (; i < n; i += stride) p[i] = 0u;
-}
-
-hipError_t launch_zero(uint32_t* p, size_t nwords, hipStream_t st) {
-  if (nwords == 0) return hipSuccess;
-  int blocks = (int)((nwords + 255) / 256);
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, st, p, nwords);
-  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------- scoring ---
@@ -393,6 +379,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
   const int* bt = bv.block_table + (size_t)b * bv.max_pages;
   const int K = p.topk;
   uint32_t* ctr = W.seq_ctr(p.seq_base + b);
+  uint32_t* failed = W.seq_failed(p.seq_base + b);
 
   if (tid < MAXQ) {
     s_prefix[tid] = 0u;
@@ -637,14 +624,10 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
         const uint32_t c = qhist[q * kRadixBins + i];
         if (c) atomic_add_agent(&gh[i], c);
       }
-      if (j == 0 && pass + 1 < kMaxPasses) {
-        uint32_t* nh = W.hist(tok0 + q, pass + 1);
-        for (int i = tid; i < kRadixBins; i += kIdxThreads) store_relaxed_agent(&nh[i], 0u);
-      }
     }
     DSA_STAMP(3 + 3 * pass);
     round++;
-    group_barrier(ctr, (uint32_t)(nb * round), W.err());
+    group_barrier(ctr, (uint32_t)(nb * round) + p.barrier_slack, W.err(), failed, p.spin_limit);
     DSA_STAMP(4 + 3 * pass);
     // each thread owns kBinsPerThread consecutive bins of every query; suffix
     // sums from the top bin down
@@ -718,6 +701,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
   }
   DSA_STAMP(12);
 
+  __shared__ int s_failed;
+  __shared__ uint32_t s_ticket;
   // ---- 3b. equal keys straddle the boundary: smallest positions win ---------
   bool any_tie = false;
   for (int q = 0; q < MAXQ; q++) any_tie |= (s_state[q] == kTiePass);
@@ -739,7 +724,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
       __syncthreads();
     }
     round++;
-    group_barrier(ctr, (uint32_t)(nb * round), W.err());
+    group_barrier(ctr, (uint32_t)(nb * round) + p.barrier_slack, W.err(), failed, p.spin_limit);
     for (int q = 0; q < T && q < MAXQ; q++) {
       if (s_state[q] != kTiePass) continue;
       if (tid == 0) {
@@ -789,16 +774,34 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
       for (int q = 0; q < MAXQ; q++) s_wcnt[q][wave] = cnt[q];
     }
     __syncthreads();
-    if (tid < MAXQ) {
-      int tot = 0;
+    // One thread reserves the workgroup's slots of every query and reads the
+    // sequence's failure flag; without a tie pass these are its last accesses
+    // to shared workspace state, so it then takes the exit ticket (ordered
+    // after the reservations), whose latency overlaps the row writes below.
+    if (tid == 0) {
+      uint32_t got[MAXQ];
 #pragma unroll
-      for (int w = 0; w < kIdxWaves; w++) tot += s_wcnt[tid][w];
-      s_wgbase[tid] = tot ? (int)atomic_add_agent(W.outcnt(tok0 + tid), (uint32_t)tot) : 0;
+      for (int q = 0; q < MAXQ; q++) {
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < kIdxWaves; w++) tot += s_wcnt[q][w];
+        got[q] = tot ? atomic_add_agent(W.outcnt(tok0 + q), (uint32_t)tot) : 0u;
+      }
+      const uint32_t fl = load_relaxed_agent(failed);
+#pragma unroll
+      for (int q = 0; q < MAXQ; q++) s_wgbase[q] = (int)got[q];
+      s_failed = fl != 0u;
+      if (!any_tie) {
+        __builtin_amdgcn_s_waitcnt(0);
+        s_ticket = atomic_add_agent(W.seq_exit(p.seq_base + b), 1u);
+      }
     }
     __syncthreads();
+    // a failed sequence writes no rows: its last workgroup out poisons them
+    const bool write_rows = !s_failed;
 #pragma unroll
     for (int q = 0; q < MAXQ; q++) {
-      if (!tb[q]) continue;
+      if (!tb[q] || !write_rows) continue;
       const uint32_t pre = s_prefix[q], pm = s_pmask[q];
       const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
       int32_t* row = p.idx_out + (size_t)(tok0 + q) * K;
@@ -845,7 +848,10 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
       mine += tot_sel;
       ties_seen += tot_tie;
     }
-    if (tid == 0) s_base = (int)atomic_add_agent(oc, (uint32_t)mine);
+    if (tid == 0) {
+      s_base = (int)atomic_add_agent(oc, (uint32_t)mine);
+      s_failed = load_relaxed_agent(failed) != 0u;
+    }
     __syncthreads();
     int base = s_base;
     ties_seen = 0;
@@ -859,13 +865,53 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
       const bool sel = above || (tie && ties_seen + r < take);
       int tot_sel;
       const int rs = block_rank(sel, s_rank, tot_sel);
-      if (sel && base + rs < K) row[base + rs] = s0 + i;
+      if (sel && base + rs < K && !s_failed) row[base + rs] = s0 + i;
       base += tot_sel;
       ties_seen += tot_tie;
     }
     __syncthreads();
   }
   DSA_STAMP(14);
+
+  // ---- 5. the sequence's last workgroup out ---------------------------------
+  // A workgroup takes its exit ticket after its last access to the shared
+  // workspace state (its histogram atomics, tie counts and slot reservations
+  // are performed by then), so the one that draws the last ticket sees the
+  // sequence's use of the workspace finished.  If any of the sequence's
+  // bounded waits gave up, the workgroups that saw the failure flag wrote no
+  // rows and this one overwrites the scored queries' rows with -1 (a visible
+  // failure: no valid row has -1 in slot 0).  It then clears everything the
+  // sequence used in the workspace; plain stores suffice, as the next launch
+  // sees them.
+  {
+    __shared__ int s_last;
+    if (any_tie) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) s_ticket = atomic_add_agent(W.seq_exit(p.seq_base + b), 1u);
+    }
+    __syncthreads();
+    if (tid == 0) s_last = (s_ticket == (uint32_t)(nb - 1));
+    __syncthreads();
+    if (s_last) {
+      const bool poison = load_relaxed_agent(failed) != 0u;
+      for (int q = 0; q < T && q < MAXQ; q++) {
+        if (L - T + q + 1 <= K) continue;        // kept every position: no scores, no workspace
+        const int g = tok0 + q;
+        if (poison) {
+          int32_t* row = p.idx_out + (size_t)g * K;
+          for (int s = tid; s < K; s += kIdxThreads) row[s] = -1;
+        }
+        u32x4* h0 = (u32x4*)W.qa(g);              // hist0, outcnt and its pad
+        for (int i = tid; i < 2080 / 4; i += kIdxThreads) h0[i] = u32x4{0u, 0u, 0u, 0u};
+        u32x4* h12 = (u32x4*)W.hist(g, 1);        // hist1, hist2
+        for (int i = tid; i < 4096 / 4; i += kIdxThreads) h12[i] = u32x4{0u, 0u, 0u, 0u};
+        uint32_t* tw = W.tie(g);
+        for (int i = tid; i < nb; i += kIdxThreads) tw[i] = 0u;
+      }
+      if (tid < 3) W.seq_ctr(p.seq_base + b)[tid] = 0u;   // barrier, exit, failure
+    }
+  }
 }
 
 // ------------------------------------------------------- f32 (small shapes) ---
@@ -906,10 +952,15 @@ struct MfmaScorer<kF32, H, D> {
 
 // ------------------------------------------------------------------ launch ---
 
-// The grid never exceeds what the device holds at once (the host sizes it from
-// the occupancy query), and kernels on one stream run one after another, so
-// every workgroup of a sequence is resident while its peers wait at a barrier.
-// A plain launch therefore suffices; the bounded waits remain the safety net.
+// The workgroups of a sequence wait for each other, so the whole grid must be
+// resident at once.  The host sizes the grid from the occupancy query (at most
+// what the device holds at once), and kernels on one stream run one after
+// another, so a plain launch is resident as a whole unless other work shares
+// the device; then the bounded waits give up, the affected rows are poisoned
+// and the error bit is set (see the end of the kernel).  A cooperative launch
+// would have the runtime guarantee residency, but it measured about 11 us of
+// idle device time before and after each launch on this part (74 us kernel,
+// 22 us of gaps per call).
 template <int DT, int H, int D, int MAXQ>
 static hipError_t launch_one(const IndexerDecodeParams& p, size_t lds, hipStream_t st) {
   auto kern = indexer_decode_kernel<DT, H, D, MAXQ>;

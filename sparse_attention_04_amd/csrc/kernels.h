@@ -32,15 +32,15 @@ struct IndexerDecodeParams {
   int32_t grid;            // workgroups launched
   int32_t chunk_cap;       // LDS score slots per query (keys)
   int32_t stage_pages;     // LDS slots for the workgroup's block-table slice
+  uint32_t spin_limit;     // sleeps before a cross-workgroup wait gives up
+  uint32_t barrier_slack;  // added to every barrier target (0; a test sets it to force timeouts)
 };
 
 size_t indexer_ws_bytes(int nseq, int nq, int grid);
-size_t indexer_ws_zero_bytes(int nseq, int nq);
 size_t indexer_decode_lds_bytes(int dtype, int maxq, int chunk_cap, int stage_pages);
 hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t lds, int* blocks_per_cu);
 hipError_t launch_indexer_decode(int dtype, int H, int D, int maxq, const IndexerDecodeParams& p,
                                  hipStream_t st);
-hipError_t launch_zero(uint32_t* p, size_t nwords, hipStream_t st);
 
 struct IndexerPrefillParams {
   BatchView bv;

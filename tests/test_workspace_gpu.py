@@ -1,0 +1,110 @@
+"""The decode indexer's workspace contract and its failure path, on the GPU.
+
+A workspace is zero-filled once; every call leaves it ready for the next, so
+one buffer serves calls of different shapes back to back.  When a bounded
+cross-workgroup wait gives up (forced here from the host: the test hook makes
+every barrier target unreachable and every wait give up after a few sleeps,
+so all kernels still end normally), the affected index rows come back as -1
+and DSA_DEBUG=1 reports DSA_ERR_HIP."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from checker import check_topk_row
+from sparse_attention_04_amd import binding as B
+from sparse_attention_04_amd.inputs import case_to, make_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    B.lib()
+
+
+def _check_all(case, idx):
+    idx_h = idx.cpu().numpy()
+    for b in range(case.batch):
+        for i in range(int(case.q_lens_host[b])):
+            check_topk_row(idx_h[case.token(b, i)], oracle.run_query(case, b, i), case.topk)
+
+
+def _cases():
+    return [case_to(make_case("c2_decode_bf16", 51, batch=4, seq_len_range=(2500, 7000)), "cuda"),
+            case_to(make_case("c5_decode4", 52, batch=2, seq_len_range=(3000, 5000)), "cuda"),
+            case_to(make_case("c4_decode_fp8", 53, batch=5, seq_len_range=(2100, 4000)), "cuda"),
+            case_to(make_case("c2_decode_bf16", 54, batch=7, seq_len_range=(2049, 3000), page_size=16), "cuda")]
+
+
+def test_one_workspace_serves_calls_of_different_shapes():
+    cases = _cases()
+    calls = [B.Call(c) for c in cases]
+    need = max(c.workspace(B.DSA_OP_INDEXER_TOPK)[1] for c in calls)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rnd in range(2):
+        for c, call in zip(cases, calls):
+            _say(f"shared workspace round {rnd}: {c.name} B={c.batch} T={c.total_q}")
+            call.use_workspace(B.DSA_OP_INDEXER_TOPK, ws)
+            idx = call.indexer_topk().clone()
+            torch.cuda.synchronize()
+            _check_all(c, idx)
+    # the indexer leaves its part of the workspace as it found it: all zero
+    # (the header's error word and profiling stamps aside)
+    torch.cuda.synchronize()
+    assert int(ws[256:].count_nonzero()) == 0
+
+
+def _with_env(**kv):
+    class Ctx:
+        def __enter__(self):
+            self.old = {k: os.environ.get(k) for k in kv}
+            os.environ.update(kv)
+
+        def __exit__(self, *a):
+            for k, v in self.old.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    return Ctx()
+
+
+def test_forced_timeout_poisons_rows_and_is_reported():
+    case = case_to(make_case("c2_decode_bf16", 55, batch=3, seq_lens=[1500, 4000, 6000]), "cuda")
+    call = B.Call(case)
+    _say("forced timeout: indexer_topk")
+    with _with_env(DSA_TEST_FORCE_TIMEOUT="1"):
+        idx = call.indexer_topk().clone()
+        torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    # the first sequence keeps all of its 1500 positions (no scores, no waits)
+    assert np.array_equal(idx_h[0, :1500], np.arange(1500)) and np.all(idx_h[0, 1500:] == -1)
+    # the scored sequences' rows are poisoned
+    assert np.all(idx_h[1:] == -1)
+    _say("forced timeout: fused decode, SFA over poisoned rows")
+    with _with_env(DSA_TEST_FORCE_TIMEOUT="1"):
+        out, lse, fidx = call.fused_decode()
+        torch.cuda.synchronize()
+    assert np.all(fidx.cpu().numpy()[1:] == -1)
+    assert np.all(np.isneginf(lse.cpu().numpy()[1:]))
+    _say("forced timeout: DSA_DEBUG=1 reports it")
+    with _with_env(DSA_TEST_FORCE_TIMEOUT="1", DSA_DEBUG="1"):
+        with pytest.raises(B.DsaError) as ei:
+            call.indexer_topk()
+    assert ei.value.status == B.DSA_ERR_HIP and "error bits" in str(ei.value)
+    # the failed calls left the workspace clean: the next call is correct
+    _say("forced timeout: a normal call afterwards")
+    with _with_env(DSA_DEBUG="1"):
+        idx = call.indexer_topk().clone()
+    torch.cuda.synchronize()
+    _check_all(case, idx)

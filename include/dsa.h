@@ -198,6 +198,23 @@ dsa_status dsa_fused_prefill(const dsa_batch* batch, const dsa_indexer_args* iar
                              float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* dsa_fused_decode without a workspace, for callers that cannot allocate
+ * device memory (code under graph capture, serving loops that forbid
+ * allocation).  Same arguments, results and errors as dsa_fused_decode; the
+ * scratch memory is a static array of dsa_noalloc_scratch_bytes() (64 MiB)
+ * that every GPU the library runs on holds until the process ends, looked up
+ * once per device.  A call whose dsa_workspace_size(DSA_OP_FUSED_DECODE, ...)
+ * exceeds it returns DSA_ERR_UNSUPPORTED and enqueues nothing.  The first
+ * call on a device also enqueues one clear of the array.  All calls on one
+ * GPU share its array: calls that may overlap on the same GPU (other streams,
+ * other host threads) race and must be ordered by the caller.               */
+dsa_status dsa_fused_decode_noalloc(const dsa_batch* batch, const dsa_indexer_args* iargs,
+                                    const dsa_sfa_args* sargs, void* out, float* lse,
+                                    int32_t* idx_out, void* stream);
+
+/* Bytes of the static scratch array behind dsa_fused_decode_noalloc. */
+size_t dsa_noalloc_scratch_bytes(void);
+
 /* Static text for a status code. */
 const char* dsa_status_string(int32_t status);
 

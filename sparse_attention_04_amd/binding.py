@@ -24,7 +24,8 @@ DTYPE_CODE = {"f32": DSA_F32, "bf16": DSA_BF16, "fp8": DSA_FP8_E4M3, "mxfp8": DS
               "fp8_t128": DSA_FP8_E4M3_TILE128}
 
 EXPORTED = ("dsa_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_fused_decode",
-            "dsa_fused_prefill", "dsa_status_string", "dsa_last_error")
+            "dsa_fused_prefill", "dsa_status_string", "dsa_last_error", "dsa_fused_decode_noalloc",
+            "dsa_noalloc_scratch_bytes")
 
 
 class DsaError(RuntimeError):
@@ -84,6 +85,11 @@ def lib() -> ctypes.CDLL:
         L.dsa_fused_prefill.argtypes = [P(dsa_batch), P(dsa_indexer_args), P(dsa_sfa_args), ctypes.c_int32,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]
+        L.dsa_fused_decode_noalloc.restype = ctypes.c_int
+        L.dsa_fused_decode_noalloc.argtypes = [P(dsa_batch), P(dsa_indexer_args), P(dsa_sfa_args), ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.dsa_noalloc_scratch_bytes.restype = ctypes.c_size_t
+        L.dsa_noalloc_scratch_bytes.argtypes = []
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_status_string.argtypes = [ctypes.c_int32]
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -134,6 +140,15 @@ def dsa_fused_prefill(batch, iargs, sargs, q_block, out, lse, idx_out, ws, ws_by
     _check(lib().dsa_fused_prefill(ctypes.pointer(batch), ctypes.pointer(iargs), ctypes.pointer(sargs),
                                    q_block, _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes,
                                    _stream(stream)))
+
+
+def dsa_fused_decode_noalloc(batch, iargs, sargs, out, lse, idx_out, stream=None):
+    _check(lib().dsa_fused_decode_noalloc(ctypes.pointer(batch), ctypes.pointer(iargs), ctypes.pointer(sargs),
+                                          _ptr(out), _ptr(lse), _ptr(idx_out), _stream(stream)))
+
+
+def dsa_noalloc_scratch_bytes() -> int:
+    return int(lib().dsa_noalloc_scratch_bytes())
 
 
 # ------------------------------------------- struct builders from tensors ---
@@ -190,6 +205,10 @@ class Call:
         dsa_fused_decode(self.batch, self.iargs, self.sargs, self.out, self.lse,
                          self.idx if with_idx else None, ws, n, stream)
         return self.out, self.lse, self.idx
+
+    def fused_decode_noalloc(self, out, lse, idx=None, stream=None):
+        dsa_fused_decode_noalloc(self.batch, self.iargs, self.sargs, out, lse, idx, stream)
+        return out, lse, idx
 
     def fused_prefill(self, with_idx=True, stream=None, q_block=64):
         ws, n = self.workspace(DSA_OP_FUSED_PREFILL)

@@ -1,0 +1,66 @@
+"""The allocation-free decode entry point against the workspace one, on the GPU.
+
+Two calls in a row through the C ABI, the second with a smaller batch (the
+static scratch keeps the first call's contents): the index sets must be
+identical and the SFA output within the bf16 bar of the workspace path's, and
+both are checked against the oracle on every query."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from checker import check_sfa, check_topk_row
+from sparse_attention_04_amd import binding as B
+from sparse_attention_04_amd.inputs import case_to, make_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def test_noalloc_matches_workspace_entry_point():
+    assert torch.cuda.is_available()
+    B.lib()
+    cases = [case_to(make_case("c2_decode_bf16", 61, batch=6, seq_len_range=(3000, 9000)), "cuda"),
+             case_to(make_case("c5_decode4", 62, batch=2, seq_len_range=(2500, 4000)), "cuda")]
+    for case in cases:
+        call = B.Call(case)
+        _say(f"no-alloc: {case.name} B={case.batch} T={case.total_q}: workspace path")
+        out_w, lse_w, idx_w = (t.clone() for t in call.fused_decode())
+        out = torch.empty_like(out_w)
+        lse = torch.empty_like(lse_w)
+        idx = torch.empty_like(idx_w)
+        _say(f"no-alloc: {case.name}: static-scratch path")
+        call.fused_decode_noalloc(out, lse, idx)
+        torch.cuda.synchronize()
+        assert torch.equal(torch.sort(idx, 1).values, torch.sort(idx_w, 1).values)
+        out_h, outw_h = out.float().cpu().numpy(), out_w.float().cpu().numpy()
+        idx_h = idx.cpu().numpy()
+        for b in range(case.batch):
+            for i in range(int(case.q_lens_host[b])):
+                tok = case.token(b, i)
+                check_sfa(out_h[tok], outw_h[tok], "bf16")
+                ref = oracle.run_query(case, b, i)
+                check_topk_row(idx_h[tok], ref, case.topk)
+                sel = idx_h[tok][idx_h[tok] >= 0]
+                check_sfa(out_h[tok], oracle.sfa_query(case, b, i, sel)[0], "bf16")
+        assert np.allclose(lse.cpu().numpy(), lse_w.cpu().numpy(), atol=1e-4, rtol=1e-5)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    B.lib()
+    case = case_to(make_case("c2_decode_bf16", 63, batch=2, seq_len_range=(3000, 4000)), "cuda")
+    call = B.Call(case)
+    call.batch.total_q = 4096          # a decode batch whose scratch exceeds the static array
+    call.batch.batch = 2
+    call.batch.max_q_len = 2048
+    need = B.dsa_workspace_size(B.DSA_OP_FUSED_DECODE, call.batch, call.iargs, call.sargs)
+    assert need > B.dsa_noalloc_scratch_bytes()
+    st = B.lib().dsa_fused_decode_noalloc(*(B.ctypes.pointer(x) for x in (call.batch, call.iargs, call.sargs)),
+                                          call.out.data_ptr(), call.lse.data_ptr(), None, None)
+    assert st == B.DSA_ERR_UNSUPPORTED and b"static scratch" in B.lib().dsa_last_error()

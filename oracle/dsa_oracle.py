@@ -31,6 +31,12 @@ What is computed (the method as the pages state it):
     tile of 128 elements ([P1] sec. 3, "FP8 Block Quantization for SFA KV
     Cache"; [P2] sec. 4.3 and its table; [P3] quantisation item 2; [P4] sec. 4
     and its table).
+  * before the indexer, the prolog projects each new token's hidden row to
+    the indexer query, its key (normalised) and the head weights, quantises
+    the query and key dynamically and appends the key to the paged cache
+    ([P1] sec. 2 "Three-Stream Coordination for Indexer Prolog"; [P2] sec. 3.2
+    and 4.2; [P4] sec. 3.3); the readings it takes are listed with its
+    functions at the end of this module.
 
 Readings where the pages are silent (each is listed in the design notes):
   * no activation on per-head scores; the weighted combination is a sum over
@@ -273,3 +279,147 @@ def _np(x) -> np.ndarray:
             _HOST_CACHE.pop(next(iter(_HOST_CACHE)))
         _HOST_CACHE[id(x)] = (x, a)
     return a
+
+
+# ===================================================== indexer prolog (NEXT) ===
+# The steps the pages place before the fused indexer ([P1] sec. 2 "Three-Stream
+# Coordination for Indexer Prolog"; [P2] sec. 3.2 and 4.2; [P4] sec. 3.3):
+# Q projection, K normalisation, dynamic Q quantisation and the head-weight
+# projection, plus writing the new tokens' keys into the paged K cache.
+# Readings (the pages name the steps, not their formulas):
+#   * one bf16 hidden row x[t] of width d_model per new token feeds all three
+#     projections; weights are bf16 in the linear-layer layout [out][in];
+#   * q = bf16(x W_q^T) reshaped [H][D]; the projections stay bf16 ([P2] sec. 4:
+#     projection is precision-sensitive);
+#   * k = bf16(LayerNorm(x W_k^T)) over the D elements, biased variance,
+#     eps = 1e-6, then gamma and beta;
+#   * w = x W_w^T in float (one weight per head);
+#   * quantisation as for the quantised indexer inputs: FP8 with scale
+#     amax / 448 (1 if amax = 0) in float32, elements x / scale rounded to
+#     nearest-even and saturated (per token and head for q, per token for k);
+#     MXFP8 with E = floor(log2 amax) - 8 clamped to [-127, 127] per group of
+#     32, elements x * 2^-E rounded and saturated (OCP MX v1.0 rule for e4m3);
+#   * the new key of token i of sequence b goes to position t = L_b - T_b + i:
+#     row t % P of page block_table[b][t // P], with its scale(s).
+
+def round_bf16_bits(x) -> np.ndarray:
+    """float64 -> bf16 bit pattern (uint16) rounding the exact value to nearest,
+    ties to an even significand: a bf16 number has 8 significant bits (7
+    stored), the float32 exponent range and subnormals below 2^-126."""
+    x = np.asarray(x, np.float64)
+    out = np.zeros(x.shape, np.uint16)
+    flat, res = x.reshape(-1), out.reshape(-1)
+    for n, v in enumerate(flat):
+        if v != v:
+            res[n] = 0x7FC0
+            continue
+        sign = 0x8000 if (v < 0 or (v == 0 and np.signbit(v))) else 0
+        a = abs(float(v))
+        if a == 0.0:
+            res[n] = sign
+            continue
+        e = max(int(np.floor(np.log2(a))), -126)
+        if 2.0 ** e > a:            # guard log2 rounding
+            e -= 1
+        elif 2.0 ** (e + 1) <= a:
+            e += 1
+        e = max(e, -126)
+        q = a / 2.0 ** (e - 7)      # significand in units of the last place
+        m = np.floor(q)
+        frac = q - m
+        if frac > 0.5 or (frac == 0.5 and int(m) % 2 == 1):
+            m += 1
+        val = m * 2.0 ** (e - 7)
+        if val >= 2.0 ** 128:
+            res[n] = sign | 0x7F80          # overflow: infinity
+            continue
+        b = np.float32(val).view(np.uint32) >> 16
+        res[n] = sign | int(b)
+    return out
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """float -> OCP e4m3fn byte: the nearest value of the e4m3 table (ties to
+    the even code), saturating to +-448; the sign of zero is kept."""
+    y = np.asarray(y, np.float64)
+    t = _E4M3[:0x7F]                 # codes 0x00..0x7E: 0 .. 448, increasing
+    a = np.minimum(np.abs(y), 448.0)
+    hi = np.clip(np.searchsorted(t, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - t[lo], t[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    neg = np.signbit(y)
+    return np.where(neg, code | 0x80, code).astype(np.uint8)
+
+
+def fp8_quantise(v):
+    """One row of float values (float32-exact) -> (e4m3 bytes, float32 scale):
+    scale = amax / 448 in float32 (1 for an all-zero row), elements v / scale
+    in float32, then rounded to e4m3."""
+    v = np.asarray(v, np.float32)
+    amax = np.float32(np.max(np.abs(v))) if v.size else np.float32(0)
+    s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    y = (v / s).astype(np.float32)
+    return e4m3_encode(y), s
+
+
+def mx_quantise(v, group: int = 32):
+    """One row (float32-exact values) -> (e4m3 bytes, e8m0 bytes per group):
+    E = floor(log2 amax) - 8 (amax = 0 -> -127), clamped to [-127, 127];
+    elements v * 2^-E, rounded to e4m3 with saturation."""
+    v = np.asarray(v, np.float32).reshape(-1, group)
+    codes, scales = [], []
+    for g in v:
+        amax = float(np.max(np.abs(g)))
+        if amax > 0:
+            m, ex = np.frexp(amax)            # amax = m 2^ex, m in [0.5, 1)
+            E = int(ex) - 1 - 8
+        else:
+            E = -127
+        E = min(max(E, -127), 127)
+        codes.append(e4m3_encode(np.ldexp(g.astype(np.float64), -E)))
+        scales.append(E + 127)
+    return np.concatenate(codes), np.asarray(scales, np.uint8)
+
+
+def layer_norm(v, gamma, beta, eps: float = 1e-6):
+    """(v - mean) / sqrt(var + eps) * gamma + beta over the last axis, biased var."""
+    v = np.asarray(v, np.float64)
+    mu = v.mean(axis=-1, keepdims=True)
+    var = ((v - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (v - mu) / np.sqrt(var + eps) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+
+
+def prolog_token(x_bits, wq_bits, wk_bits, ww_bits, gamma, beta, n_heads: int, head_dim: int,
+                 eps: float = 1e-6):
+    """The projections of one new token: x [d_model] bf16 bits, weights bf16 bits
+    [out][in].  Returns (q bf16 bits [H][D], k bf16 bits [D], w float64 [H])."""
+    x = decode_bf16_bits(x_bits)
+    q = decode_bf16_bits(wq_bits) @ x
+    k = layer_norm(decode_bf16_bits(wk_bits) @ x, gamma, beta, eps)
+    w = decode_bf16_bits(ww_bits) @ x
+    return round_bf16_bits(q).reshape(n_heads, head_dim), round_bf16_bits(k), w
+
+
+def quantise_query(q_bits, dtype: str):
+    """q bf16 bits [H][D] -> (stored q, its scales) for the indexer dtype."""
+    q = decode_bf16_bits(q_bits)
+    if dtype == "bf16":
+        return np.asarray(q_bits, np.uint16), None
+    parts = [fp8_quantise(r) if dtype == "fp8" else mx_quantise(r) for r in q]
+    return np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts])
+
+
+def quantise_key(k_bits, dtype: str):
+    """k bf16 bits [D] -> (stored key row, its scale(s))."""
+    if dtype == "bf16":
+        return np.asarray(k_bits, np.uint16), None
+    k = decode_bf16_bits(k_bits)
+    return fp8_quantise(k) if dtype == "fp8" else mx_quantise(k)
+
+
+def append_position(seq_len: int, q_len: int, i: int, block_table_row, page_size: int):
+    """(page, row) where the key of new token i goes: position t = L - T + i."""
+    t = query_position(seq_len, q_len, i)
+    return int(np.asarray(block_table_row)[t // page_size]), t % page_size

@@ -145,6 +145,29 @@ def prefill_line(torch, B, make_case, steps):
             "peak_tflops": MFMA_PEAK_TFLOPS["bf16"]}
 
 
+def prolog_line(torch, B, make_case, steps, warmup):
+    """The indexer prolog for the quantised decode workload's 64 new tokens
+    (hidden rows of 7168, FP8 q and keys): projections, LayerNorm, dynamic
+    quantisation and the key append, against the HBM roof (the weights dominate
+    its bytes)."""
+    from sparse_attention_04_amd.inputs import make_prolog
+    case = make_case("c4_decode_fp8", 4, device="cuda")
+    pros = [make_prolog(case, 80 + r, d_model=7168) for r in range(2)]
+    call = B.Call(case)
+    call.prolog(pros[0])
+    ms = time_calls(lambda s: call.prolog(pros[s % 2]), steps, warmup, torch)
+    T, H, D, dm = case.total_q, case.h_i, case.d_i, pros[0]["d_model"]
+    wbytes = (H * D + D + H) * dm * 2
+    nbytes = wbytes + T * dm * 2 + T * H * (D + 4 + 4) + T * (D + 4)
+    out = {"workload": "c4 prolog: 64 new tokens, hidden 7168 -> q 64x128, k 128 (LayerNorm), w 64; FP8 q and keys, "
+                       "keys appended to the paged cache", "ms_per_call": ms,
+           "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+           "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del call, case, pros
+    torch.cuda.empty_cache()
+    return out
+
+
 def config_line(torch, B, make_case, name, steps, warmup, sets):
     """One more workload of the scope table: fused-call time and its rate
     against the roof that bounds it (HBM for decode, MFMA for prefill)."""
@@ -195,6 +218,8 @@ def main():
                     help="skip the 32k causal prefill measurement")
     ap.add_argument("--no-extra", dest="extra", action="store_false",
                     help="skip the C4 and C5 measurements")
+    ap.add_argument("--only-prolog", action="store_true",
+                    help="print only the indexer prolog measurement")
     ap.add_argument("--only-prefill", action="store_true",
                     help="print only the 32k causal prefill measurement (--steps calls per stage)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -211,6 +236,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     B.lib()
+    if args.only_prolog:
+        print(json.dumps(prolog_line(torch, B, make_case, args.steps, args.warmup)), flush=True)
+        return
     if args.only_prefill:
         print(json.dumps(prefill_line(torch, B, make_case, args.steps)), flush=True)
         return
@@ -288,6 +316,8 @@ def main():
     headline = args.workload == "c2_decode_bf16_32k"
     if headline and args.prefill:
         line["prefill_32k"] = prefill_line(torch, B, make_case, 3)
+    if headline and args.extra:
+        line["prolog"] = prolog_line(torch, B, make_case, 50, 5)
     if headline and args.extra:
         line["other_configs"] = {
             n: config_line(torch, B, make_case, n, *((3, 1, 1) if n == "c5_chunk_prefill" else (50, 5, 2)))

@@ -155,6 +155,31 @@ typedef struct {
   const dsa_paged_cache* kv_cache;
 } dsa_sfa_args;
 
+/* Indexer prolog operands: the projections of the new tokens' hidden rows
+ * that feed the indexer ("Three-Stream Coordination for Indexer Prolog", Day0
+ * Inference Optimization on Ascend CANN, sec. 2; Adapting and Optimizing
+ * Inference for a New Model Architecture on Ascend, sec. 3.2 and 4.2).
+ * x        device bf16 [total_q][d_model], one hidden row per new token
+ * w_q      device bf16 [n_heads * head_dim][d_model]  (linear-layer layout)
+ * w_k      device bf16 [head_dim][d_model]
+ * w_w      device bf16 [n_heads][d_model]
+ * ln_gamma, ln_beta  device float32 [head_dim]: the key LayerNorm
+ * out_dtype DSA_BF16, DSA_FP8_E4M3 or DSA_MXFP8_E4M3: how q and the appended
+ *          keys are stored (the indexer's dtype)                            */
+typedef struct {
+  const void* x;
+  int32_t d_model;             /* a positive multiple of 512                     */
+  const void* w_q;
+  const void* w_k;
+  const void* w_w;
+  const float* ln_gamma;
+  const float* ln_beta;
+  float ln_eps;
+  int32_t n_heads;             /* a multiple of 32                                */
+  int32_t head_dim;            /* 128                                             */
+  int32_t out_dtype;
+} dsa_prolog_args;
+
 /* Bytes of workspace the call needs (0 is possible).  Device pointers are not
  * read; the scalars are, and sfa->kv_cache->dtype when sfa->kv_cache is not
  * NULL (an FP8 KV cache changes the work split).  `topk` for
@@ -214,6 +239,37 @@ dsa_status dsa_fused_decode_noalloc(const dsa_batch* batch, const dsa_indexer_ar
 
 /* Bytes of the static scratch array behind dsa_fused_decode_noalloc. */
 size_t dsa_noalloc_scratch_bytes(void);
+
+/* Indexer prolog for the new tokens of a step (the steps the pages place
+ * before the fused indexer: Q projection, K normalisation, dynamic Q
+ * quantisation, head-weight projection; index Q/K dynamically quantised, MXFP8
+ * in groups of 32 -- same pages as dsa_prolog_args).  For every new token:
+ *   q = bf16(x W_q^T) as [n_heads][head_dim]; k = bf16(LayerNorm(x W_k^T))
+ *   (biased variance, ln_eps, then gamma and beta); w = x W_w^T (float32).
+ *   Quantisation per out_dtype: FP8 scale = amax / 448 (1 for an all-zero
+ *   row) in float32, elements x / scale rounded to nearest even and saturated,
+ *   per (token, head) for q and per token for k; MXFP8 E = floor(log2 amax) - 8
+ *   clamped to [-127, 127] per 32 elements, elements x 2^-E rounded and
+ *   saturated (OCP MX v1.0 for e4m3).
+ * Outputs (device): q_out [total_q][n_heads][head_dim] (bf16 or e4m3 bytes);
+ *   q_scale_out float32 [total_q][n_heads] (FP8) or e8m0 [total_q][n_heads]
+ *   [head_dim/32] (MXFP8), NULL for bf16; w_out float32 [total_q][n_heads].
+ *   Token i of sequence b (t = L_b - T_b + i) has its key written into
+ *   k_cache at row t % P of page block_table[b][t / P], with its scale(s);
+ *   no other cache row is touched (k_cache->dtype must equal out_dtype).
+ *   q_bf16_out (optional, [total_q][n_heads*head_dim] bf16) receives q before
+ *   quantisation (ignored for bf16 output, where q_out holds it), k_bf16_out
+ *   (optional, [total_q][head_dim]) k before it.
+ * Alignment: x, the weights, q_out, q_bf16_out and w_out 16 bytes.
+ * Workspace: dsa_prolog_workspace_size() bytes (no state kept between calls).
+ * Errors as for the other entry points.                                     */
+dsa_status dsa_indexer_prolog(const dsa_batch* batch, const dsa_prolog_args* args, void* q_out,
+                              void* q_scale_out, float* w_out, const dsa_paged_cache* k_cache,
+                              void* q_bf16_out, void* k_bf16_out, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Bytes of workspace dsa_indexer_prolog needs (0 for invalid arguments). */
+size_t dsa_prolog_workspace_size(const dsa_batch* batch, const dsa_prolog_args* args);
 
 /* Static text for a status code. */
 const char* dsa_status_string(int32_t status);

@@ -25,7 +25,7 @@ DTYPE_CODE = {"f32": DSA_F32, "bf16": DSA_BF16, "fp8": DSA_FP8_E4M3, "mxfp8": DS
 
 EXPORTED = ("dsa_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_fused_decode",
             "dsa_fused_prefill", "dsa_status_string", "dsa_last_error", "dsa_fused_decode_noalloc",
-            "dsa_noalloc_scratch_bytes")
+            "dsa_noalloc_scratch_bytes", "dsa_indexer_prolog", "dsa_prolog_workspace_size")
 
 
 class DsaError(RuntimeError):
@@ -55,6 +55,13 @@ class dsa_sfa_args(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("q_dtype", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("qk_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("kv_cache", ctypes.POINTER(dsa_paged_cache))]
+
+
+class dsa_prolog_args(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("d_model", ctypes.c_int32), ("w_q", ctypes.c_void_p),
+                ("w_k", ctypes.c_void_p), ("w_w", ctypes.c_void_p), ("ln_gamma", ctypes.c_void_p),
+                ("ln_beta", ctypes.c_void_p), ("ln_eps", ctypes.c_float), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
 
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -90,6 +97,12 @@ def lib() -> ctypes.CDLL:
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.dsa_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.dsa_noalloc_scratch_bytes.argtypes = []
+        L.dsa_indexer_prolog.restype = ctypes.c_int
+        L.dsa_indexer_prolog.argtypes = [P(dsa_batch), P(dsa_prolog_args), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, P(dsa_paged_cache), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.dsa_prolog_workspace_size.restype = ctypes.c_size_t
+        L.dsa_prolog_workspace_size.argtypes = [P(dsa_batch), P(dsa_prolog_args)]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_status_string.argtypes = [ctypes.c_int32]
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -151,6 +164,17 @@ def dsa_noalloc_scratch_bytes() -> int:
     return int(lib().dsa_noalloc_scratch_bytes())
 
 
+def dsa_indexer_prolog(batch, pargs, q_out, q_scale_out, w_out, k_cache, q_bf16_out, k_bf16_out, ws, ws_bytes,
+                       stream=None):
+    _check(lib().dsa_indexer_prolog(ctypes.pointer(batch), ctypes.pointer(pargs), _ptr(q_out), _ptr(q_scale_out),
+                                    _ptr(w_out), ctypes.pointer(k_cache), _ptr(q_bf16_out), _ptr(k_bf16_out),
+                                    _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dsa_prolog_workspace_size(batch, pargs) -> int:
+    return int(lib().dsa_prolog_workspace_size(ctypes.pointer(batch), ctypes.pointer(pargs)))
+
+
 # ------------------------------------------- struct builders from tensors ---
 
 class Call:
@@ -205,6 +229,21 @@ class Call:
         dsa_fused_decode(self.batch, self.iargs, self.sargs, self.out, self.lse,
                          self.idx if with_idx else None, ws, n, stream)
         return self.out, self.lse, self.idx
+
+    def prolog(self, pro, q_bf16_out=None, k_bf16_out=None, stream=None):
+        """Run the indexer prolog on the prolog inputs `pro` (make_prolog): it
+        writes this case's indexer q, q scales and head weights and appends the
+        new tokens' keys to its K cache.  Returns the tensors it wrote."""
+        c = self.case
+        args = dsa_prolog_args(_ptr(pro["x"]), pro["d_model"], _ptr(pro["w_q"]), _ptr(pro["w_k"]),
+                               _ptr(pro["w_w"]), _ptr(pro["ln_gamma"]), _ptr(pro["ln_beta"]), pro["ln_eps"],
+                               c.h_i, c.d_i, DTYPE_CODE[c.idx_dtype])
+        n = dsa_prolog_workspace_size(self.batch, args)
+        if "prolog" not in self._ws or self._ws["prolog"].numel() < n:
+            self._ws["prolog"] = torch.zeros(max(n, 1), dtype=torch.uint8, device=c.q_s.device)
+        dsa_indexer_prolog(self.batch, args, c.q_i, c.q_i_scale, c.w, self.k_cache, q_bf16_out, k_bf16_out,
+                           self._ws["prolog"], n, stream)
+        return c.q_i, c.q_i_scale, c.w
 
     def fused_decode_noalloc(self, out, lse, idx=None, stream=None):
         dsa_fused_decode_noalloc(self.batch, self.iargs, self.sargs, out, lse, idx, stream)

@@ -487,6 +487,69 @@ void clear_error() { g_err.clear(); }
 
 extern "C" {
 
+size_t dsa_prolog_workspace_size(const dsa_batch* b, const dsa_prolog_args* a) {
+  if (!b || !a || b->total_q < 0 || a->n_heads < 1 || a->head_dim < 1) return 0;
+  return align_up((size_t)b->total_q * a->n_heads * a->head_dim * 2, 256) +
+         align_up((size_t)b->total_q * a->head_dim * 4, 256) + 256;
+}
+
+dsa_status dsa_indexer_prolog(const dsa_batch* b, const dsa_prolog_args* a, void* q_out, void* q_scale_out,
+                              float* w_out, const dsa_paged_cache* kc, void* q_bf16_out, void* k_bf16_out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  dsa_status s = check_batch(b);
+  if (s != DSA_OK) return s;
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "prolog args are NULL");
+  if (!a->x || !a->w_q || !a->w_k || !a->w_w || !a->ln_gamma || !a->ln_beta)
+    return fail(DSA_ERR_INVALID_ARG, "prolog x, weights and LayerNorm parameters must be non-NULL");
+  if (a->out_dtype != DSA_BF16 && a->out_dtype != DSA_FP8_E4M3 && a->out_dtype != DSA_MXFP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "prolog out_dtype %d: bf16, fp8 or mxfp8", a->out_dtype);
+  if (a->head_dim != 128 || a->n_heads < 32 || a->n_heads % 32 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "prolog shape (heads %d, dim %d) not compiled in: head_dim 128, heads a multiple of 32",
+                a->n_heads, a->head_dim);
+  if (a->d_model < 512 || a->d_model % 512 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "prolog d_model %d must be a positive multiple of 512", a->d_model);
+  if (!(a->ln_eps >= 0.f) || !(a->ln_eps < 1e30f)) return fail(DSA_ERR_INVALID_ARG, "ln_eps must be finite and >= 0");
+  const bool quant = a->out_dtype != DSA_BF16;
+  if (!q_out || !w_out || (quant && !q_scale_out))
+    return fail(DSA_ERR_INVALID_ARG, "q_out, w_out (and q_scale_out for a quantised dtype) must be non-NULL");
+  if (!aligned(a->x, 16) || !aligned(a->w_q, 16) || !aligned(a->w_k, 16) || !aligned(a->w_w, 16) ||
+      !aligned(q_out, 16) || !aligned(w_out, 16) || !aligned(q_bf16_out, 16) || !aligned(k_bf16_out, 4) ||
+      !aligned(a->ln_gamma, 4) || !aligned(a->ln_beta, 4) || !aligned(q_scale_out, 4) || !aligned(ws, 16))
+    return fail(DSA_ERR_INVALID_ARG, "prolog x, weights, q_out, q_bf16_out, w_out and ws must be 16-byte aligned, "
+                                     "the other arrays 4-byte aligned");
+  s = check_cache(kc, "k_cache", a->head_dim, a->out_dtype, b);
+  if (s != DSA_OK) return s;
+  const size_t need = dsa_prolog_workspace_size(b, a);
+  if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (b->total_q == 0) return DSA_OK;
+  unsigned char* w = (unsigned char*)ws;
+  PrologParams p{};
+  p.bv = view_of(b, kc->page_size);
+  p.total_q = b->total_q;
+  p.d_model = a->d_model;
+  p.H = a->n_heads;
+  p.D = a->head_dim;
+  p.x = a->x;
+  p.w_q = a->w_q;
+  p.w_k = a->w_k;
+  p.w_w = a->w_w;
+  p.ln_gamma = a->ln_gamma;
+  p.ln_beta = a->ln_beta;
+  p.ln_eps = a->ln_eps;
+  p.q_bf16 = !quant ? q_out : (q_bf16_out ? q_bf16_out : (void*)w);
+  p.q_out = q_out;
+  p.q_scale_out = q_scale_out;
+  p.w_out = w_out;
+  p.k_f32 = (float*)(w + align_up((size_t)b->total_q * a->n_heads * a->head_dim * 2, 256));
+  p.k_bf16_out = k_bf16_out;
+  p.k_data = const_cast<void*>(kc->data);
+  p.k_scale = const_cast<void*>(kc->scale);
+  hipError_t e = launch_prolog(dt_kernel(a->out_dtype), p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prolog launch");
+  return DSA_OK;
+}
+
 dsa_status dsa_fused_prefill(const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa,
                              int32_t q_block, void* out, float* lse, int32_t* idx_out, void* ws,
                              size_t ws_bytes, void* stream) {

@@ -58,6 +58,31 @@ int indexer_prefill_max_pages();
 int indexer_prefill_max_topk();
 hipError_t launch_indexer_prefill(int dtype, int H, int D, const IndexerPrefillParams& p, hipStream_t st);
 
+// -------------------------------------------------------- indexer prolog ---
+
+struct PrologParams {
+  BatchView bv;
+  int32_t total_q, d_model, H, D;
+  const void* x;           // [total_q][d_model] bf16
+  const void* w_q;         // [H*D][d_model] bf16
+  const void* w_k;         // [D][d_model] bf16
+  const void* w_w;         // [H][d_model] bf16
+  const float* ln_gamma;   // [D]
+  const float* ln_beta;    // [D]
+  float ln_eps;
+  void* q_bf16;            // [total_q][H*D] bf16: the projected q (q_out itself for bf16 output)
+  void* q_out;             // fp8 / mx: [total_q][H][D] e4m3 bytes
+  void* q_scale_out;       // fp8: f32 [total_q][H]; mx: u8 [total_q][H][D/32]
+  float* w_out;            // [total_q][H]
+  float* k_f32;            // [total_q][D] projected keys before normalisation (workspace)
+  void* k_bf16_out;        // optional [total_q][D] bf16 normalised keys
+  void* k_data;            // paged K cache [num_pages][P][D] (written at the new tokens' rows)
+  void* k_scale;           // its scales (fp8: f32 [num_pages][P]; mx: u8 [num_pages][P][D/32])
+};
+
+int prolog_n_tiles(int H, int D);
+hipError_t launch_prolog(int out_dtype, const PrologParams& p, hipStream_t st);
+
 // ------------------------------------------------------------------- SFA ---
 
 // (dtype, H_S, Dqk, Dv) instantiations of SFA.

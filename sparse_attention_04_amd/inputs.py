@@ -52,7 +52,8 @@ KV_TILE = 128
 
 # Tensor ids for per-tensor seeding (fixed: changing them changes every case).
 _TID = dict(seq_lens=1, pages=2, q_i=3, k_i=4, w=5, q_s=6, kv=7,
-            out_q_i=8, out_k_i=9, out_q_s=10, out_kv=11)
+            out_q_i=8, out_k_i=9, out_q_s=10, out_kv=11,
+            pro_x=12, pro_wq=13, pro_wk=14, pro_ww=15, pro_ln=16)
 
 
 def _gen(seed: int, tid: str, device: str) -> torch.Generator:
@@ -404,3 +405,28 @@ def case_to(case: Case, device: str) -> Case:
         d[f.name] = v.to(device) if isinstance(v, torch.Tensor) else v
     d["device"] = device
     return Case(**d)
+
+
+def make_prolog(case: Case, seed: int, d_model: int = 7168, ln_eps: float = 1e-6) -> dict:
+    """Seeded synthetic inputs of the indexer prolog for a case's new tokens:
+    hidden rows x ~ N(0, 1) in bf16; projection weights in the linear-layer
+    layout [out][in], bf16, N(0, 1/d_model) so that the projections are of unit
+    scale (the head-weight rows further divided by 64, like the head weights
+    of the indexer workloads, and of either sign); LayerNorm gamma ~ 1 +
+    0.1 N(0, 1), beta ~ 0.1 N(0, 1) in float32."""
+    dev, T, H, D = case.device, case.total_q, case.h_i, case.d_i
+    sd = 1.0 / math.sqrt(d_model)
+
+    def nrm(tid, shape, mult=1.0):
+        return torch.randn(shape, generator=_gen(seed, tid, dev), device=dev, dtype=torch.float32) * mult
+
+    gl = _gen(seed, "pro_ln", dev)
+    return dict(
+        d_model=d_model, ln_eps=ln_eps,
+        x=round_bf16(nrm("pro_x", (T, d_model))).contiguous(),
+        w_q=round_bf16(nrm("pro_wq", (H * D, d_model), sd)).contiguous(),
+        w_k=round_bf16(nrm("pro_wk", (D, d_model), sd)).contiguous(),
+        w_w=round_bf16(nrm("pro_ww", (H, d_model), sd / 64.0)).contiguous(),
+        ln_gamma=(1.0 + 0.1 * torch.randn(D, generator=gl, device=dev)).float().contiguous(),
+        ln_beta=(0.1 * torch.randn(D, generator=gl, device=dev)).float().contiguous(),
+    )

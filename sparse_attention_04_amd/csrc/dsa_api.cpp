@@ -507,8 +507,9 @@ dsa_status dsa_indexer_prolog(const dsa_batch* b, const dsa_prolog_args* a, void
   if (a->head_dim != 128 || a->n_heads < 32 || a->n_heads % 32 != 0)
     return fail(DSA_ERR_UNSUPPORTED, "prolog shape (heads %d, dim %d) not compiled in: head_dim 128, heads a multiple of 32",
                 a->n_heads, a->head_dim);
-  if (a->d_model < 512 || a->d_model % 512 != 0)
-    return fail(DSA_ERR_UNSUPPORTED, "prolog d_model %d must be a positive multiple of 512", a->d_model);
+  if (a->d_model < prolog_d_model_unit() || a->d_model % prolog_d_model_unit() != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "prolog d_model %d must be a positive multiple of %d", a->d_model,
+                prolog_d_model_unit());
   if (!(a->ln_eps >= 0.f) || !(a->ln_eps < 1e30f)) return fail(DSA_ERR_INVALID_ARG, "ln_eps must be finite and >= 0");
   const bool quant = a->out_dtype != DSA_BF16;
   if (!q_out || !w_out || (quant && !q_scale_out))

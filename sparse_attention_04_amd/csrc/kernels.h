@@ -81,6 +81,7 @@ struct PrologParams {
 };
 
 int prolog_n_tiles(int H, int D);
+int prolog_d_model_unit();
 hipError_t launch_prolog(int out_dtype, const PrologParams& p, hipStream_t st);
 
 // ------------------------------------------------------------------- SFA ---

@@ -15,8 +15,8 @@
 // workgroup per token, quantises q per (token, head) or per 32-group,
 // normalises and quantises k and writes it into the cache.
 //
-//   prolog_gemm_kernel: out[t][c] = sum_k x[t][k] W[c][k] over d_model; four
-//     waves split d_model and their partial tiles are summed in LDS in wave
+//   prolog_gemm_kernel: out[t][c] = sum_k x[t][k] W[c][k] over d_model; eight
+//     waves split d_model and their partial tiles are summed in LDS in a fixed
 //     order (deterministic).  q columns are rounded to bf16, k and w stay
 //     float32.  32x32x16 bf16 MFMAs: x rows on M (tokens, 64 per workgroup),
 //     weight rows on N (32 columns per workgroup).  For decode (tens of tokens)
@@ -30,10 +30,12 @@ namespace dsa {
 
 namespace {
 
-constexpr int kPgThreads = 256;     // 4 waves
+constexpr int kPgWaves = 8;
+constexpr int kPgThreads = 64 * kPgWaves;
 constexpr int kPgM = 64;            // tokens per workgroup (two 32-row M-tiles)
 constexpr int kPgN = 32;            // weight rows (output columns) per workgroup
 constexpr int kPgChunk = 8;         // K-steps of 16 loaded together
+constexpr int kPgDmodelUnit = kPgWaves * 16 * kPgChunk;   // d_model granularity (1024)
 
 __device__ __forceinline__ int find_seq_pg(const BatchView& bv, int tok) {
   int lo = 0, hi = bv.batch - 1;
@@ -53,15 +55,19 @@ __device__ __forceinline__ void tile_of(const PrologParams& p, int tile, int& ma
   else { mat = 2; row0 = (tile - nq - nk) * kPgN; }
 }
 
+// Eight waves split d_model; each streams its slice in chunks of 8 K-steps
+// through two register buffers used alternately (unrolled by two, so the next
+// chunk's loads stay in flight while the current chunk's MFMAs run, with no
+// register copies that would wait for them).
 __global__ __launch_bounds__(kPgThreads) void prolog_gemm_kernel(PrologParams p) {
-  __shared__ __attribute__((aligned(16))) float part[4][2][16][64];   // [wave][mt][i][lane]
+  __shared__ __attribute__((aligned(16))) float part[4][2][16][64];   // [wave % 4][mt][i][lane]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int mat, row0;
   tile_of(p, blockIdx.x, mat, row0);
   const uint16_t* W = (const uint16_t*)(mat == 0 ? p.w_q : mat == 1 ? p.w_k : p.w_w);
   const int m0 = blockIdx.y * kPgM;
   const int dm = p.d_model;
-  const int kw = dm / 4;                              // this wave's slice of d_model
+  const int kw = dm / kPgWaves;                       // this wave's slice of d_model
   const int kbeg = wave * kw;
   // lane l: A rows (tokens) m0 + 32 mt + l%32, B row (column) row0 + l%32;
   // K elements 8 (l/32) .. +7 of each 16-wide step
@@ -74,68 +80,85 @@ __global__ __launch_bounds__(kPgThreads) void prolog_gemm_kernel(PrologParams p)
   f32x16 acc0, acc1;
 #pragma unroll
   for (int i = 0; i < 16; i++) { acc0[i] = 0.f; acc1[i] = 0.f; }
+  struct Buf { u32x4 a0[kPgChunk], a1[kPgChunk], b[kPgChunk]; };
   // a step is 16 elements = 2 u32x4 apart in each row
-  const int nsteps = kw / 16;
-  u32x4 ra[2][kPgChunk], rb[kPgChunk], na[2][kPgChunk], nb[kPgChunk];
-  auto load = [&](int c, u32x4 (&a)[2][kPgChunk], u32x4 (&b)[kPgChunk]) {
+  auto load = [&](int c, Buf& f) {
 #pragma unroll
     for (int s = 0; s < kPgChunk; s++) {
       const int st = c * kPgChunk + s;
-      a[0][s] = xa0[2 * st];
-      a[1][s] = xa1[2 * st];
-      b[s] = wb[2 * st];
+      f.a0[s] = xa0[2 * st];
+      f.a1[s] = xa1[2 * st];
+      f.b[s] = wb[2 * st];
     }
   };
-  const int nchunks = nsteps / kPgChunk;
-  load(0, ra, rb);
-  for (int c = 0; c < nchunks; c++) {
-    if (c + 1 < nchunks) load(c + 1, na, nb);
+  auto mma = [&](const Buf& f) {
 #pragma unroll
     for (int s = 0; s < kPgChunk; s++) {
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, rb[s]);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ra[0][s]), bv, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ra[1][s]), bv, acc1, 0, 0, 0);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, f.b[s]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a0[s]), bv, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a1[s]), bv, acc1, 0, 0, 0);
     }
-#pragma unroll
-    for (int s = 0; s < kPgChunk; s++) {
-      ra[0][s] = na[0][s];
-      ra[1][s] = na[1][s];
-      rb[s] = nb[s];
+  };
+  const int nchunks = kw / (16 * kPgChunk);
+  Buf f0, f1;
+  load(0, f0);
+  if (nchunks > 1) load(1, f1);
+  for (int c = 0; c < nchunks; c += 2) {
+    mma(f0);
+    if (c + 2 < nchunks) load(c + 2, f0);
+    if (c + 1 < nchunks) {
+      mma(f1);
+      if (c + 3 < nchunks) load(c + 3, f1);
     }
   }
+  // sum the eight waves' tiles in a fixed order: waves 4..7 into 0..3, then
+  // the four
+  if (wave >= 4) {
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    part[wave][0][i][lane] = acc0[i];
-    part[wave][1][i][lane] = acc1[i];
+    for (int i = 0; i < 16; i++) {
+      part[wave - 4][0][i][lane] = acc0[i];
+      part[wave - 4][1][i][lane] = acc1[i];
+    }
   }
   __syncthreads();
-  // thread t: token m0 + t/4, columns 8 (t%4) .. +7 of the tile; partials
-  // summed in wave order.  C layout of a 32x32 tile: lane l holds column l%32
-  // and rows 8 (i/4) + 4 (l/32) + i%4.
-  const int tl = tid >> 2, cg = tid & 3;
+  if (wave < 4) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      acc0[i] += part[wave][0][i][lane];
+      acc1[i] += part[wave][1][i][lane];
+    }
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      part[wave][0][i][lane] = acc0[i];
+      part[wave][1][i][lane] = acc1[i];
+    }
+  }
+  __syncthreads();
+  // thread t: token m0 + t/8, columns 4 (t%8) .. +3 of the tile.  C layout of
+  // a 32x32 tile: lane l holds column l%32 and rows 8 (i/4) + 4 (l/32) + i%4.
+  const int tl = tid >> 3, cg = tid & 7;
   const int tok = m0 + tl;
   if (tok >= p.total_q) return;
   const int mt = tl >> 5, r = tl & 31;
   const int ii = (r >> 3) * 4 + (r & 3), lh = (r >> 2) & 1;
-  float v[8];
+  float v[4];
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const int ln = lh * 32 + 8 * cg + j;
+  for (int j = 0; j < 4; j++) {
+    const int ln = lh * 32 + 4 * cg + j;
     v[j] = ((part[0][mt][ii][ln] + part[1][mt][ii][ln]) + part[2][mt][ii][ln]) + part[3][mt][ii][ln];
   }
-  const int col = row0 + 8 * cg;
+  const int col = row0 + 4 * cg;
   if (mat == 0) {
-    uint16_t* dst = (uint16_t*)p.q_bf16 + (size_t)tok * p.H * p.D + col;
-    uint4 pk;
+    uint2 pk;
     pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
     pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-    pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-    *(uint4*)dst = pk;
+    *(uint2*)((uint16_t*)p.q_bf16 + (size_t)tok * p.H * p.D + col) = pk;
   } else {
     float* dst = (mat == 1) ? p.k_f32 + (size_t)tok * p.D + col : p.w_out + (size_t)tok * p.H + col;
     *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
-    *(f32x4*)(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
   }
 }
 
@@ -152,17 +175,26 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return ex == 0 ? -127 : max(ex - 127 - 8, -127);
 }
 
+constexpr int kFinThreads = 256;   // 4 waves; 4 workgroups per token, 16 heads each
+
 template <int OUT>
-__global__ __launch_bounds__(kPgThreads) void prolog_finish_kernel(PrologParams p) {
+__global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams p) {
   const int tok = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = p.H, D = p.D;          // D == 128: two elements per lane
-  // ---- q: wave w quantises heads w, w + 4, ...
+  // ---- q: workgroup y quantises heads 16y .. 16y + 15, four per wave (all
+  // four loaded before any is used)
   if (OUT != kBF16) {
     const uint16_t* q = (const uint16_t*)p.q_bf16 + (size_t)tok * H * D;
-    for (int h = wave; h < H; h += 4) {
-      const uint32_t two = *(const uint32_t*)(q + (size_t)h * D + 2 * lane);
-      const float a = bf16_to_f32((uint16_t)(two & 0xFFFFu)), b = bf16_to_f32((uint16_t)(two >> 16));
+    const int hb = 16 * blockIdx.y + 4 * wave;
+    uint32_t two[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) two[u] = (hb + u < H) ? *(const uint32_t*)(q + (size_t)(hb + u) * D + 2 * lane) : 0u;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int h = hb + u;
+      if (h >= H) break;
+      const float a = bf16_to_f32((uint16_t)(two[u] & 0xFFFFu)), b = bf16_to_f32((uint16_t)(two[u] >> 16));
       float m = fmaxf(fabsf(a), fabsf(b));
       uint32_t bytes;
       if (OUT == kFP8) {
@@ -181,8 +213,8 @@ __global__ __launch_bounds__(kPgThreads) void prolog_finish_kernel(PrologParams 
       *(uint16_t*)((uint8_t*)p.q_out + ((size_t)tok * H + h) * D + 2 * lane) = (uint16_t)bytes;
     }
   }
-  // ---- k: LayerNorm over D (wave 0), bf16, quantise, append
-  if (wave != 0) return;
+  // ---- k: LayerNorm over D (workgroup 0's wave 0), bf16, quantise, append
+  if (wave != 0 || blockIdx.y != 0) return;
   const float* kv = p.k_f32 + (size_t)tok * D;
   const float a0 = kv[2 * lane], a1 = kv[2 * lane + 1];
   const float mean = wave_sum(a0 + a1) / (float)D;
@@ -224,20 +256,22 @@ __global__ __launch_bounds__(kPgThreads) void prolog_finish_kernel(PrologParams 
 }  // namespace
 
 int prolog_n_tiles(int H, int D) { return (H * D + D + H) / kPgN; }
+int prolog_d_model_unit() { return kPgDmodelUnit; }
 
 hipError_t launch_prolog(int out_dtype, const PrologParams& p, hipStream_t st) {
   if (p.total_q == 0) return hipSuccess;
-  if (p.D != 128 || (p.H % kPgN) != 0 || (p.d_model % (4 * 16 * kPgChunk)) != 0) return hipErrorInvalidValue;
+  if (p.D != 128 || (p.H % kPgN) != 0 || p.d_model <= 0 || (p.d_model % kPgDmodelUnit) != 0) return hipErrorInvalidValue;
   const dim3 g1(prolog_n_tiles(p.H, p.D), (p.total_q + kPgM - 1) / kPgM);
   hipLaunchKernelGGL(prolog_gemm_kernel, g1, dim3(kPgThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const dim3 g2(p.total_q, (p.H + 15) / 16);
   if (out_dtype == kBF16)
-    hipLaunchKernelGGL(prolog_finish_kernel<kBF16>, dim3(p.total_q), dim3(kPgThreads), 0, st, p);
+    hipLaunchKernelGGL(prolog_finish_kernel<kBF16>, g2, dim3(kFinThreads), 0, st, p);
   else if (out_dtype == kFP8)
-    hipLaunchKernelGGL(prolog_finish_kernel<kFP8>, dim3(p.total_q), dim3(kPgThreads), 0, st, p);
+    hipLaunchKernelGGL(prolog_finish_kernel<kFP8>, g2, dim3(kFinThreads), 0, st, p);
   else
-    hipLaunchKernelGGL(prolog_finish_kernel<kMX>, dim3(p.total_q), dim3(kPgThreads), 0, st, p);
+    hipLaunchKernelGGL(prolog_finish_kernel<kMX>, g2, dim3(kFinThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -139,14 +139,14 @@ def test_prolog_bf16_multi_token():
     # four new tokens per sequence over 16-token pages: keys appended at the
     # last four positions, some in a fresh page
     case = case_to(make_case("c5_decode4", 72, batch=2, seq_lens=[3001, 4100], page_size=16), "cuda")
-    call = _run_prolog(case, 512, 72)
+    call = _run_prolog(case, 1024, 72)
     _check_decode(case, call)
 
 
 def test_prolog_many_tokens_ragged():
     # 150 new tokens: three 64-token blocks, the last ragged; MXFP8 keys
     case = case_to(make_case("c4_decode_mxfp8", 73, batch=2, seq_lens=[2600, 3100], q_lens=[70, 80]), "cuda")
-    _run_prolog(case, 1536, 73)
+    _run_prolog(case, 2048, 73)
 
 
 def test_prolog_full_size_fp8():

@@ -311,23 +311,32 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
   // ceil(sum pages / (grid - B)), which always fits (each sequence's last
   // workgroup wastes less than one) and is the bound the host sizes LDS by.
   if (tid < kWave) {
-    int tot = 0;
-    for (int b0 = 0; b0 < bv.batch; b0 += kWave) {
-      const int b = b0 + lane;
-      const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) >> bv.page_shift : 0;
-      tot += wave_sum(pg);
+    // page counts of the first kPgRegs * 64 sequences stay in registers for
+    // the search below (each pass would otherwise wait on a reload)
+    constexpr int kPgRegs = 4;
+    int pgr[kPgRegs];
+#pragma unroll
+    for (int r = 0; r < kPgRegs; r++) {
+      const int b = 64 * r + lane;
+      pgr[r] = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) >> bv.page_shift : 0;
     }
+    auto pages = [&](int b0) -> int {
+      const int b = b0 + lane;
+      int v = 0;
+#pragma unroll
+      for (int r = 0; r < kPgRegs; r++) v = (b0 == 64 * r) ? pgr[r] : v;
+      if (b0 >= 64 * kPgRegs) v = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) >> bv.page_shift : 0;
+      return v;
+    };
+    int tot = 0;
+    for (int b0 = 0; b0 < bv.batch; b0 += kWave) tot += wave_sum(pages(b0));
     int cap = (tot + (p.grid - bv.batch) - 1) / (p.grid - bv.batch);
     if (tot > 0) {
       int lo = (tot + p.grid - 1) / p.grid;
       while (lo < cap) {  // uniform over the wave: every bound comes from a wave sum
         const int mid = (lo + cap) / 2;
         int wgs = 0;
-        for (int b0 = 0; b0 < bv.batch; b0 += kWave) {
-          const int b = b0 + lane;
-          const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) >> bv.page_shift : 0;
-          wgs += wave_sum((pg + mid - 1) / mid);
-        }
+        for (int b0 = 0; b0 < bv.batch; b0 += kWave) wgs += wave_sum((pages(b0) + mid - 1) / mid);
         if (wgs <= p.grid) cap = mid;
         else lo = mid + 1;
       }
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
     int acc = 0, found = 0;
     for (int b0 = 0; b0 < bv.batch && !found; b0 += kWave) {
       const int b = b0 + lane;
-      const int pg = (b < bv.batch) ? (bv.seq_lens[b] + P - 1) >> bv.page_shift : 0;
+      const int pg = pages(b0);
       const int nb = (cap > 0) ? (pg + cap - 1) / cap : 0;
       // inclusive prefix of nb over the wave
       int inc = nb;
@@ -703,6 +712,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
 
   __shared__ int s_failed;
   __shared__ uint32_t s_ticket;
+  uint32_t ticket = 0u;     // thread 0: this workgroup's exit ticket
   // ---- 3b. equal keys straddle the boundary: smallest positions win ---------
   bool any_tie = false;
   for (int q = 0; q < MAXQ; q++) any_tie |= (s_state[q] == kTiePass);
@@ -777,7 +787,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
     // One thread reserves the workgroup's slots of every query and reads the
     // sequence's failure flag; without a tie pass these are its last accesses
     // to shared workspace state, so it then takes the exit ticket (ordered
-    // after the reservations), whose latency overlaps the row writes below.
+    // after the reservations).  The ticket's value is only needed after the
+    // row writes, so it stays in a register and its latency overlaps them.
     if (tid == 0) {
       uint32_t got[MAXQ];
 #pragma unroll
@@ -793,7 +804,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
       s_failed = fl != 0u;
       if (!any_tie) {
         __builtin_amdgcn_s_waitcnt(0);
-        s_ticket = atomic_add_agent(W.seq_exit(p.seq_base + b), 1u);
+        ticket = atomic_add_agent(W.seq_exit(p.seq_base + b), 1u);
       }
     }
     __syncthreads();
@@ -888,8 +899,9 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
     if (any_tie) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (tid == 0) s_ticket = atomic_add_agent(W.seq_exit(p.seq_base + b), 1u);
+      if (tid == 0) ticket = atomic_add_agent(W.seq_exit(p.seq_base + b), 1u);
     }
+    if (tid == 0) s_ticket = ticket;
     __syncthreads();
     if (tid == 0) s_last = (s_ticket == (uint32_t)(nb - 1));
     __syncthreads();

@@ -87,34 +87,54 @@ def time_calls(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps  # ms per call
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, budget_s):
-    """The oracle as it stands, timed on this host on a bounded sample."""
+    """The oracle as it stands, timed on this host on a bounded sample: the
+    same seeded order of the workload's query tokens, with NumPy's BLAS on
+    every core and on one thread, median of three runs each."""
     import numpy as np
     import oracle
     from oracle import dsa_oracle as od
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     qs = [(b, i) for b in range(case.batch) for i in range(int(case.q_lens_host[b]))]
     # host copies of the pools are input staging, done before the clock starts
     for t in (case.k_pool, case.kv_pool, case.k_scale, case.block_table):
         if t is not None:
             od._np(t)
-    # seeded order over the workload's query tokens, repeated until the budget
-    # is spent (at least one token)
-    done, t0 = 0, time.perf_counter()
     order = np.random.default_rng(0).permutation(len(qs))
-    while True:
-        oracle.run_query(case, *qs[order[done % len(qs)]])
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} query tokens ({done / len(qs):.1f} passes over the {len(qs)} of the same "
-                      f"workload, first seed, seeded order), {el:.1f} s, float64 NumPy, "
+    per_run = budget_s / 6.0
+
+    def one_run():
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.run_query(case, *qs[order[done % len(qs)]])
+            done += 1
+            if time.perf_counter() - t0 > per_run:
+                break
+        return done, time.perf_counter() - t0
+
+    runs = {}
+    for label, limit in (("all", None), ("one", 1)):
+        with threadpool_limits(limits=limit):
+            runs[label] = [one_run() for _ in range(3)]
+    rate = {k: float(np.median([d / e for d, e in v])) for k, v in runs.items()}
+    n_all = sum(d for d, _ in runs["all"])
+    return {"value": rate["all"], "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "one_thread_value": rate["one"],
+            "cpu_model": _cpu_model(),
+            "sample": f"seeded order over the {len(qs)} query tokens of the same workload (first seed), "
+                      f"{per_run:.1f} s per run, median of 3 runs with BLAS on {threads} threads "
+                      f"({n_all} tokens in all) and of 3 on 1 thread; float64 NumPy; "
                       f"host cores available {len(os.sched_getaffinity(0))}"}
 
 
@@ -134,12 +154,17 @@ def prefill_line(torch, B, make_case, steps):
     rows = int(np.minimum(case.topk, t + 1).sum())
     pairs = int(((t + 1) * (t + 1 > case.topk)).sum())   # queries that need scores
     f_idx = 2 * case.h_i * case.d_i * pairs
+    # with no activation on the per-head scores the head sum collapses into one
+    # weighted query per token (sum_h w_h q_h, then one dot product per key):
+    # the flops a collapsed indexer would need, printed so that the per-head
+    # count is never read as required work
+    f_idx_collapsed = 2 * case.d_i * pairs + 2 * case.h_i * case.d_i * int((t + 1 > case.topk).sum())
     f_sfa = 2 * case.h_s * (case.d_qk + case.d_v) * rows
     peak = MFMA_PEAK_TFLOPS["bf16"] * 1e12
     return {"workload": "c3_prefill_bf16: one sequence, 32768 query tokens, causal, bf16, k=2048",
             "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
             "stages_ms": {"indexer_topk": ms_idx, "sparse_attn": ms_sfa},
-            "algorithmic_flops": {"indexer_per_head": f_idx, "sfa": f_sfa},
+            "algorithmic_flops": {"indexer_per_head": f_idx, "indexer_collapsed": f_idx_collapsed, "sfa": f_sfa},
             "mfma_frac": {"fused": (f_idx + f_sfa) / (ms * 1e-3) / peak,
                           "indexer": f_idx / (ms_idx * 1e-3) / peak, "sfa": f_sfa / (ms_sfa * 1e-3) / peak},
             "peak_tflops": MFMA_PEAK_TFLOPS["bf16"]}
@@ -218,6 +243,8 @@ def main():
                     help="skip the 32k causal prefill measurement")
     ap.add_argument("--no-extra", dest="extra", action="store_false",
                     help="skip the C4 and C5 measurements")
+    ap.add_argument("--only-config", default=None, choices=sorted(CONFIGS_EXTRA),
+                    help="print only this workload's fused-call measurement (--steps calls)")
     ap.add_argument("--only-prolog", action="store_true",
                     help="print only the indexer prolog measurement")
     ap.add_argument("--only-prefill", action="store_true",
@@ -236,6 +263,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     B.lib()
+    if args.only_config:
+        print(json.dumps(config_line(torch, B, make_case, args.only_config, args.steps, args.warmup,
+                                     1 if args.only_config == "c5_chunk_prefill" else 2)), flush=True)
+        return
     if args.only_prolog:
         print(json.dumps(prolog_line(torch, B, make_case, args.steps, args.warmup)), flush=True)
         return
@@ -266,7 +297,12 @@ def main():
 
     a = algorithmic(case)
     tokens = case.total_q
-    kern = {"indexer": (ms_idx, a["indexer_bytes"]), "sfa": (ms_sfa, a["sfa_bytes"])}
+    # The dominant kernel: dsa_indexer_topk is one launch of the decode
+    # indexer kernel, so back-to-back calls timed with events on the stream it
+    # runs on give that kernel's average duration (plus the inter-launch gap);
+    # dsa_sparse_attn is two launches (attention and the split combine).
+    kern = {"indexer_decode_kernel": (ms_idx, a["indexer_bytes"]),
+            "sfa_bf16_kernel+sfa_combine_kernel": (ms_sfa, a["sfa_bytes"])}
     dom = max(kern, key=lambda k: kern[k][0])
     dms, dbytes = kern[dom]
     achieved = dbytes / (dms * 1e-3) / 1e9
@@ -275,7 +311,7 @@ def main():
     if os.path.exists(prof):
         try:
             tr = json.load(open(prof))
-            ent = tr.get(args.workload, {}).get(dom)
+            ent = tr.get(args.workload, {}).get(dom.split("+")[0])
             if ent and ent.get("kernel_source_sha") == _kernel_sha():
                 traffic = ent["bytes_per_launch"]
         except Exception:
@@ -307,7 +343,8 @@ def main():
                         "sfa_flops": a["sfa_flops"]},
         "step_hbm_frac": a["fused_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dbytes, "us_per_launch": dms * 1e3},
         "mfma_frac": {
             "indexer": a["indexer_flops"] / (ms_idx * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[case.idx_dtype],
             "sfa": a["sfa_flops"] / (ms_sfa * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[case.sfa_dtype],

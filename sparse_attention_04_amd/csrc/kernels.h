@@ -74,14 +74,16 @@ struct PrologParams {
   void* q_out;             // fp8 / mx: [total_q][H][D] e4m3 bytes
   void* q_scale_out;       // fp8: f32 [total_q][H]; mx: u8 [total_q][H][D/32]
   float* w_out;            // [total_q][H]
-  float* k_f32;            // [total_q][D] projected keys before normalisation (workspace)
+  float* kw_part;          // [n_parts][total_q][D + H] partial sums of the k and w columns (workspace)
+  int32_t n_parts;         // set by the launcher
+  int32_t split_extra;     // set by the launcher: k / w tiles split by chunk over the q workgroups
   void* k_bf16_out;        // optional [total_q][D] bf16 normalised keys
   void* k_data;            // paged K cache [num_pages][P][D] (written at the new tokens' rows)
   void* k_scale;           // its scales (fp8: f32 [num_pages][P]; mx: u8 [num_pages][P][D/32])
 };
 
-int prolog_n_tiles(int H, int D);
 int prolog_d_model_unit();
+int prolog_n_parts(int total_q, int d_model);
 hipError_t launch_prolog(int out_dtype, const PrologParams& p, hipStream_t st);
 
 // ------------------------------------------------------------------- SFA ---

@@ -15,14 +15,13 @@
 // workgroup per token, quantises q per (token, head) or per 32-group,
 // normalises and quantises k and writes it into the cache.
 //
-//   prolog_gemm_kernel: out[t][c] = sum_k x[t][k] W[c][k] over d_model; eight
-//     waves split d_model and their partial tiles are summed in LDS in a fixed
-//     order (deterministic).  q columns are rounded to bf16, k and w stay
-//     float32.  32x32x16 bf16 MFMAs: x rows on M (tokens, 64 per workgroup),
-//     weight rows on N (32 columns per workgroup).  For decode (tens of tokens)
-//     the launch is bound by the weight stream (d_model x 8384 bf16).
-//   prolog_finish_kernel: quantise q; LayerNorm k in float32, round to bf16,
-//     quantise, append at t = L_b - T_b + i through the block table.
+//   prolog_gemm_kernel: out[t][c] = sum_k x[t][k] W[c][k] over d_model, the
+//     weights staged through LDS (see the kernel); q columns are rounded to
+//     bf16, k and w stay float32.  For decode (tens of tokens) the launch is
+//     bound by the weight stream (d_model x 8384 bf16).
+//   prolog_finish_kernel: quantise q; add up the k and w partials; LayerNorm k
+//     in float32, round to bf16, quantise, append at t = L_b - T_b + i through
+//     the block table.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,12 +29,18 @@ namespace dsa {
 
 namespace {
 
-constexpr int kPgWaves = 8;
-constexpr int kPgThreads = 64 * kPgWaves;
-constexpr int kPgM = 64;            // tokens per workgroup (two 32-row M-tiles)
-constexpr int kPgN = 32;            // weight rows (output columns) per workgroup
-constexpr int kPgChunk = 8;         // K-steps of 16 loaded together
-constexpr int kPgDmodelUnit = kPgWaves * 16 * kPgChunk;   // d_model granularity (1024)
+constexpr int kPgThreads = 256;    // 4 waves
+constexpr int kPgM = 64;            // tokens per workgroup (each wave: 16)
+constexpr int kPgN = 32;            // weight rows (output columns) per tile
+constexpr int kPgKC = 256;          // d_model elements per staged chunk
+constexpr int kPgRowB = kPgKC * 2;  // bytes of one row's chunk (512)
+constexpr int kPgRows = kPgN + kPgM;                    // weight rows, then token rows
+constexpr int kPgChunkB = kPgRows * kPgRowB;            // 48 KiB per chunk
+constexpr int kPgLoads = kPgChunkB / 1024;              // 1-KiB loads per chunk (48)
+constexpr int kPgLPW = kPgLoads / 4;                    // per wave (12)
+constexpr int kPgNBuf = 3;                              // chunks in the LDS ring
+constexpr int kPgDmodelUnit = kPgKC;
+static_assert(kPgLoads % 4 == 0 && kPgRowB * 2 == 1024, "two rows per 1-KiB load");
 
 __device__ __forceinline__ int find_seq_pg(const BatchView& bv, int tok) {
   int lo = 0, hi = bv.batch - 1;
@@ -46,8 +51,16 @@ __device__ __forceinline__ int find_seq_pg(const BatchView& bv, int tok) {
   return lo;
 }
 
-// Column tile -> (matrix, first row of that matrix).  Matrices: 0 = W_q
-// (H*D rows), 1 = W_k (D rows), 2 = W_w (H rows); all are multiples of 32.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+#define DSA_PG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// Tile t of the concatenated weight rows [W_q | W_k | W_w] (all multiples of
+// 32 rows): its matrix (0 q, 1 k, 2 w) and first row in that matrix.
 __device__ __forceinline__ void tile_of(const PrologParams& p, int tile, int& mat, int& row0) {
   const int nq = p.H * p.D / kPgN, nk = p.D / kPgN;
   if (tile < nq) { mat = 0; row0 = tile * kPgN; }
@@ -55,110 +68,128 @@ __device__ __forceinline__ void tile_of(const PrologParams& p, int tile, int& ma
   else { mat = 2; row0 = (tile - nq - nk) * kPgN; }
 }
 
-// Eight waves split d_model; each streams its slice in chunks of 8 K-steps
-// through two register buffers used alternately (unrolled by two, so the next
-// chunk's loads stay in flight while the current chunk's MFMAs run, with no
-// register copies that would wait for them).
-__global__ __launch_bounds__(kPgThreads) void prolog_gemm_kernel(PrologParams p) {
-  __shared__ __attribute__((aligned(16))) float part[4][2][16][64];   // [wave % 4][mt][i][lane]
+// out[t][c] = sum_k x[t][k] W[c][k].  A workgroup computes 64 tokens x 32
+// weight rows; wave w owns tokens 16w .. 16w + 15 with 16x16x32 bf16 MFMAs
+// (two 16-column N-tiles), so no partial sums cross waves.  d_model streams in
+// chunks of 256 elements through a 3-deep LDS ring: 48 one-KiB direct
+// global->LDS loads per chunk (two rows each, fully coalesced), rows of 512
+// bytes whose 16-byte pieces are XOR-swizzled by row (piece c of row r sits in
+// slot c ^ (r % 32)), so the operand reads of 16 rows hit 16 distinct bank
+// groups.
+//
+// Jobs: the workgroup's main tile over every chunk, then (decode launches, a
+// single token block) its share of slices: the K and head-weight tiles split
+// by chunk over the workgroups, so the grid is exactly the q tiles and one
+// round of workgroups covers it.  Their partial sums go to part[chunk] and the
+// finish kernel adds them in chunk order.  Launches with several token blocks
+// (many workgroups anyway) give every tile, K and head-weight ones included,
+// a workgroup of its own (part[0]).
+__global__ __launch_bounds__(kPgThreads, 1) void prolog_gemm_kernel(PrologParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char pg_smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int mat, row0;
-  tile_of(p, blockIdx.x, mat, row0);
-  const uint16_t* W = (const uint16_t*)(mat == 0 ? p.w_q : mat == 1 ? p.w_k : p.w_w);
   const int m0 = blockIdx.y * kPgM;
   const int dm = p.d_model;
-  const int kw = dm / kPgWaves;                       // this wave's slice of d_model
-  const int kbeg = wave * kw;
-  // lane l: A rows (tokens) m0 + 32 mt + l%32, B row (column) row0 + l%32;
-  // K elements 8 (l/32) .. +7 of each 16-wide step
-  const int t0 = min(m0 + (lane & 31), p.total_q - 1);
-  const int t1 = min(m0 + 32 + (lane & 31), p.total_q - 1);
-  const int koff = kbeg + 8 * (lane >> 5);
-  const u32x4* xa0 = (const u32x4*)((const uint16_t*)p.x + (size_t)t0 * dm + koff);
-  const u32x4* xa1 = (const u32x4*)((const uint16_t*)p.x + (size_t)t1 * dm + koff);
-  const u32x4* wb = (const u32x4*)(W + (size_t)(row0 + (lane & 31)) * dm + koff);
-  f32x16 acc0, acc1;
-#pragma unroll
-  for (int i = 0; i < 16; i++) { acc0[i] = 0.f; acc1[i] = 0.f; }
-  struct Buf { u32x4 a0[kPgChunk], a1[kPgChunk], b[kPgChunk]; };
-  // a step is 16 elements = 2 u32x4 apart in each row
-  auto load = [&](int c, Buf& f) {
-#pragma unroll
-    for (int s = 0; s < kPgChunk; s++) {
-      const int st = c * kPgChunk + s;
-      f.a0[s] = xa0[2 * st];
-      f.a1[s] = xa1[2 * st];
-      f.b[s] = wb[2 * st];
+  const int nch = dm / kPgKC;
+  const int nq_tiles = p.H * p.D / kPgN, nx_tiles = (p.D + p.H) / kPgN;
+  const bool split = p.split_extra != 0;
+  const int nmain = nch;
+  int nextra = 0;
+  if (split)
+    for (int e = blockIdx.x; e < nx_tiles * nch; e += nq_tiles) nextra++;
+  const int njobs = nmain + nextra;
+  int main_mat, main_row0;
+  tile_of(p, blockIdx.x, main_mat, main_row0);
+
+  // job -> (weight matrix, first row, chunk)
+  auto job = [&](int j, int& mat, int& row0, int& c) {
+    if (j < nmain) {
+      mat = main_mat; row0 = main_row0; c = j;
+    } else {
+      const int e = blockIdx.x + (j - nmain) * nq_tiles;
+      tile_of(p, nq_tiles + e / nch, mat, row0);
+      c = e % nch;
     }
   };
-  auto mma = [&](const Buf& f) {
+  const uint32_t ring = lds_addr(pg_smem);
+  auto issue = [&](int j) {
+    int mat, row0, c;
+    job(j, mat, row0, c);
+    const uint16_t* W = (const uint16_t*)(mat == 0 ? p.w_q : mat == 1 ? p.w_k : p.w_w);
+    const uint32_t buf = ring + (uint32_t)(j % kPgNBuf) * kPgChunkB;
 #pragma unroll
-    for (int s = 0; s < kPgChunk; s++) {
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, f.b[s]);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a0[s]), bv, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a1[s]), bv, acc1, 0, 0, 0);
+    for (int k = 0; k < kPgLPW; k++) {
+      const int ins = wave + 4 * k;
+      const int R = 2 * ins + (lane >> 5);
+      const int piece = (lane & 31) ^ (R & 31);
+      const uint16_t* src = (R < kPgN)
+          ? W + (size_t)(row0 + R) * dm
+          : (const uint16_t*)p.x + (size_t)min(m0 + R - kPgN, p.total_q - 1) * dm;
+      dma16(src + c * kPgKC + piece * 8, __builtin_amdgcn_readfirstlane(buf + ins * 1024u));
     }
   };
-  const int nchunks = kw / (16 * kPgChunk);
-  Buf f0, f1;
-  load(0, f0);
-  if (nchunks > 1) load(1, f1);
-  for (int c = 0; c < nchunks; c += 2) {
-    mma(f0);
-    if (c + 2 < nchunks) load(c + 2, f0);
-    if (c + 1 < nchunks) {
-      mma(f1);
-      if (c + 3 < nchunks) load(c + 3, f1);
-    }
-  }
-  // sum the eight waves' tiles in a fixed order: waves 4..7 into 0..3, then
-  // the four
-  if (wave >= 4) {
+  issue(0);
+  if (njobs > 1) issue(1);
+
+  const int g16 = lane >> 4, l16 = lane & 15;
+  f32x4 acc[2], acce[2];
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      part[wave - 4][0][i][lane] = acc0[i];
-      part[wave - 4][1][i][lane] = acc1[i];
-    }
+  for (int n = 0; n < 2; n++) {
+    acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acce[n] = acc[n];
   }
-  __syncthreads();
-  if (wave < 4) {
+  for (int j = 0; j < njobs; j++) {
+    if (j + 1 < njobs) DSA_PG_WAIT_VMCNT(kPgLPW); else DSA_PG_WAIT_VMCNT(0);
+    // every wave's loads of job j have landed, and every wave is done with the
+    // buffer of job j - 1, which job j + 2 refills
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (j + 2 < njobs) issue(j + 2);
+    const unsigned char* buf = pg_smem + (size_t)(j % kPgNBuf) * kPgChunkB;
+    const bool is_main = j < nmain;
+    if (!is_main) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      acc0[i] += part[wave][0][i][lane];
-      acc1[i] += part[wave][1][i][lane];
+      for (int n = 0; n < 2; n++) acce[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  }
-  __syncthreads();
-  if (wave < 4) {
+    // A: token row kPgN + 16 wave + l16; B: weight rows l16 and 16 + l16;
+    // K-step ks takes pieces 4 ks + g16 (8 elements each)
+    const int ra = kPgN + 16 * wave + l16;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      part[wave][0][i][lane] = acc0[i];
-      part[wave][1][i][lane] = acc1[i];
+    for (int ks = 0; ks < kPgKC / 32; ks++) {
+      const int pc = 4 * ks + g16;
+      const bf16x8 a = *(const bf16x8*)(buf + ra * kPgRowB + ((pc ^ (ra & 31)) * 16));
+      const bf16x8 b0 = *(const bf16x8*)(buf + l16 * kPgRowB + ((pc ^ l16) * 16));
+      const bf16x8 b1 = *(const bf16x8*)(buf + (16 + l16) * kPgRowB + ((pc ^ (16 + l16)) * 16));
+      if (is_main) {
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[1], 0, 0, 0);
+      } else {
+        acce[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acce[0], 0, 0, 0);
+        acce[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acce[1], 0, 0, 0);
+      }
     }
-  }
-  __syncthreads();
-  // thread t: token m0 + t/8, columns 4 (t%8) .. +3 of the tile.  C layout of
-  // a 32x32 tile: lane l holds column l%32 and rows 8 (i/4) + 4 (l/32) + i%4.
-  const int tl = tid >> 3, cg = tid & 7;
-  const int tok = m0 + tl;
-  if (tok >= p.total_q) return;
-  const int mt = tl >> 5, r = tl & 31;
-  const int ii = (r >> 3) * 4 + (r & 3), lh = (r >> 2) & 1;
-  float v[4];
+    // C layout of a 16x16 tile: lane l holds column l % 16 and rows
+    // 4 (l / 16) + i.  Tokens past total_q are not written.
+    const bool last_main = (j == nmain - 1);
+    if (!last_main && is_main) continue;
+    int mat, row0, c;
+    job(j, mat, row0, c);
+    f32x4 v[2];
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int ln = lh * 32 + 4 * cg + j;
-    v[j] = ((part[0][mt][ii][ln] + part[1][mt][ii][ln]) + part[2][mt][ii][ln]) + part[3][mt][ii][ln];
-  }
-  const int col = row0 + 4 * cg;
-  if (mat == 0) {
-    uint2 pk;
-    pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    *(uint2*)((uint16_t*)p.q_bf16 + (size_t)tok * p.H * p.D + col) = pk;
-  } else {
-    float* dst = (mat == 1) ? p.k_f32 + (size_t)tok * p.D + col : p.w_out + (size_t)tok * p.H + col;
-    *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
+    for (int n = 0; n < 2; n++) v[n] = is_main ? acc[n] : acce[n];
+#pragma unroll
+    for (int n = 0; n < 2; n++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int tok = m0 + 16 * wave + 4 * g16 + i;
+        if (tok >= p.total_q) continue;
+        const int col = row0 + 16 * n + l16;
+        if (mat == 0) {
+          ((uint16_t*)p.q_bf16)[(size_t)tok * p.H * p.D + col] = f32_to_bf16(v[n][i]);
+        } else {
+          const int kc = (mat == 1) ? col : p.D + col;     // column of [k | w]
+          const int part = is_main ? 0 : c;
+          p.kw_part[((size_t)part * p.total_q + tok) * (p.D + p.H) + kc] = v[n][i];
+        }
+      }
   }
 }
 
@@ -213,10 +244,46 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
       *(uint16_t*)((uint8_t*)p.q_out + ((size_t)tok * H + h) * D + 2 * lane) = (uint16_t)bytes;
     }
   }
-  // ---- k: LayerNorm over D (workgroup 0's wave 0), bf16, quantise, append
-  if (wave != 0 || blockIdx.y != 0) return;
-  const float* kv = p.k_f32 + (size_t)tok * D;
-  const float a0 = kv[2 * lane], a1 = kv[2 * lane + 1];
+  if (blockIdx.y != 0) return;
+  // ---- k and w: the sums of their partials.  Thread t adds parts
+  // c = t / 128 (mod 2) of k column t % 128, and parts c = t / 64 (mod 4) of w
+  // column t % 64 (loads unrolled); the sub-sums then meet in LDS in a fixed
+  // order.
+  __shared__ float s_k[2][128], s_w[4][64];
+  const int KW = D + H;
+  const float* pk = p.kw_part + (size_t)tok * KW;
+  const size_t pstride = (size_t)p.total_q * KW;
+  {
+    const int kc = tid & 127, kh = tid >> 7;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int c = kh, u = 0;
+#pragma unroll 4
+    for (; c < p.n_parts; c += 2, u = (u + 1) & 3) acc[u] += pk[c * pstride + kc];
+    s_k[kh][kc] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if (H <= 64) {
+      const int wc = tid & 63, wh = tid >> 6;
+      float aw[4] = {0.f, 0.f, 0.f, 0.f};
+      int cw = wh, uw = 0;
+      const bool has = wc < H;
+#pragma unroll 4
+      for (; cw < p.n_parts; cw += 4, uw = (uw + 1) & 3) aw[uw] += has ? pk[cw * pstride + D + wc] : 0.f;
+      s_w[wh][wc] = (aw[0] + aw[1]) + (aw[2] + aw[3]);
+    }
+  }
+  __syncthreads();
+  if (H <= 64) {
+    if (tid < H) p.w_out[(size_t)tok * H + tid] = (s_w[0][tid] + s_w[1][tid]) + (s_w[2][tid] + s_w[3][tid]);
+  } else if (wave == 1) {
+    for (int h = lane; h < H; h += 64) {
+      float acc = 0.f;
+      for (int c = 0; c < p.n_parts; c++) acc += pk[c * pstride + D + h];
+      p.w_out[(size_t)tok * H + h] = acc;
+    }
+  }
+  if (wave != 0) return;
+  // ---- k: LayerNorm over D (wave 0), bf16, quantise, append
+  const float a0 = s_k[0][2 * lane] + s_k[1][2 * lane];
+  const float a1 = s_k[0][2 * lane + 1] + s_k[1][2 * lane + 1];
   const float mean = wave_sum(a0 + a1) / (float)D;
   const float d0 = a0 - mean, d1 = a1 - mean;
   const float var = wave_sum(d0 * d0 + d1 * d1) / (float)D;
@@ -255,15 +322,27 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
 
 }  // namespace
 
-int prolog_n_tiles(int H, int D) { return (H * D + D + H) / kPgN; }
 int prolog_d_model_unit() { return kPgDmodelUnit; }
 
-hipError_t launch_prolog(int out_dtype, const PrologParams& p, hipStream_t st) {
-  if (p.total_q == 0) return hipSuccess;
-  if (p.D != 128 || (p.H % kPgN) != 0 || p.d_model <= 0 || (p.d_model % kPgDmodelUnit) != 0) return hipErrorInvalidValue;
-  const dim3 g1(prolog_n_tiles(p.H, p.D), (p.total_q + kPgM - 1) / kPgM);
-  hipLaunchKernelGGL(prolog_gemm_kernel, g1, dim3(kPgThreads), 0, st, p);
-  hipError_t e = hipGetLastError();
+// Partial-sum slots of the K / head-weight columns a launch needs.
+int prolog_n_parts(int total_q, int d_model) {
+  return (total_q <= kPgM) ? d_model / kPgKC : 1;
+}
+
+hipError_t launch_prolog(int out_dtype, const PrologParams& p0, hipStream_t st) {
+  if (p0.total_q == 0) return hipSuccess;
+  if (p0.D != 128 || (p0.H % kPgN) != 0 || p0.d_model <= 0 || (p0.d_model % kPgDmodelUnit) != 0)
+    return hipErrorInvalidValue;
+  PrologParams p = p0;
+  const int mblocks = (p.total_q + kPgM - 1) / kPgM;
+  p.split_extra = (mblocks == 1) ? 1 : 0;
+  p.n_parts = prolog_n_parts(p.total_q, p.d_model);
+  const int ntiles = p.H * p.D / kPgN + (p.split_extra ? 0 : (p.D + p.H) / kPgN);
+  const size_t lds = (size_t)kPgNBuf * kPgChunkB;
+  hipError_t e = hipFuncSetAttribute((const void*)prolog_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prolog_gemm_kernel, dim3(ntiles, mblocks), dim3(kPgThreads), lds, st, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g2(p.total_q, (p.H + 15) / 16);
   if (out_dtype == kBF16)

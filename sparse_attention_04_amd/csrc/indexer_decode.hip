@@ -275,12 +275,19 @@ __device__ __forceinline__ int block_rank(bool pred, int* scratch, int& total) {
 enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3 };
 
 // Phase timestamps of workgroup 0 (100 MHz real-time counter) in header words
-// 16.. of the workspace, for profiling the phases of one launch.
+// 16.. of the workspace, for profiling the phases of one launch; compiled in
+// only with DSA_INDEXER_STAMPS (each costs workgroup 0 a scalar-memory wait).
+#ifdef DSA_INDEXER_STAMPS
 #define DSA_STAMP(i)                                                                          \
   do {                                                                                        \
     if (blockIdx.x == 0 && threadIdx.x == 0 && (i) < 24)                                      \
       ((unsigned long long*)(W.base + 16))[(i)] = __builtin_amdgcn_s_memrealtime();            \
   } while (0)
+#else
+#define DSA_STAMP(i) \
+  do {               \
+  } while (0)
+#endif
 
 template <int DT, int H, int D, int MAXQ>
 __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerDecodeParams p) {

@@ -217,7 +217,14 @@ dsa_status dsa_fused_decode(const dsa_batch* batch, const dsa_indexer_args* iarg
 /* Causal (chunked) prefill (large T_b): query blocks of q_block tokens are
  * paired from the two ends of each sequence (zigzag) so that every workgroup
  * gets one short-history and one long-history block; results are written back
- * to their original rows.  q_block must be 64.  idx_out may be NULL.          */
+ * to their original rows.  q_block must be 64.  idx_out may be NULL.
+ * The zigzag pairing is the load balancing of causal prefill described in
+ * "Adapting and Optimizing Inference for a New Model Architecture on Ascend",
+ * section 5.2, and in "Day0 Inference Optimization on Ascend CANN: A Deep
+ * Dive into Hybrid Architecture Acceleration", section 4 (its zigzag layout),
+ * where it balances devices; here it balances workgroups of one GPU.  The
+ * indexer scores and selection follow the same pages' section 2 (indexer)
+ * and the sparse attention their section 3.1, as for dsa_fused_decode.       */
 dsa_status dsa_fused_prefill(const dsa_batch* batch, const dsa_indexer_args* iargs,
                              const dsa_sfa_args* sargs, int32_t q_block, void* out,
                              float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,

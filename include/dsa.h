@@ -24,11 +24,16 @@
  *     with dsa_workspace_size().  One workspace must not be used by two calls
  *     that may run concurrently.
  *   Workspace state: a workspace must be zero-filled before its first use
- *     (hipMemsetAsync, or allocate it zeroed).  Every call that is enqueued
- *     leaves the parts it relies on zero again when its kernels finish, so the
- *     same workspace serves any later call of any shape without being cleared
- *     (the decode indexer keeps its cross-workgroup counters and histograms
- *     there and clears them itself, which saves a fill launch per call).
+ *     (hipMemsetAsync, or allocate it zeroed).  The decode indexer keeps its
+ *     cross-workgroup counters and histograms at the START of the workspace
+ *     and every call leaves them zero again when its kernels finish (which
+ *     saves a fill launch per call); scratch (index rows, attention partials)
+ *     is placed at the END of the workspace and left as it is.  So one
+ *     workspace serves later calls of other shapes without being cleared,
+ *     provided it holds the largest state and the largest scratch among them
+ *     at once: sizing it with dsa_workspace_size() for a call whose batch,
+ *     query-token count and topk are each at least those of every call that
+ *     shares it is enough.
  *   Alignment: the workspace and the q, k_cache / kv_cache data and output
  *     arrays are 16-byte aligned (the kernels move them 16 bytes at a time);
  *     scale pools, head weights, lse, index rows, lengths and block tables
@@ -235,8 +240,10 @@ dsa_status dsa_fused_prefill(const dsa_batch* batch, const dsa_indexer_args* iar
  * allocation).  Same arguments, results and errors as dsa_fused_decode; the
  * scratch memory is a static array of dsa_noalloc_scratch_bytes() (64 MiB)
  * that every GPU the library runs on holds until the process ends, looked up
- * once per device.  A call whose dsa_workspace_size(DSA_OP_FUSED_DECODE, ...)
- * exceeds it returns DSA_ERR_UNSUPPORTED and enqueues nothing.  The first
+ * once per device.  Its first 16 MiB hold the zero state, the rest the
+ * scratch, so calls of any shapes may follow each other; a call whose state
+ * or scratch (together dsa_workspace_size(DSA_OP_FUSED_DECODE, ...)) exceeds
+ * its part returns DSA_ERR_UNSUPPORTED and enqueues nothing.  The first
  * call on a device also enqueues one clear of the array.  All calls on one
  * GPU share its array: calls that may overlap on the same GPU (other streams,
  * other host threads) race and must be ordered by the caller.               */

@@ -203,12 +203,14 @@ class Call:
         self._ws = {}
 
     def workspace(self, op):
-        """The call's workspace: zero-filled when allocated, as the ABI asks of
-        a workspace before its first use (calls leave it ready for the next)."""
+        """The call's workspace and its size in bytes (which the calls pass on:
+        the library keeps scratch at the end of the buffer it is given).
+        Zero-filled when allocated, as the ABI asks of a workspace before its
+        first use (calls leave it ready for the next)."""
         n = dsa_workspace_size(op, self.batch, self.iargs, self.sargs)
         if op not in self._ws or self._ws[op].numel() < n:
             self._ws[op] = torch.zeros(max(n, 1), dtype=torch.uint8, device=self.case.q_s.device)
-        return self._ws[op], n
+        return self._ws[op], self._ws[op].numel()
 
     def use_workspace(self, op, ws):
         """Run `op` with a caller-supplied (zero-filled before first use) workspace."""

@@ -11,6 +11,10 @@ dsa_status fused_decode_impl(const dsa_batch* b, const dsa_indexer_args* ia, con
                              void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                              void* stream, bool validate_only);
 
+// Bytes at the start of a dsa_fused_decode workspace that hold its zero state
+// (the rest of what dsa_workspace_size reports is scratch, kept at the end).
+size_t fused_decode_state_bytes(const dsa_batch* b);
+
 // Record `msg` as the thread's last error and return `st`; clear it.
 dsa_status set_error(dsa_status st, const char* msg);
 void clear_error();

@@ -377,6 +377,18 @@ dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx
   return DSA_OK;
 }
 
+// Workspace layout.  The zero state (the decode indexer's cross-workgroup
+// counters and histograms, left zero by every call) sits at the start of the
+// workspace and the scratch (index rows, attention partials) at its end, so a
+// workspace shared by calls of different shapes never finds one call's scratch
+// where another keeps its state (it needs room for the largest state and the
+// largest scratch at once).  kLayoutSlack covers aligning the scratch down.
+constexpr size_t kLayoutSlack = 256;
+unsigned char* scratch_at_end(void* ws, size_t ws_bytes, size_t scratch_bytes) {
+  const uintptr_t end = ((uintptr_t)ws + ws_bytes) & ~(uintptr_t)255;
+  return (unsigned char*)(end - scratch_bytes);
+}
+
 size_t sfa_bytes(const dsa_batch* b, const dsa_sfa_args* a, int topk) {
   const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, a->q_dtype == DSA_BF16,
                              a->kv_cache && a->kv_cache->dtype == DSA_FP8_E4M3_TILE128);
@@ -407,11 +419,16 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* b, const dsa_indexer_args
     case DSA_OP_INDEXER_TOPK:
       return indexer_bytes(b);
     case DSA_OP_SPARSE_ATTN:
-      return sa ? sfa_bytes(b, sa, topk) : 0;
+      return sa ? sfa_bytes(b, sa, topk) + kLayoutSlack : 0;
     case DSA_OP_FUSED_DECODE:
-    case DSA_OP_FUSED_PREFILL:
+      // zero state | ... | index rows, attention partials
       if (!ia || !sa) return 0;
-      return indexer_bytes(b) + align_up((size_t)b->total_q * std::max(1, topk) * 4, 256) + sfa_bytes(b, sa, topk);
+      return indexer_bytes(b) + align_up((size_t)b->total_q * std::max(1, topk) * 4, 256) + sfa_bytes(b, sa, topk) +
+             kLayoutSlack;
+    case DSA_OP_FUSED_PREFILL:
+      // scratch only (the prefill indexer keeps no state)
+      if (!ia || !sa) return 0;
+      return align_up((size_t)b->total_q * std::max(1, topk) * 4, 256) + sfa_bytes(b, sa, topk) + kLayoutSlack;
     default:
       return 0;
   }
@@ -440,9 +457,9 @@ dsa_status dsa_sparse_attn(const dsa_batch* b, const dsa_sfa_args* a, const int3
   if (!aligned(idx, 4) || !aligned(out, 16) || !aligned(lse, 4) || !aligned(ws, 16))
     return fail(DSA_ERR_INVALID_ARG, "out and ws must be 16-byte, idx and lse 4-byte aligned");
   if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", topk);
-  const size_t need = sfa_bytes(b, a, topk);
+  const size_t need = sfa_bytes(b, a, topk) + kLayoutSlack;
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
-  return run_sfa(b, a, idx, topk, out, lse, (unsigned char*)ws, (hipStream_t)stream);
+  return run_sfa(b, a, idx, topk, out, lse, scratch_at_end(ws, ws_bytes, sfa_bytes(b, a, topk)), (hipStream_t)stream);
 }
 
 dsa_status dsa_fused_decode(const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa,
@@ -471,14 +488,16 @@ dsa_status fused_decode_impl(const dsa_batch* b, const dsa_indexer_args* ia, con
   if (validate_only) return DSA_OK;
   const size_t need = dsa_workspace_size(DSA_OP_FUSED_DECODE, b, ia, sa);
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
-  unsigned char* w = (unsigned char*)ws;
-  const size_t ib = indexer_bytes(b);
-  int32_t* idx = idx_out ? idx_out : (int32_t*)(w + ib);
+  const size_t rows = align_up((size_t)b->total_q * ia->topk * 4, 256);
+  unsigned char* scr = scratch_at_end(ws, ws_bytes, rows + sfa_bytes(b, sa, ia->topk));
+  int32_t* idx = idx_out ? idx_out : (int32_t*)scr;
   hipStream_t st = (hipStream_t)stream;
-  s = run_indexer(b, ia, idx, (uint32_t*)w, st);
+  s = run_indexer(b, ia, idx, (uint32_t*)ws, st);
   if (s != DSA_OK) return s;
-  return run_sfa(b, sa, idx, ia->topk, out, lse, w + ib + align_up((size_t)b->total_q * ia->topk * 4, 256), st);
+  return run_sfa(b, sa, idx, ia->topk, out, lse, scr + rows, st);
 }
+
+size_t fused_decode_state_bytes(const dsa_batch* b) { return indexer_bytes(b); }
 
 dsa_status set_error(dsa_status st, const char* msg) { return fail(st, "%s", msg); }
 void clear_error() { g_err.clear(); }
@@ -568,13 +587,13 @@ dsa_status dsa_fused_prefill(const dsa_batch* b, const dsa_indexer_args* ia, con
     return fail(DSA_ERR_INVALID_ARG, "k_cache and kv_cache must share the page size (one block table)");
   const size_t need = dsa_workspace_size(DSA_OP_FUSED_PREFILL, b, ia, sa);
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
-  unsigned char* w = (unsigned char*)ws;
-  const size_t ib = indexer_bytes(b);
-  int32_t* idx = idx_out ? idx_out : (int32_t*)(w + ib);
+  const size_t rows = align_up((size_t)b->total_q * ia->topk * 4, 256);
+  unsigned char* scr = scratch_at_end(ws, ws_bytes, rows + sfa_bytes(b, sa, ia->topk));
+  int32_t* idx = idx_out ? idx_out : (int32_t*)scr;
   hipStream_t st = (hipStream_t)stream;
   s = run_indexer_prefill(b, ia, idx, st);
   if (s != DSA_OK) return s;
-  return run_sfa(b, sa, idx, ia->topk, out, lse, w + ib + align_up((size_t)b->total_q * ia->topk * 4, 256), st);
+  return run_sfa(b, sa, idx, ia->topk, out, lse, scr + rows, st);
 }
 
 }  // extern "C"

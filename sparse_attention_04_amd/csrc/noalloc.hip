@@ -26,6 +26,11 @@ namespace dsa {
 namespace {
 
 constexpr size_t kScratchBytes = size_t(64) << 20;   // 64 MiB per GPU
+// The first 16 MiB hold the decode indexer's zero state, the rest the index
+// rows and attention partials (placed at the array's end): a call whose state
+// or scratch exceeds its part is refused, so no call ever finds another call's
+// scratch where it keeps its state, whatever the order of their shapes.
+constexpr size_t kStateBytes = size_t(16) << 20;
 constexpr int kMaxDevices = 64;
 
 __device__ __align__(256) unsigned char scratch[kScratchBytes];
@@ -80,10 +85,11 @@ dsa_status dsa_fused_decode_noalloc(const dsa_batch* b, const dsa_indexer_args* 
   dsa_status s = dsa::fused_decode_impl(b, ia, sa, out, lse, idx_out, nullptr, 0, stream, true);
   if (s != DSA_OK) return s;
   const size_t need = dsa_workspace_size(DSA_OP_FUSED_DECODE, b, ia, sa);
-  if (need > dsa::kScratchBytes) {
-    char msg[200];
-    snprintf(msg, sizeof msg, "this call needs %zu bytes of scratch; the static scratch holds %zu", need,
-             dsa::kScratchBytes);
+  const size_t state = dsa::fused_decode_state_bytes(b);
+  if (state > dsa::kStateBytes || need - state > dsa::kScratchBytes - dsa::kStateBytes) {
+    char msg[240];
+    snprintf(msg, sizeof msg, "this call needs %zu bytes of state and %zu of scratch; the static scratch holds %zu and %zu",
+             state, need - state, dsa::kStateBytes, dsa::kScratchBytes - dsa::kStateBytes);
     return dsa::set_error(DSA_ERR_UNSUPPORTED, msg);
   }
   void* ws = nullptr;

@@ -233,11 +233,24 @@ __global__ __launch_bounds__(64 * NWV, 1) void sfa_bf16_kernel(SfaParams p) {
   const int nslots = max(0, min(p.topk - slot0, p.rows_per_split));
   const int32_t* idx = p.idx + (size_t)g * p.topk + slot0;
 
+  // q^T as the B operand of S^T = KV q^T (16x16x32): for head group ht, lane l
+  // holds head head0 + 16*ht and dims 32*k + 8*(l/16) .. +7 of K-step k.  The
+  // workgroup's 16 * NW * HG heads start at 16 * NW * HG * blockIdx.y; wave w
+  // holds HG groups of 16.  Loaded first, so that their latency overlaps the
+  // row lookups.
+  const int head0 = 16 * NW * HG * blockIdx.y + 16 * HG * wave + l16;
+  bf16x8 qb[HG][KS];
+#pragma unroll
+  for (int ht = 0; ht < HG; ht++) {
+    const bf16x8* qs = (const bf16x8*)((const uint16_t*)p.q + ((size_t)g * H + head0 + 16 * ht) * DQK);
+#pragma unroll
+    for (int k = 0; k < KS; k++) qb[ht][k] = qs[4 * k + grp];
+  }
   for (int r = tid; r < nslots; r += NT) {
     const int pos = idx[r];
     s_rows[r] = (pos >= 0) ? (bt[pos >> bv.page_shift] << bv.page_shift) + (pos & (P - 1)) : -1;
   }
-  __syncthreads();
+  lds_barrier();
   int fallback = -1;
   for (int r = 0; r < nslots && fallback < 0; r++) fallback = s_rows[r];
   const int ntiles = (fallback >= 0) ? (nslots + TR - 1) / TR : 0;
@@ -349,25 +362,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void sfa_bf16_kernel(SfaParams p) {
       }
     }
   };
-  // the first tiles' loads overlap the q load below
+  // the first tiles' loads
   if constexpr (KV8) {
     for (int t = 0; t < NBUF && t < ntiles; t++) issue8(t);
   } else {
     for (int t = 0; t < NBUF - 1 && t < ntiles; t++) issue(t);
   }
 
-  // q^T as the B operand of S^T = KV q^T (16x16x32): for head group ht, lane l
-  // holds head 32*wave + 16*ht + l%16 and dims 32*k + 8*(l/16) .. +7 of K-step k.
-  // heads of this workgroup: 64 * HG starting at 64 * HG * blockIdx.y; wave w
-  // holds HG groups of 16
-  const int head0 = 16 * NW * HG * blockIdx.y + 16 * HG * wave + l16;
-  bf16x8 qb[HG][KS];
-#pragma unroll
-  for (int ht = 0; ht < HG; ht++) {
-    const bf16x8* qs = (const bf16x8*)((const uint16_t*)p.q + ((size_t)g * H + head0 + 16 * ht) * DQK);
-#pragma unroll
-    for (int k = 0; k < KS; k++) qb[ht][k] = qs[4 * k + grp];
-  }
   f32x4 o[HG][MV];
 #pragma unroll
   for (int ht = 0; ht < HG; ht++)

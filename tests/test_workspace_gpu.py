@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from checker import check_topk_row
+from checker import check_sfa, check_topk_row
 from sparse_attention_04_amd import binding as B
 from sparse_attention_04_amd.inputs import case_to, make_case
 
@@ -62,6 +62,36 @@ def test_one_workspace_serves_calls_of_different_shapes():
     # (the header's error word and profiling stamps aside)
     torch.cuda.synchronize()
     assert int(ws[256:].count_nonzero()) == 0
+
+
+def test_one_fused_workspace_serves_growing_and_shrinking_shapes():
+    """dsa_fused_decode keeps the indexer's zero state at the start of the
+    workspace and its scratch (index rows, partials) at the end: a workspace
+    sized for the largest call serves a small call, then a larger one (whose
+    state reaches past the small call's), then the small one again."""
+    small = case_to(make_case("c2_decode_bf16", 56, batch=2, seq_len_range=(2500, 3500)), "cuda")
+    big = case_to(make_case("c5_decode4", 57, batch=6, seq_len_range=(3000, 6000)), "cuda")
+    calls = {c.name + str(c.batch): B.Call(c) for c in (small, big)}
+    need = max(call.workspace(B.DSA_OP_FUSED_DECODE)[1] for call in calls.values())
+    state = max(B.dsa_workspace_size(B.DSA_OP_INDEXER_TOPK, call.batch, call.iargs, call.sargs)
+                for call in calls.values())
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for case in (small, big, small, big):
+        call = calls[case.name + str(case.batch)]
+        _say(f"shared fused workspace: {case.name} B={case.batch} T={case.total_q}")
+        call.use_workspace(B.DSA_OP_FUSED_DECODE, ws)
+        out, lse, idx = call.fused_decode()
+        torch.cuda.synchronize()
+        idx_h, out_h = idx.cpu().numpy(), out.float().cpu().numpy()
+        for b in range(case.batch):
+            for i in range(int(case.q_lens_host[b])):
+                tok = case.token(b, i)
+                check_topk_row(idx_h[tok], oracle.run_query(case, b, i), case.topk)
+        for b in (0, case.batch - 1):
+            tok = case.token(b, 0)
+            check_sfa(out_h[tok], oracle.sfa_query(case, b, 0, idx_h[tok][idx_h[tok] >= 0])[0], "bf16")
+        # the state part is zero again (the header's error word and stamps aside)
+        assert int(ws[256:state].count_nonzero()) == 0
 
 
 def _with_env(**kv):

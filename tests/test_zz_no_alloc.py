@@ -52,6 +52,29 @@ def test_noalloc_matches_workspace_entry_point():
         assert np.allclose(lse.cpu().numpy(), lse_w.cpu().numpy(), atol=1e-4, rtol=1e-5)
 
 
+def test_noalloc_calls_of_growing_shapes():
+    """A small call, then a larger one whose indexer state reaches past where
+    the small call left its index rows: the static array keeps state and
+    scratch apart, so the larger call is still exact."""
+    B.lib()
+    for case in (case_to(make_case("c2_decode_bf16", 64, batch=2, seq_len_range=(2200, 3000)), "cuda"),
+                 case_to(make_case("c5_decode4", 65, batch=6, seq_len_range=(3000, 5000)), "cuda")):
+        call = B.Call(case)
+        out = torch.empty_like(call.out)
+        lse = torch.empty_like(call.lse)
+        idx = torch.empty_like(call.idx)
+        _say(f"no-alloc growing: {case.name} B={case.batch} T={case.total_q}")
+        call.fused_decode_noalloc(out, lse, idx)
+        torch.cuda.synchronize()
+        idx_h, out_h = idx.cpu().numpy(), out.float().cpu().numpy()
+        for b in range(case.batch):
+            for i in range(int(case.q_lens_host[b])):
+                tok = case.token(b, i)
+                check_topk_row(idx_h[tok], oracle.run_query(case, b, i), case.topk)
+        tok = case.token(case.batch - 1, 0)
+        check_sfa(out_h[tok], oracle.sfa_query(case, case.batch - 1, 0, idx_h[tok][idx_h[tok] >= 0])[0], "bf16")
+
+
 def test_noalloc_rejects_calls_beyond_its_scratch():
     B.lib()
     case = case_to(make_case("c2_decode_bf16", 63, batch=2, seq_len_range=(3000, 4000)), "cuda")

@@ -45,7 +45,12 @@
  *     returns DSA_ERR_HIP.  dsa_last_error() returns a thread-local message for
  *     the last failure.  Contents of device arrays (block-table entries, lengths)
  *     are preconditions: block_table entries < num_pages, seq_lens[b] <=
- *     max_pages_per_seq * page_size, 0 <= q_lens <= seq_lens, values finite.
+ *     max_pages_per_seq * page_size, 0 <= q_lens <= seq_lens, values finite,
+ *     index rows given to dsa_sparse_attn within [-1, seq_len).  With
+ *     DSA_DEBUG=1 in the environment every call first checks the lengths,
+ *     query offsets, block-table entries of the pages in use (and those
+ *     index rows) on the device, waits for the result and returns
+ *     DSA_ERR_INVALID_ARG, having enqueued nothing else, if one is violated.
  *     The decode indexer's workgroups wait for each other with bounded waits
  *     (its grid is sized to be resident as a whole; other work sharing the
  *     device can keep part of it waiting).  If a

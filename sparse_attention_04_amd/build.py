@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["dsa_api.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "noalloc.hip", "prolog.hip"]
+SOURCES = ["dsa_api.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "noalloc.hip", "prolog.hip",
+           "checks.hip"]
 
 # Kernels that issue LDS reads through inline assembly and wait for them later
 # with an explicit lgkmcnt: the compiler takes an asm result as ready at once,

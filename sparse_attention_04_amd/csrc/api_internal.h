@@ -1,5 +1,7 @@
 // Internal entry points shared by the C ABI's translation units (not part of the ABI).
 #pragma once
+#include <hip/hip_runtime.h>
+
 #include "dsa.h"
 
 namespace dsa {
@@ -14,6 +16,13 @@ dsa_status fused_decode_impl(const dsa_batch* b, const dsa_indexer_args* ia, con
 // Bytes at the start of a dsa_fused_decode workspace that hold its zero state
 // (the rest of what dsa_workspace_size reports is scratch, kept at the end).
 size_t fused_decode_state_bytes(const dsa_batch* b);
+
+// DSA_DEBUG=1: check the device-resident batch contents (lengths, query
+// offsets, block-table entries below num_pages, and idx rows of `topk` when
+// idx is non-NULL) on `st` and wait for the result; DSA_ERR_INVALID_ARG with
+// a message when a precondition is violated.
+dsa_status debug_check_batch(const dsa_batch* b, int num_pages, int page_size, const int32_t* idx, int topk,
+                             hipStream_t st);
 
 // Record `msg` as the thread's last error and return `st`; clear it.
 dsa_status set_error(dsa_status st, const char* msg);

@@ -444,6 +444,10 @@ dsa_status dsa_indexer_topk(const dsa_batch* b, const dsa_indexer_args* a, int32
   if (!aligned(idx_out, 4) || !aligned(ws, 16)) return fail(DSA_ERR_INVALID_ARG, "idx_out must be 4-byte, ws 16-byte aligned");
   const size_t need = dsa_workspace_size(DSA_OP_INDEXER_TOPK, b, a, nullptr);
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (debug_mode()) {
+    s = debug_check_batch(b, a->k_cache->num_pages, a->k_cache->page_size, nullptr, 0, (hipStream_t)stream);
+    if (s != DSA_OK) return s;
+  }
   return run_indexer(b, a, idx_out, (uint32_t*)ws, (hipStream_t)stream);
 }
 
@@ -459,6 +463,10 @@ dsa_status dsa_sparse_attn(const dsa_batch* b, const dsa_sfa_args* a, const int3
   if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", topk);
   const size_t need = sfa_bytes(b, a, topk) + kLayoutSlack;
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (debug_mode()) {
+    s = debug_check_batch(b, a->kv_cache->num_pages, a->kv_cache->page_size, idx, topk, (hipStream_t)stream);
+    if (s != DSA_OK) return s;
+  }
   return run_sfa(b, a, idx, topk, out, lse, scratch_at_end(ws, ws_bytes, sfa_bytes(b, a, topk)), (hipStream_t)stream);
 }
 
@@ -492,6 +500,11 @@ dsa_status fused_decode_impl(const dsa_batch* b, const dsa_indexer_args* ia, con
   unsigned char* scr = scratch_at_end(ws, ws_bytes, rows + sfa_bytes(b, sa, ia->topk));
   int32_t* idx = idx_out ? idx_out : (int32_t*)scr;
   hipStream_t st = (hipStream_t)stream;
+  if (debug_mode()) {
+    s = debug_check_batch(b, std::min(ia->k_cache->num_pages, sa->kv_cache->num_pages), ia->k_cache->page_size,
+                          nullptr, 0, st);
+    if (s != DSA_OK) return s;
+  }
   s = run_indexer(b, ia, idx, (uint32_t*)ws, st);
   if (s != DSA_OK) return s;
   return run_sfa(b, sa, idx, ia->topk, out, lse, scr + rows, st);
@@ -544,6 +557,10 @@ dsa_status dsa_indexer_prolog(const dsa_batch* b, const dsa_prolog_args* a, void
   const size_t need = dsa_prolog_workspace_size(b, a);
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
   if (b->total_q == 0) return DSA_OK;
+  if (debug_mode()) {
+    s = debug_check_batch(b, kc->num_pages, kc->page_size, nullptr, 0, (hipStream_t)stream);
+    if (s != DSA_OK) return s;
+  }
   unsigned char* w = (unsigned char*)ws;
   PrologParams p{};
   p.bv = view_of(b, kc->page_size);
@@ -591,6 +608,11 @@ dsa_status dsa_fused_prefill(const dsa_batch* b, const dsa_indexer_args* ia, con
   unsigned char* scr = scratch_at_end(ws, ws_bytes, rows + sfa_bytes(b, sa, ia->topk));
   int32_t* idx = idx_out ? idx_out : (int32_t*)scr;
   hipStream_t st = (hipStream_t)stream;
+  if (debug_mode()) {
+    s = debug_check_batch(b, std::min(ia->k_cache->num_pages, sa->kv_cache->num_pages), ia->k_cache->page_size,
+                          nullptr, 0, st);
+    if (s != DSA_OK) return s;
+  }
   s = run_indexer_prefill(b, ia, idx, st);
   if (s != DSA_OK) return s;
   return run_sfa(b, sa, idx, ia->topk, out, lse, scr + rows, st);

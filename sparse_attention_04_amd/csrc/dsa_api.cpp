@@ -312,8 +312,10 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
 
 dsa_status run_indexer_prefill(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out, hipStream_t st) {
   if (b->total_q == 0) return DSA_OK;
-  if (a->q_dtype != DSA_BF16)
-    return fail(DSA_ERR_UNSUPPORTED, "the prefill indexer (more than %d query tokens per sequence) is built for bf16 only", kMaxDecodeQ);
+  if (a->q_dtype != DSA_BF16 && a->q_dtype != DSA_FP8_E4M3 && a->q_dtype != DSA_MXFP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "the prefill indexer (more than %d query tokens per sequence) is built for bf16, FP8 and MXFP8 only", kMaxDecodeQ);
+  if (a->q_dtype == DSA_MXFP8_E4M3 && !aligned(a->k_cache->scale, 4))
+    return fail(DSA_ERR_INVALID_ARG, "the prefill indexer reads MXFP8 key scales as 4-byte words: k_cache->scale must be 4-byte aligned");
   if (a->topk > indexer_prefill_max_topk())
     return fail(DSA_ERR_UNSUPPORTED, "prefill topk %d above %d", a->topk, indexer_prefill_max_topk());
   const int P = a->k_cache->page_size;
@@ -323,8 +325,10 @@ dsa_status run_indexer_prefill(const dsa_batch* b, const dsa_indexer_args* a, in
   IndexerPrefillParams p{};
   p.bv = view_of(b, P);
   p.q = a->q;
+  p.q_scale = a->q_scale;
   p.w = a->head_weights;
   p.k_data = a->k_cache->data;
+  p.k_scale = a->k_cache->scale;
   p.topk = a->topk;
   p.idx_out = idx_out;
   p.grid = indexer_prefill_grid(b->total_q, b->batch);

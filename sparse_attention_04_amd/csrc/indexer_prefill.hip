@@ -16,7 +16,11 @@
 //
 // Inside a unit, queries are taken 4 at a time, one per wave.  64-key tiles of
 // the K cache stream through a 2-deep LDS ring shared by the 4 waves; each
-// wave scores its query against the tile with 32x32x16 MFMAs and appends the
+// wave scores its query against the tile with 32x32 MFMAs (bf16, or scaled
+// e4m3 for the quantised caches, which the pages' fused indexer serves in
+// prefill as in decode: Day0 Inference Optimization on Ascend CANN, sec. 2;
+// Adapting and Optimizing Inference for a New Model Architecture on Ascend,
+// sec. 2.2) and appends the
 // keys above its current threshold to its own candidate buffer in LDS.  When a
 // buffer fills, a wave-level radix select (four 8-bit digits) keeps exactly
 // the k best, stably (so equal scores stay in position order and the smaller
@@ -34,13 +38,34 @@ constexpr int kPfWaves = 4;
 constexpr int kQBlock = 64;         // query block of the zigzag schedule
 constexpr int kKT = 64;             // keys per tile
 constexpr int kCap = 3072;          // candidate buffer entries per query
-constexpr int kRowPitch = 128 * 2 + 16;            // LDS bytes per key row (bf16, padded)
-constexpr int kTileBytes = 20 * 1024;              // 64 rows of kRowPitch, rounded to whole loads
 constexpr int kMaxPages = 4096;                    // block-table entries staged in LDS
 constexpr int kHistWords = 260;                    // per-wave select histogram (256 bins, a spare word, padding)
 
+// LDS image of one 64-key tile of 128-dim keys.  bf16: rows of 256 bytes at a
+// 272-byte pitch, 20 1-KiB loads (the last three only fill padding).  e4m3
+// (FP8 and MXFP8): rows of 128 bytes at a 144-byte pitch (9 loads), then the
+// 64 rows' 4-byte scale words (FP8: the float32 per-token scale; MXFP8: the
+// four e8m0 bytes of the row's 32-element groups) at byte kScaleOff, loaded
+// by a 4-byte-per-lane load in the place of load 9.  Both pitches keep the
+// 16-byte operand reads of 16 consecutive rows on distinct banks.
+template <int DT>
+struct PfTile {
+  static constexpr bool kQuant = (DT != kBF16);
+  static constexpr int kRowBytes = kQuant ? 128 : 256;
+  static constexpr int kPitch = kRowBytes + 16;
+  static constexpr int kRowLoads = (64 * kPitch + 1023) / 1024;     // 1-KiB loads that fill the rows
+  static constexpr int kScaleOff = 64 * kPitch;                    // bf16: unused
+  static constexpr int kLoads = kQuant ? 12 : 20;                   // load slots, 4 waves x kLoads / 4
+  static constexpr int kBytes = kQuant ? kScaleOff + 64 * 4 : 20 * 1024;   // ring stride
+  static_assert(kQuant ? (kRowLoads == 9 && kRowLoads < kLoads) : kRowLoads <= kLoads, "tile loads");
+  static_assert(kBytes % 16 == 0 && kLoads % 4 == 0, "tile layout");
+};
+
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
@@ -185,15 +210,134 @@ __device__ uint32_t wave_select(uint32_t* keys, uint32_t* pos, int& count, int n
   return wave_min_u32(kmin) + mn;
 }
 
-template <int H, int D, bool BIG_PAGE>
+// Query operands of one wave in the 32x32 MFMA layout, and the tile product.
+// bf16 (32x32x16): lane half h holds dims [64h, 64h + 64) of its head row and
+// of its key row, which fixes one order of the contraction index for both.
+// e4m3 (scaled 32x32x64): a lane's bytes 0..15 belong to the instruction's
+// k-block 0 and bytes 16..31 to k-block 1, and the scale of block b of row m
+// is taken from lane m + 32b; K-step kk covers the 32-element groups 2kk and
+// 2kk + 1, so lane half h carries dims 64kk + 16h .. +15 and 64kk + 32 + 16h
+// .. +15 and supplies the scale of group 2kk + h.  FP8 enters with unit
+// block scales: its per-(token, head) query scale is folded into the head
+// weight and the per-token key scale multiplies the head-weighted sum.
+template <int DT, int H, int D>
+struct PfQuery;
+
+template <int H, int D>
+struct PfQuery<kBF16, H, D> {
+  static constexpr int MT = H / 32, KS = D / 16;
+  bf16x8 a[MT][KS];
+  float wr[MT][16];
+  __device__ void load(const IndexerPrefillParams& p, size_t tok) {
+    const int lane = threadIdx.x & 63;
+    const uint16_t* qp = (const uint16_t*)p.q + tok * H * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const bf16x8* src = (const bf16x8*)(qp + (size_t)(32 * mt + (lane & 31)) * D + (lane >> 5) * (D / 2));
+#pragma unroll
+      for (int kk = 0; kk < KS; kk++) a[mt][kk] = src[kk];
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        wr[mt][i] = p.w[tok * H + 32 * mt + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3)];
+    }
+  }
+  // both 32-key N-tiles at once: four independent accumulator chains
+  __device__ void mma(const unsigned char* cur, f32x16 (&acc)[2][MT]) const {
+    constexpr int PITCH = PfTile<kBF16>::kPitch;
+    const int lane = threadIdx.x & 63;
+    const unsigned char* kp = cur + (lane & 31) * PITCH + (lane >> 5) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) {
+      const bf16x8 kb0 = *(const bf16x8*)(kp + 16 * kk);
+      const bf16x8 kb1 = *(const bf16x8*)(kp + 32 * PITCH + 16 * kk);
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], kb0, acc[0][mt], 0, 0, 0);
+        acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], kb1, acc[1][mt], 0, 0, 0);
+      }
+    }
+  }
+  __device__ float key_scale(const unsigned char*) const { return 1.f; }
+};
+
+template <int DT, int H, int D>
+struct PfQueryF8 {
+  static constexpr int MT = H / 32, KS = D / 64;
+  i32x8 a[MT][KS];
+  int32_t sa[MT][KS];     // MXFP8: e8m0 byte of group 2kk + h of this lane's head row
+  float wr[MT][16];       // FP8: w * q_scale
+  __device__ static i32x8 step(const unsigned char* rowp, int kk, int h) {
+    const u32x4* v = (const u32x4*)rowp;
+    const u32x4 lo = v[4 * kk + h], hi = v[4 * kk + 2 + h];
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+  __device__ void load(const IndexerPrefillParams& p, size_t tok) {
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const unsigned char* qp = (const unsigned char*)p.q + tok * H * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const int hrow = 32 * mt + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < KS; kk++) {
+        a[mt][kk] = step(qp + (size_t)hrow * D, kk, h);
+        if constexpr (DT == kMX)
+          sa[mt][kk] = ((const uint8_t*)p.q_scale)[(tok * H + hrow) * (D / 32) + 2 * kk + h];
+        else
+          sa[mt][kk] = 127;   // 2^0
+      }
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int hh = 32 * mt + 8 * (i / 4) + 4 * h + (i & 3);
+        float wv = p.w[tok * H + hh];
+        if constexpr (DT == kFP8) wv *= ((const float*)p.q_scale)[tok * H + hh];
+        wr[mt][i] = wv;
+      }
+    }
+  }
+  __device__ void mma(const unsigned char* cur, f32x16 (&acc)[2][MT]) const {
+    constexpr int PITCH = PfTile<DT>::kPitch;
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const unsigned char* kp = cur + (lane & 31) * PITCH;
+    uint32_t sw[2] = {127u, 127u};
+    if constexpr (DT == kMX) {
+      const uint32_t* st = (const uint32_t*)(cur + PfTile<DT>::kScaleOff);
+      sw[0] = st[lane & 31];
+      sw[1] = st[32 + (lane & 31)];
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) {
+      const i32x8 kb0 = step(kp, kk, h);
+      const i32x8 kb1 = step(kp + 32 * PITCH, kk, h);
+      const int sb0 = (DT == kMX) ? (int)((sw[0] >> (8 * (2 * kk + h))) & 0xFFu) : 127;
+      const int sb1 = (DT == kMX) ? (int)((sw[1] >> (8 * (2 * kk + h))) & 0xFFu) : 127;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        acc[0][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][kk], kb0, acc[0][mt], 0, 0, 0, sa[mt][kk], 0, sb0);
+        acc[1][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][kk], kb1, acc[1][mt], 0, 0, 0, sa[mt][kk], 0, sb1);
+      }
+    }
+  }
+  // FP8: the per-token scale of key `lane` of the tile
+  __device__ float key_scale(const unsigned char* cur) const {
+    if constexpr (DT == kFP8) return ((const float*)(cur + PfTile<DT>::kScaleOff))[threadIdx.x & 63];
+    return 1.f;
+  }
+};
+template <int H, int D>
+struct PfQuery<kFP8, H, D> : PfQueryF8<kFP8, H, D> {};
+template <int H, int D>
+struct PfQuery<kMX, H, D> : PfQueryF8<kMX, H, D> {};
+
+template <int DT, int H, int D, bool BIG_PAGE>
 __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerPrefillParams p) {
   static_assert(H == 64 && D == 128, "prefill indexer is compiled for 64 heads x 128");
+  using TL = PfTile<DT>;
+  using Q = PfQuery<DT, H, D>;
   constexpr int MT = H / 32;        // M-tiles over heads
-  constexpr int KS = D / 16;        // K-steps of 16
-  constexpr int LPW = kTileBytes / 1024 / kPfWaves;   // 1-KiB loads per wave per tile (5)
+  constexpr int LPW = TL::kLoads / kPfWaves;          // load slots per wave per tile (5 bf16, 3 e4m3)
   extern __shared__ __attribute__((aligned(16))) unsigned char pf_smem[];
   unsigned char* ring = pf_smem;                                              // 2 tiles
-  uint32_t* cand = (uint32_t*)(pf_smem + 2 * kTileBytes);                     // [4][2][kCap]
+  uint32_t* cand = (uint32_t*)(pf_smem + 2 * TL::kBytes);                     // [4][2][kCap]
   uint32_t* hist = cand + kPfWaves * 2 * kCap;                                // [4][kHistWords]
   int32_t* s_bt = (int32_t*)(hist + kPfWaves * kHistWords);                   // [kMaxPages]
   __shared__ int s_unit[4];
@@ -202,7 +346,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
   const BatchView& bv = p.bv;
   const int P = bv.page_size;
   const int K = p.topk;
-
   // ---- unit -> (sequence, first block): sequence b has NB_b = ceil(T_b/64)
   // blocks and ceil(NB_b/2) units; unit u owns blocks u and NB_b-1-u.
   if (wave == 0) {
@@ -254,15 +397,16 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
   const int blocks[2] = {u, NB - 1 - u};
   const int nblk = (blocks[1] != blocks[0]) ? 2 : 1;
 
-  // per-lane source of each of this wave's LPW tile loads: LDS byte
-  // (wave + 4k) * 1024 + 16 * lane is row off / kRowPitch, 16-byte column
-  // (off % kRowPitch) / 16; padding bytes load row 0, column 0
+  // per-lane source of each of this wave's LPW tile loads: load slot c = wave
+  // + 4k fills LDS bytes 1024c + 16 * lane, row off / pitch, 16-byte column
+  // (off % pitch) / 16; padding bytes load row 0, column 0.  e4m3: slot 9
+  // loads the 64 rows' scale words (lane = row), slots 10 and 11 are unused.
   int lrow[LPW], lcol[LPW];
 #pragma unroll
   for (int k = 0; k < LPW; k++) {
     const int off = (wave + kPfWaves * k) * 1024 + lane * 16;
-    const int r = off / kRowPitch, c = (off % kRowPitch) / 16;
-    const bool real = r < kKT && c < (D * 2) / 16;
+    const int r = off / TL::kPitch, c = (off % TL::kPitch) / 16;
+    const bool real = r < kKT && c < TL::kRowBytes / 16;
     lrow[k] = real ? r : 0;
     lcol[k] = real ? c * 16 : 0;
   }
@@ -289,49 +433,45 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
       const bool groups_all_keep = (tmax + 1 <= K);  // uniform: every wave's t <= tmax
       if (groups_all_keep) continue;
 
-      // query operands in the 32x32 layout: lane half h holds dims [64h, 64h+64)
-      bf16x8 a[MT][KS];
-      float wr[MT][16];
-      {
-        const int qq = have_q ? q : q1 - 1;
-        const uint16_t* qp = (const uint16_t*)p.q + (size_t)(tok0 + qq) * H * D;
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++) {
-          const bf16x8* src = (const bf16x8*)(qp + (size_t)(32 * mt + (lane & 31)) * D + (lane >> 5) * (D / 2));
-#pragma unroll
-          for (int kk = 0; kk < KS; kk++) a[mt][kk] = src[kk];
-#pragma unroll
-          for (int i = 0; i < 16; i++)
-            wr[mt][i] = p.w[(size_t)(tok0 + qq) * H + 32 * mt + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3)];
-        }
-      }
+      Q qo;
+      qo.load(p, (size_t)(tok0 + (have_q ? q : q1 - 1)));
       __builtin_amdgcn_s_waitcnt(0);
       int count = 0;
       uint32_t thr = 0u;    // keys must exceed this to become candidates
       const int nt = (tmax + 1 + kKT - 1) / kKT;
       // tile `tile`'s keys tile*64 .. tile*64+63 (rows past tmax repeat row
-      // tmax) go to ring buffer tile & 1: each wave issues LPW 1-KiB loads
+      // tmax) go to ring buffer tile & 1
       auto issue = [&](int tile) {
         const int s0 = tile * kKT;
         const int lim = tmax - s0;     // rows above lim repeat row lim
-        const uint32_t m0 = ring_lds + (uint32_t)(tile & 1) * kTileBytes + (uint32_t)wave_u * 1024u;
+        const uint32_t m0 = ring_lds + (uint32_t)(tile & 1) * TL::kBytes + (uint32_t)wave_u * 1024u;
+        const unsigned char* src[LPW];
         if constexpr (BIG_PAGE) {
           // the whole tile lies in one page
           const int64_t prow0 = ((int64_t)bt[s0 >> bv.page_shift] << bv.page_shift) + (s0 & (P - 1));
-          const unsigned char* base = (const unsigned char*)p.k_data + prow0 * (D * 2);
-#pragma unroll
-          for (int k = 0; k < LPW; k++)
-            dma16(base + (min(lrow[k], lim) * (D * 2) + lcol[k]), m0 + k * kPfWaves * 1024u);
-        } else {
-          const unsigned char* src[LPW];
 #pragma unroll
           for (int k = 0; k < LPW; k++) {
-            const int srow = s0 + min(lrow[k], lim);
-            const int64_t prow = ((int64_t)bt[srow >> bv.page_shift] << bv.page_shift) + (srow & (P - 1));
-            src[k] = (const unsigned char*)p.k_data + prow * (D * 2) + lcol[k];
+            const int c = wave_u + kPfWaves * k;
+            src[k] = (TL::kQuant && c == TL::kRowLoads)
+                         ? (const unsigned char*)p.k_scale + (prow0 + min(lane, lim)) * 4
+                         : (const unsigned char*)p.k_data + (prow0 + min(lrow[k], lim)) * TL::kRowBytes + lcol[k];
           }
+        } else {
 #pragma unroll
-          for (int k = 0; k < LPW; k++) dma16(src[k], m0 + k * kPfWaves * 1024u);
+          for (int k = 0; k < LPW; k++) {
+            const int c = wave_u + kPfWaves * k;
+            const bool sl = TL::kQuant && c == TL::kRowLoads;
+            const int srow = s0 + min(sl ? lane : lrow[k], lim);
+            const int64_t prow = ((int64_t)bt[srow >> bv.page_shift] << bv.page_shift) + (srow & (P - 1));
+            src[k] = sl ? (const unsigned char*)p.k_scale + prow * 4
+                        : (const unsigned char*)p.k_data + prow * TL::kRowBytes + lcol[k];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < LPW; k++) {
+          const int c = wave_u + kPfWaves * k;   // uniform over the wave
+          if (!TL::kQuant || c < TL::kRowLoads) dma16(src[k], m0 + k * kPfWaves * 1024u);
+          else if (c == TL::kRowLoads) dma4(src[k], ring_lds + (uint32_t)(tile & 1) * TL::kBytes + TL::kScaleOff);
         }
       };
       // 2-buffer ring: tile t + 1 is loaded while t is scored.  The barrier at
@@ -342,10 +482,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
         DSA_PF_WAIT_VMCNT(0);
         lds_barrier();
         if (tile + 1 < nt) issue(tile + 1);
-        const unsigned char* cur = ring + (tile & 1) * kTileBytes;
-        // ---- scores of the 64 keys of this tile for this wave's query: both
-        // 32-key N-tiles at once, so four independent accumulator chains
-        // keep the matrix unit busy
+        const unsigned char* cur = ring + (tile & 1) * TL::kBytes;
+        // ---- scores of the 64 keys of this tile for this wave's query
         float sc[2];
         {
           f32x16 acc[2][MT];
@@ -355,17 +493,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
             for (int mt = 0; mt < MT; mt++)
 #pragma unroll
               for (int e = 0; e < 16; e++) acc[n][mt][e] = 0.f;
-          const unsigned char* kp = cur + (lane & 31) * kRowPitch + (lane >> 5) * D;
-#pragma unroll
-          for (int kk = 0; kk < KS; kk++) {
-            const bf16x8 kb0 = *(const bf16x8*)(kp + 16 * kk);
-            const bf16x8 kb1 = *(const bf16x8*)(kp + 32 * kRowPitch + 16 * kk);
-#pragma unroll
-            for (int mt = 0; mt < MT; mt++) {
-              acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], kb0, acc[0][mt], 0, 0, 0);
-              acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], kb1, acc[1][mt], 0, 0, 0);
-            }
-          }
+          qo.mma(cur, acc);
 #pragma unroll
           for (int n = 0; n < 2; n++) {
             // four partial sums (entries i mod 4 of each M-tile), added
@@ -374,7 +502,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
 #pragma unroll
             for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-              for (int i = 0; i < 16; i++) s4[i & 3] = fmaf(wr[mt][i], acc[n][mt][i], s4[i & 3]);
+              for (int i = 0; i < 16; i++) s4[i & 3] = fmaf(qo.wr[mt][i], acc[n][mt][i], s4[i & 3]);
             const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
             const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
             sc[n] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);   // lanes l and l ^ 32 summed
@@ -382,7 +510,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
         }
         // lane l takes key tile*64 + l: N-tile l/32, column l%32
         const int spos = tile * kKT + lane;
-        const float v = (lane < 32) ? sc[0] : sc[1];
+        const float v = ((lane < 32) ? sc[0] : sc[1]) * qo.key_scale(cur);
         const uint32_t x = (have_q && spos <= t) ? float_key(v) : 0u;
         bool cnd = x > thr;
         uint64_t m = __ballot(cnd);
@@ -415,8 +543,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
 
 }  // namespace
 
-size_t indexer_prefill_lds_bytes() {
-  return 2 * (size_t)kTileBytes + (size_t)kPfWaves * 2 * kCap * 4 + kPfWaves * kHistWords * 4 + kMaxPages * 4;
+size_t indexer_prefill_lds_bytes(int dtype) {
+  const size_t tile = (dtype == kBF16) ? PfTile<kBF16>::kBytes : PfTile<kFP8>::kBytes;
+  return 2 * tile + (size_t)kPfWaves * 2 * kCap * 4 + kPfWaves * kHistWords * 4 + kMaxPages * 4;
 }
 
 int indexer_prefill_max_pages() { return kMaxPages; }
@@ -433,11 +562,17 @@ int indexer_prefill_grid(int total_q, int batch) {
 }
 
 hipError_t launch_indexer_prefill(int dtype, int H, int D, const IndexerPrefillParams& p, hipStream_t st) {
-  if (dtype != kBF16 || H != 64 || D != 128) return hipErrorInvalidValue;
+  if ((dtype != kBF16 && dtype != kFP8 && dtype != kMX) || H != 64 || D != 128) return hipErrorInvalidValue;
   if (p.grid <= 0) return hipSuccess;
   // pages of 64 tokens or more hold each 64-key tile whole
-  auto kern = p.bv.page_size >= kKT ? indexer_prefill_kernel<64, 128, true> : indexer_prefill_kernel<64, 128, false>;
-  const size_t lds = indexer_prefill_lds_bytes();
+  const bool big = p.bv.page_size >= kKT;
+  void (*kern)(IndexerPrefillParams) = nullptr;
+  switch (dtype) {
+    case kBF16: kern = big ? indexer_prefill_kernel<kBF16, 64, 128, true> : indexer_prefill_kernel<kBF16, 64, 128, false>; break;
+    case kFP8: kern = big ? indexer_prefill_kernel<kFP8, 64, 128, true> : indexer_prefill_kernel<kFP8, 64, 128, false>; break;
+    default: kern = big ? indexer_prefill_kernel<kMX, 64, 128, true> : indexer_prefill_kernel<kMX, 64, 128, false>; break;
+  }
+  const size_t lds = indexer_prefill_lds_bytes(dtype);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kPfThreads), lds, st, p);

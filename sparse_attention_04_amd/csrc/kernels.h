@@ -44,15 +44,17 @@ hipError_t launch_indexer_decode(int dtype, int H, int D, int maxq, const Indexe
 
 struct IndexerPrefillParams {
   BatchView bv;
-  const void* q;           // [total_q][H][D] bf16
+  const void* q;           // [total_q][H][D] bf16 or e4m3 bytes
+  const void* q_scale;     // fp8: f32 [total_q][H]; mx: u8 [total_q][H][D/32]
   const float* w;          // [total_q][H]
-  const void* k_data;      // [num_pages][P][D] bf16
+  const void* k_data;      // [num_pages][P][D] bf16 or e4m3 bytes
+  const void* k_scale;     // fp8: f32 [num_pages][P]; mx: u8 [num_pages][P][D/32], 4-byte aligned
   int32_t topk;
   int32_t* idx_out;        // [total_q][topk]
   int32_t grid;            // workgroups launched (>= number of zigzag units)
 };
 
-size_t indexer_prefill_lds_bytes();
+size_t indexer_prefill_lds_bytes(int dtype);
 int indexer_prefill_grid(int total_q, int batch);
 int indexer_prefill_max_pages();
 int indexer_prefill_max_topk();

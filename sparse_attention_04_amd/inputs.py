@@ -222,6 +222,17 @@ PRESETS = {
                             h_i=64, d_i=128, topk=2048, idx_dtype=MXFP8, w_div=64.0,
                             h_s=128, d_qk=576, d_v=512, scale_dim=192, sfa_dtype=BF16, sfa_mult=1.0,
                             outliers=0.01),
+    # The causal prefill of c3_prefill_bf16 with the indexer's q and K cache
+    # quantised as in c4_decode_fp8 / c4_decode_mxfp8 (1% outliers at 20 sigma
+    # in the indexer's values); the SFA stays bf16 on N(0,1) values.
+    "c3_prefill_fp8": dict(batch=1, seq_len_range=(32768, 32768), q_len=32768, page_size=64,
+                           h_i=64, d_i=128, topk=2048, idx_dtype=FP8, w_div=64.0,
+                           h_s=128, d_qk=576, d_v=512, scale_dim=192, sfa_dtype=BF16, sfa_mult=1.0,
+                           idx_outliers=0.01),
+    "c3_prefill_mxfp8": dict(batch=1, seq_len_range=(32768, 32768), q_len=32768, page_size=64,
+                             h_i=64, d_i=128, topk=2048, idx_dtype=MXFP8, w_div=64.0,
+                             h_s=128, d_qk=576, d_v=512, scale_dim=192, sfa_dtype=BF16, sfa_mult=1.0,
+                             idx_outliers=0.01),
     # Long context: 8192-token chunk appended after 122880 cached tokens.
     "c5_chunk_prefill": dict(batch=8, seq_len_range=(131072, 131072), q_len=8192, page_size=64,
                              h_i=64, d_i=128, topk=2048, idx_dtype=BF16, w_div=64.0,
@@ -332,6 +343,9 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", value_seed: Optiona
     h_i, d_i, h_s, d_qk, d_v = p["h_i"], p["d_i"], p["h_s"], p["d_qk"], p["d_v"]
     idt, sdt = p["idx_dtype"], p["sfa_dtype"]
     outl = p.get("outliers", 0.0)
+    # the indexer's q and K may take outliers of their own (idx_outliers), so a
+    # quantised indexer can be tested on C4's recipe beside a plain SFA
+    outl_i = p.get("idx_outliers", outl)
     mult = p["sfa_mult"]
     chunk = 1 << 16
 
@@ -341,7 +355,7 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", value_seed: Optiona
 
     # 3. indexer q
     g, og = _gen(vseed, "q_i", dev), _gen(vseed, "out_q_i", dev)
-    q_i, q_i_scale = _encode(_randn((total_q, h_i, d_i), g, dev, 1.0, outl, og), idt)
+    q_i, q_i_scale = _encode(_randn((total_q, h_i, d_i), g, dev, 1.0, outl_i, og), idt)
     # 4. indexer K, logical rows scattered into the pool
     k_pool = torch.empty((num_pages, P, d_i), dtype=storage_dtype(idt), device=dev)
     k_pool.fill_(_poison_value(k_pool))
@@ -351,7 +365,7 @@ def make_case(name: str, seed: int = 0, device: str = "cpu", value_seed: Optiona
     elif idt == MXFP8:
         k_scale = torch.full((num_pages, P, d_i // MX_GROUP), 127, dtype=torch.uint8, device=dev)
     g, og = _gen(vseed, "k_i", dev), _gen(vseed, "out_k_i", dev)
-    _fill_pool(k_pool, k_scale, lambda n: _randn((n, d_i), g, dev, 1.0, outl, og),
+    _fill_pool(k_pool, k_scale, lambda n: _randn((n, d_i), g, dev, 1.0, outl_i, og),
                n_keys, phys_t, idt, chunk)
     # 5. head weights U(0,1)/w_div, or U(-1,1)/w_div with w_signed (the
     # weights are projections of the hidden state and may take either sign)

@@ -418,6 +418,32 @@ def test_prefill_fp8kv():
     _run_prefill(case, _sample_prefill_queries(case, per_seq=30))
 
 
+@pytest.mark.parametrize("name", ["c3_prefill_fp8", "c3_prefill_mxfp8"])
+def test_prefill_quantised_indexer(name):
+    # the quantised indexer in causal prefill: e4m3 key rows and their scale
+    # words staged per tile, 1% outliers at 20 sigma in q and K, ragged last
+    # query block and page
+    case = case_to(make_case(name, 61, seq_len_range=(4133, 4133), q_len=4133), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=30))
+
+
+@pytest.mark.parametrize("name", ["c3_prefill_fp8", "c3_prefill_mxfp8"])
+def test_chunked_prefill_quantised_small_pages(name):
+    # a 700-token chunk after 5300 cached tokens over 16-token pages: every key
+    # row and its scale word are looked up through their own page
+    case = case_to(make_case(name, 62, batch=2, seq_len_range=(6000, 6000), q_len=700, page_size=16,
+                             topk=1024), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=25))
+
+
+@pytest.mark.parametrize("name", ["c3_prefill_fp8", "c3_prefill_mxfp8"])
+def test_quantised_prefill_mixed_batch(name):
+    # sequences with different numbers of query blocks share a launch
+    case = case_to(make_case(name, 63, batch=3, seq_lens=[3000, 2100, 4100], q_lens=[130, 64, 257],
+                             topk=512), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=20))
+
+
 def test_prefill_equal_scores():
     case = make_case("c3_prefill_bf16", 25, seq_len_range=(3500, 3500), q_len=300, topk=1024)
     case.k_pool[:] = case.k_pool[0, 0]
@@ -436,6 +462,21 @@ def test_c3_full_size_sampled():
     _say("c3 full size: generating on device")
     case = make_case("c3_prefill_bf16", 3, device="cuda")
     qs = [(0, i) for i in (0, 2047, 2048, 2049, 9000, 20000, 32767)]
+    idx_h = _run_prefill(case, qs)
+    t = np.arange(case.total_q)
+    n = np.minimum(case.topk, t + 1)
+    valid = idx_h >= 0
+    assert np.array_equal(valid.sum(1), n)
+    assert np.all(np.where(valid, idx_h <= t[:, None], True))
+
+
+@pytest.mark.parametrize("name", ["c3_prefill_fp8", "c3_prefill_mxfp8"])
+def test_quantised_prefill_full_size_sampled(name):
+    """The 32768-token causal prefill with the quantised indexer, checked on
+    sampled queries and, for every query, on the properties of its index row."""
+    _say(f"{name} full size: generating on device")
+    case = make_case(name, 3, device="cuda")
+    qs = [(0, i) for i in (0, 2048, 2049, 15000, 32767)]
     idx_h = _run_prefill(case, qs)
     t = np.arange(case.total_q)
     n = np.minimum(case.topk, t + 1)

@@ -124,3 +124,19 @@ def test_abi_refuses_prefill_topk_above_bound():
                                    ctypes.c_void_p(0x2000), None, None, ctypes.c_void_p(0x3000), need, None)
     assert st == B.DSA_ERR_UNSUPPORTED, B.lib().dsa_last_error()
     assert b"2752" in B.lib().dsa_last_error()
+
+
+def test_abi_refuses_mx_prefill_with_unaligned_key_scales():
+    """The MXFP8 prefill indexer reads each row's four e8m0 bytes as one 4-byte
+    word: a scale pool that is not 4-byte aligned is refused before any launch."""
+    fake = 0x1000
+    batch = B.dsa_batch(1, fake, fake, fake, 100, 100, 100, 4096)
+    kc = B.dsa_paged_cache(fake, ctypes.c_void_p(0x2001), B.DSA_MXFP8_E4M3, 64, 64, 128)
+    ia = B.dsa_indexer_args(fake, B.DSA_MXFP8_E4M3, ctypes.c_void_p(0x3000), fake, 64, 128, 2048, ctypes.pointer(kc))
+    vc = B.dsa_paged_cache(fake, None, B.DSA_BF16, 64, 64, 576)
+    sa = B.dsa_sfa_args(fake, B.DSA_BF16, 128, 576, 512, 0.07, ctypes.pointer(vc))
+    need = B.dsa_workspace_size(B.DSA_OP_FUSED_PREFILL, batch, ia, sa)
+    st = B.lib().dsa_fused_prefill(ctypes.pointer(batch), ctypes.pointer(ia), ctypes.pointer(sa), 64,
+                                   ctypes.c_void_p(0x2000), None, None, ctypes.c_void_p(0x3000), need, None)
+    assert st == B.DSA_ERR_INVALID_ARG, B.lib().dsa_last_error()
+    assert b"4-byte" in B.lib().dsa_last_error()

@@ -138,10 +138,20 @@ def cpu_baseline(case, budget_s):
                       f"host cores available {len(os.sched_getaffinity(0))}"}
 
 
-def prefill_line(torch, B, make_case, steps):
-    """The 32768-token causal prefill: fused call time and MFMA fractions."""
+PREFILL_WORKLOADS = {
+    "c3_prefill_bf16": "one sequence, 32768 query tokens, causal, bf16, k=2048",
+    "c3_prefill_fp8": "one sequence, 32768 query tokens, causal, FP8 indexer (1 % outliers), bf16 SFA, k=2048",
+    "c3_prefill_mxfp8": "one sequence, 32768 query tokens, causal, MXFP8 indexer (1 % outliers), bf16 SFA, k=2048",
+}
+
+
+def prefill_line(torch, B, make_case, steps, name="c3_prefill_bf16"):
+    """The 32768-token causal prefill: fused call time and MFMA fractions.  The
+    indexer's flops are priced at its own dtype's peak (e4m3 for the quantised
+    indexers), the SFA's at bf16; the fused fraction is the time both would
+    take at their peaks over the measured time."""
     import numpy as np
-    case = make_case("c3_prefill_bf16", 3, device="cuda")
+    case = make_case(name, 3, device="cuda")
     call = B.Call(case)
     for op in (B.DSA_OP_FUSED_PREFILL, B.DSA_OP_INDEXER_TOPK, B.DSA_OP_SPARSE_ATTN):
         call.workspace(op)
@@ -160,14 +170,18 @@ def prefill_line(torch, B, make_case, steps):
     # count is never read as required work
     f_idx_collapsed = 2 * case.d_i * pairs + 2 * case.h_i * case.d_i * int((t + 1 > case.topk).sum())
     f_sfa = 2 * case.h_s * (case.d_qk + case.d_v) * rows
-    peak = MFMA_PEAK_TFLOPS["bf16"] * 1e12
-    return {"workload": "c3_prefill_bf16: one sequence, 32768 query tokens, causal, bf16, k=2048",
-            "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
-            "stages_ms": {"indexer_topk": ms_idx, "sparse_attn": ms_sfa},
-            "algorithmic_flops": {"indexer_per_head": f_idx, "indexer_collapsed": f_idx_collapsed, "sfa": f_sfa},
-            "mfma_frac": {"fused": (f_idx + f_sfa) / (ms * 1e-3) / peak,
-                          "indexer": f_idx / (ms_idx * 1e-3) / peak, "sfa": f_sfa / (ms_sfa * 1e-3) / peak},
-            "peak_tflops": MFMA_PEAK_TFLOPS["bf16"]}
+    peak_i = MFMA_PEAK_TFLOPS["fp8" if case.idx_dtype in ("fp8", "mxfp8") else "bf16"] * 1e12
+    peak_s = MFMA_PEAK_TFLOPS["bf16"] * 1e12
+    out = {"workload": f"{name}: {PREFILL_WORKLOADS[name]}",
+           "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+           "stages_ms": {"indexer_topk": ms_idx, "sparse_attn": ms_sfa},
+           "algorithmic_flops": {"indexer_per_head": f_idx, "indexer_collapsed": f_idx_collapsed, "sfa": f_sfa},
+           "mfma_frac": {"fused": (f_idx / peak_i + f_sfa / peak_s) / (ms * 1e-3),
+                         "indexer": f_idx / (ms_idx * 1e-3) / peak_i, "sfa": f_sfa / (ms_sfa * 1e-3) / peak_s},
+           "peak_tflops": {"indexer": peak_i / 1e12, "sfa": peak_s / 1e12}}
+    del call, case
+    torch.cuda.empty_cache()
+    return out
 
 
 def prolog_line(torch, B, make_case, steps, warmup):
@@ -249,6 +263,8 @@ def main():
                     help="print only the indexer prolog measurement")
     ap.add_argument("--only-prefill", action="store_true",
                     help="print only the 32k causal prefill measurement (--steps calls per stage)")
+    ap.add_argument("--prefill-workload", default="c3_prefill_bf16", choices=sorted(PREFILL_WORKLOADS),
+                    help="the prefill workload of --only-prefill")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -271,7 +287,7 @@ def main():
         print(json.dumps(prolog_line(torch, B, make_case, args.steps, args.warmup)), flush=True)
         return
     if args.only_prefill:
-        print(json.dumps(prefill_line(torch, B, make_case, args.steps)), flush=True)
+        print(json.dumps(prefill_line(torch, B, make_case, args.steps, args.prefill_workload)), flush=True)
         return
     seed = 2
     cases = [make_case(args.workload, seed, device="cuda", value_seed=seed + 100 * r) for r in range(args.sets)]
@@ -353,6 +369,9 @@ def main():
     headline = args.workload == "c2_decode_bf16_32k"
     if headline and args.prefill:
         line["prefill_32k"] = prefill_line(torch, B, make_case, 3)
+        if args.extra:
+            line["prefill_32k_quantised_indexer"] = {
+                n: prefill_line(torch, B, make_case, 3, n) for n in ("c3_prefill_fp8", "c3_prefill_mxfp8")}
     if headline and args.extra:
         line["prolog"] = prolog_line(torch, B, make_case, 50, 5)
     if headline and args.extra:

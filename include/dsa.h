@@ -234,7 +234,11 @@ dsa_status dsa_fused_decode(const dsa_batch* batch, const dsa_indexer_args* iarg
  * Dive into Hybrid Architecture Acceleration", section 4 (its zigzag layout),
  * where it balances devices; here it balances workgroups of one GPU.  The
  * indexer scores and selection follow the same pages' section 2 (indexer)
- * and the sparse attention their section 3.1, as for dsa_fused_decode.       */
+ * and the sparse attention their section 3.1, as for dsa_fused_decode.  The
+ * indexer may be bf16, DSA_FP8_E4M3 or DSA_MXFP8_E4M3 here as in decode (the
+ * fused indexer serves both phases quantised: the Day0 page, section 2); an
+ * MXFP8 k_cache->scale must then be 4-byte aligned (each row's 4 scale bytes
+ * are read as one word), else DSA_ERR_INVALID_ARG.                          */
 dsa_status dsa_fused_prefill(const dsa_batch* batch, const dsa_indexer_args* iargs,
                              const dsa_sfa_args* sargs, int32_t q_block, void* out,
                              float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,

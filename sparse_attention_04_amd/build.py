@@ -19,14 +19,14 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 SOURCES = ["dsa_api.cpp", "indexer_decode.hip", "indexer_prefill.hip", "sfa.hip", "noalloc.hip", "prolog.hip",
-           "checks.hip"]
+           "checks.hip", "fused_decode.hip"]
 
 # Kernels that issue LDS reads through inline assembly and wait for them later
 # with an explicit lgkmcnt: the compiler takes an asm result as ready at once,
 # so a spill or copy of such a register before the wait would read stale data.
 # Their build must report no scratch and no spills, and their device assembly
 # must not touch such a register before a wait that covers its read.
-NO_SPILL = {"sfa.hip": ("sfa_bf16_kernel",)}
+NO_SPILL = {"sfa.hip": ("sfa_bf16_kernel",), "fused_decode.hip": ("fused_decode_kernel",)}
 
 
 def hipcc() -> str:

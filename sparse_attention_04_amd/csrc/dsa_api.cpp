@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -218,6 +219,50 @@ bool profile_mode() {
 
 // ------------------------------------------------------------ launchers ---
 
+IndexerDecodeParams indexer_decode_params(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out,
+                                          uint32_t* ws, int grid, int chunk_cap, int stage) {
+  IndexerDecodeParams p{};
+  p.bv = view_of(b, a->k_cache->page_size);
+  p.q = a->q;
+  p.q_scale = a->q_scale;
+  p.w = a->head_weights;
+  p.k_data = a->k_cache->data;
+  p.k_scale = a->k_cache->scale;
+  p.topk = a->topk;
+  p.idx_out = idx_out;
+  p.ws = ws;
+  p.ws_nseq = b->batch;
+  p.ws_nq = b->total_q;
+  p.ws_grid_pad = (kMaxGrid + 31) / 32 * 32;
+  p.grid = grid;
+  p.chunk_cap = chunk_cap;
+  p.stage_pages = stage;
+  p.spin_limit = kSpinLimit;
+  p.barrier_slack = 0;
+  if (force_timeout_mode()) {
+    // test hook: no barrier can complete, and every wait gives up quickly
+    p.spin_limit = 64;
+    p.barrier_slack = 1u << 30;
+  }
+  return p;
+}
+
+// DSA_DEBUG: wait for the call and report the error bits its bounded waits set.
+dsa_status debug_error_bits(uint32_t* ws, hipStream_t st) {
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "indexer (debug sync)");
+  uint32_t flags = 0;
+  e = hipMemcpy(&flags, ws, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "indexer (debug flags)");
+  if (flags) {
+    const uint32_t zero = 0;
+    e = hipMemcpy(ws, &zero, 4, hipMemcpyHostToDevice);   // report each failure once
+    if (e != hipSuccess) return hip_fail(e, "indexer (debug flags reset)");
+    return fail(DSA_ERR_HIP, "indexer reported error bits 0x%x (bounded wait expired or LDS bound)", flags);
+  }
+  return DSA_OK;
+}
+
 dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out,
                               uint32_t* ws, hipStream_t st) {
   if (b->total_q == 0) return DSA_OK;
@@ -261,28 +306,7 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
   }
   if (grid == 0) return fail(DSA_ERR_UNSUPPORTED, "context too long for the decode indexer's on-chip score buffer");
 
-  IndexerDecodeParams p{};
-  p.q = a->q;
-  p.q_scale = a->q_scale;
-  p.w = a->head_weights;
-  p.k_data = a->k_cache->data;
-  p.k_scale = a->k_cache->scale;
-  p.topk = a->topk;
-  p.idx_out = idx_out;
-  p.ws = ws;
-  p.ws_nseq = b->batch;
-  p.ws_nq = b->total_q;
-  p.ws_grid_pad = (kMaxGrid + 31) / 32 * 32;
-  p.grid = grid;
-  p.chunk_cap = chunk_cap;
-  p.stage_pages = stage;
-  p.spin_limit = kSpinLimit;
-  p.barrier_slack = 0;
-  if (force_timeout_mode()) {
-    // test hook: no barrier can complete, and every wait gives up quickly
-    p.spin_limit = 64;
-    p.barrier_slack = 1u << 30;
-  }
+  IndexerDecodeParams p = indexer_decode_params(b, a, idx_out, ws, grid, chunk_cap, stage);
   for (int b0 = 0; b0 < b->batch; b0 += sub) {
     const int nb = std::min(sub, b->batch - b0);
     p.bv = view_of(b, P);
@@ -294,20 +318,7 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
     e = launch_indexer_decode(dt, a->n_heads, a->head_dim, maxq, p, st);
     if (e != hipSuccess) return hip_fail(e, "indexer launch");
   }
-  if (debug_mode()) {
-    e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e, "indexer (debug sync)");
-    uint32_t flags = 0;
-    e = hipMemcpy(&flags, ws, 4, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return hip_fail(e, "indexer (debug flags)");
-    if (flags) {
-      const uint32_t zero = 0;
-      e = hipMemcpy(ws, &zero, 4, hipMemcpyHostToDevice);   // report each failure once
-      if (e != hipSuccess) return hip_fail(e, "indexer (debug flags reset)");
-      return fail(DSA_ERR_HIP, "indexer reported error bits 0x%x (bounded wait expired or LDS bound)", flags);
-    }
-  }
-  return DSA_OK;
+  return debug_mode() ? debug_error_bits(ws, st) : DSA_OK;
 }
 
 dsa_status run_indexer_prefill(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out, hipStream_t st) {
@@ -345,17 +356,13 @@ dsa_status run_indexer(const dsa_batch* b, const dsa_indexer_args* a, int32_t* i
   return run_indexer_prefill(b, a, idx_out, st);
 }
 
-dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx, int topk,
-                   void* out, float* lse, unsigned char* ws, hipStream_t st) {
-  if (b->total_q == 0) return DSA_OK;
-  const bool bf16 = (a->q_dtype == DSA_BF16);
-  const bool kv8 = (a->kv_cache->dtype == DSA_FP8_E4M3_TILE128);
-  const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, bf16, kv8);
+SfaParams sfa_params(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx, int topk, void* out,
+                     float* lse, unsigned char* ws, const SfaPlan& pl) {
   SfaParams p{};
   p.bv = view_of(b, a->kv_cache->page_size);
   p.q = a->q;
   p.kv = a->kv_cache->data;
-  p.kv8 = kv8 ? 1 : 0;
+  p.kv8 = (a->kv_cache->dtype == DSA_FP8_E4M3_TILE128) ? 1 : 0;
   p.kv_scale = p.kv8 ? (const float*)a->kv_cache->scale : nullptr;
   p.idx = idx;
   p.topk = topk;
@@ -373,12 +380,89 @@ dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx
   p.part_o = (float*)ws;
   p.part_ml = (float*)(ws + pl.part_o_bytes);
   p.dbg = profile_mode() ? (unsigned long long*)(ws + pl.part_o_bytes + pl.part_ml_bytes) : nullptr;
+  return p;
+}
+
+dsa_status run_sfa(const dsa_batch* b, const dsa_sfa_args* a, const int32_t* idx, int topk,
+                   void* out, float* lse, unsigned char* ws, hipStream_t st) {
+  if (b->total_q == 0) return DSA_OK;
+  const bool bf16 = (a->q_dtype == DSA_BF16);
+  const bool kv8 = (a->kv_cache->dtype == DSA_FP8_E4M3_TILE128);
+  const SfaPlan pl = plan_sfa(b, a->n_heads, a->v_dim, topk, bf16, kv8);
+  const SfaParams p = sfa_params(b, a, idx, topk, out, lse, ws, pl);
   const int dt = dt_kernel(a->q_dtype);
   hipError_t e = launch_sfa(dt, a->n_heads, a->qk_dim, a->v_dim, p, st);
   if (e != hipSuccess) return hip_fail(e, "sfa launch");
   e = launch_sfa_combine(dt, a->n_heads, a->v_dim, p, st);
   if (e != hipSuccess) return hip_fail(e, "sfa combine launch");
   return DSA_OK;
+}
+
+
+// The fused decode kernel (indexer and attention in one launch, the combine
+// after it) serves a decode call when its shapes have an instance, the whole
+// batch fits one indexer launch of one workgroup per CU (every sequence with
+// at least two workgroups' worth of slack, as for the indexer alone), and the
+// attention's tasks fit that grid, one per workgroup.  Otherwise, or with
+// DSA_FUSED_KERNEL=0, the call runs the two stages as separate kernels.
+// `launched` tells which happened.
+bool fused_kernel_enabled() {
+  const char* s = getenv("DSA_FUSED_KERNEL");
+  return !(s && s[0] == '0');
+}
+
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t e;
+  do {
+    e = counter.fetch_add(1u) + 1u;
+  } while (e == 0u);   // 0 is a cleared ready word
+  return e;
+}
+
+dsa_status run_fused_kernel(const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa, int32_t* idx,
+                            void* out, float* lse, uint32_t* ws, unsigned char* sfa_ws, hipStream_t st,
+                            bool& launched) {
+  launched = false;
+  if (!fused_kernel_enabled() || b->total_q == 0 || b->max_q_len > kMaxDecodeQ) return DSA_OK;
+  if (sa->q_dtype != DSA_BF16 || sa->kv_cache->dtype == DSA_FP8_E4M3_TILE128 || sa->n_heads != 128 ||
+      sa->qk_dim != 576 || sa->v_dim != 512)
+    return DSA_OK;
+  const int maxq = (b->max_q_len <= 1) ? 1 : kMaxDecodeQ;
+  const int dt = dt_kernel(ia->q_dtype);
+  const SfaPlan pl = plan_sfa(b, sa->n_heads, sa->v_dim, ia->topk, true, false);
+  const bool lo = (int64_t)b->total_q < kSfaTargetWG;
+  if (!fused_decode_supported(dt, maxq, lo) || pl.hsplit != 1 || pl.rows_per_split > fused_decode_max_rows())
+    return DSA_OK;
+  DeviceInfo di;
+  dsa_status s = device_info(di);
+  if (s != DSA_OK) return s;
+  const int G = std::min(kMaxGrid, di.cus) / 8 * 8;
+  const int64_t tasks = 8 * (int64_t)((b->total_q + 7) / 8) * pl.splits;
+  if (G < 8 || tasks > G || b->batch > G / 2) return DSA_OK;
+  // the indexer's geometry for one launch over the whole batch, as the
+  // indexer alone computes it
+  const int P = ia->k_cache->page_size;
+  const int maxp = (b->max_seq_len + P - 1) / P;
+  const int64_t cap_pages = ((int64_t)b->batch * std::max(1, maxp) + (G - b->batch) - 1) / (G - b->batch);
+  const int64_t cap_keys = (cap_pages * P + 7) / 8 * 8;
+  const int64_t stage_pages = cap_pages + 1;
+  if (cap_keys > (1 << 24)) return DSA_OK;
+  const size_t lds = std::max(indexer_decode_lds_bytes(dt, maxq, (int)cap_keys, (int)stage_pages),
+                              fused_decode_sfa_lds_bytes(pl.rows_per_split));
+  if (lds > kLdsMax) return DSA_OK;
+  int occ = 0;
+  hipError_t e = fused_decode_occupancy(dt, maxq, lo, lds, &occ);
+  if (e != hipSuccess) return hip_fail(e, "occupancy query (fused decode)");
+  if (occ < 1) return DSA_OK;
+  const IndexerDecodeParams ip = indexer_decode_params(b, ia, idx, ws, G, (int)cap_keys, (int)stage_pages);
+  const SfaParams sp = sfa_params(b, sa, idx, ia->topk, out, lse, sfa_ws, pl);
+  e = launch_fused_decode(dt, maxq, ip, sp, next_epoch(), lds, st);
+  if (e != hipSuccess) return hip_fail(e, "fused decode launch");
+  e = launch_sfa_combine(kBF16, sa->n_heads, sa->v_dim, sp, st);
+  if (e != hipSuccess) return hip_fail(e, "sfa combine launch");
+  launched = true;
+  return debug_mode() ? debug_error_bits(ws, st) : DSA_OK;
 }
 
 // Workspace layout.  The zero state (the decode indexer's cross-workgroup
@@ -509,6 +593,9 @@ dsa_status fused_decode_impl(const dsa_batch* b, const dsa_indexer_args* ia, con
                           nullptr, 0, st);
     if (s != DSA_OK) return s;
   }
+  bool launched = false;
+  s = run_fused_kernel(b, ia, sa, idx, out, lse, (uint32_t*)ws, scr + rows, st, launched);
+  if (s != DSA_OK || launched) return s;
   s = run_indexer(b, ia, idx, (uint32_t*)ws, st);
   if (s != DSA_OK) return s;
   return run_sfa(b, sa, idx, ia->topk, out, lse, scr + rows, st);

@@ -116,6 +116,16 @@ struct SfaParams {
 };
 
 hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hipStream_t st);
+
+// ------------------------------------------------------------- fused decode ---
+// The decode indexer and the bf16 SFA (H = 128, 576/512, bf16 rows) in one
+// launch of one workgroup per CU; the combine follows as its own kernel.
+bool fused_decode_supported(int dtype, int maxq, bool precise_weights);
+size_t fused_decode_sfa_lds_bytes(int rows_per_split);
+int fused_decode_max_rows();
+hipError_t fused_decode_occupancy(int dtype, int maxq, bool precise_weights, size_t lds, int* blocks_per_cu);
+hipError_t launch_fused_decode(int dtype, int maxq, const IndexerDecodeParams& ip, const SfaParams& sp,
+                               uint32_t epoch, size_t lds, hipStream_t st);
 hipError_t launch_sfa_combine(int dtype, int H, int Dv, const SfaParams& p, hipStream_t st);
 
 }  // namespace dsa

@@ -1,0 +1,117 @@
+"""The fused decode kernel (indexer and attention in one launch) against the
+two-kernel path of the same call (DSA_FUSED_KERNEL=0) and against the oracle.
+
+Both paths select the same index sets (exact Top-K); the order of positions
+within a row depends on which workgroup scored which pages, so rows are
+compared as sets, and the attention outputs, which sum the same rows split
+into differently ordered ranges, within the bf16 bar.  The per-sequence ready
+words the fused kernel uses must be left zero, so one workspace keeps serving
+calls of any shape."""
+import contextlib
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from checker import check_sfa, check_topk_row
+from sparse_attention_04_amd import binding as B
+from sparse_attention_04_amd.inputs import case_to, make_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    B.lib()
+
+
+@contextlib.contextmanager
+def _env(**kv):
+    old = {k: os.environ.get(k) for k in kv}
+    os.environ.update(kv)
+    try:
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def _fused(call):
+    out, lse, idx = call.fused_decode()
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+
+
+def _compare_paths(case, sample=None):
+    call = B.Call(case)
+    _say(f"{case.name} B={case.batch} T={case.total_q}: two-kernel path")
+    with _env(DSA_FUSED_KERNEL="0"):
+        out0, lse0, idx0 = _fused(call)
+    _say(f"{case.name}: fused kernel")
+    out1, lse1, idx1 = _fused(call)
+    assert np.array_equal(np.sort(idx0, 1), np.sort(idx1, 1))
+    # the same rows in other ranges: within a few bf16 ulps of each other
+    tol = 2.0 ** -7 * np.maximum(np.abs(out0), 1e-3) + 1e-4
+    assert np.all(np.abs(out0 - out1) <= tol), float(np.max(np.abs(out0 - out1)))
+    assert np.allclose(lse0, lse1, atol=1e-4, rtol=1e-5)
+    toks = range(case.total_q) if sample is None else sample
+    where = {case.token(b, i): (b, i) for b in range(case.batch) for i in range(int(case.q_lens_host[b]))}
+    for g in toks:
+        b, i = where[g]
+        ref = oracle.run_query(case, b, i)
+        check_topk_row(idx1[g], ref, case.topk)
+        sel = idx1[g][idx1[g] >= 0]
+        ref_o, _ = oracle.sfa_query(case, b, i, sel)
+        check_sfa(out1[g], ref_o, case.sfa_dtype)
+    return call
+
+
+def test_fused_kernel_matches_two_kernel_path_small():
+    case = case_to(make_case("c2_decode_bf16", 81, batch=5, seq_len_range=(2500, 9000)), "cuda")
+    _compare_paths(case)
+
+
+def test_fused_kernel_short_and_ragged_contexts():
+    # sequences that keep every position (no scores: published without a
+    # barrier), one just above k, ragged last pages, 16-token pages
+    case = case_to(make_case("c2_decode_bf16", 82, batch=4, seq_lens=[1, 2048, 2049, 5001], page_size=16),
+                   "cuda")
+    _compare_paths(case)
+
+
+def test_fused_kernel_full_size_32k():
+    _say("c2_decode_bf16_32k: generating on device")
+    case = make_case("c2_decode_bf16_32k", 83, device="cuda")
+    _compare_paths(case, sample=[0, 13, 31])
+
+
+def test_fused_kernel_leaves_ready_words_zero():
+    """Calls of different batch sizes on one workspace: the per-sequence state
+    (counters, ready words) is zero after each call and every call is right."""
+    small = case_to(make_case("c2_decode_bf16", 84, batch=2, seq_len_range=(3000, 5000)), "cuda")
+    big = case_to(make_case("c2_decode_bf16", 85, batch=7, seq_len_range=(3000, 9000)), "cuda")
+    calls = {c.batch: B.Call(c) for c in (small, big)}
+    need = max(call.workspace(B.DSA_OP_FUSED_DECODE)[1] for call in calls.values())
+    state = max(B.dsa_workspace_size(B.DSA_OP_INDEXER_TOPK, call.batch, call.iargs, call.sargs)
+                for call in calls.values())
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for k, case in enumerate((small, big, small, big)):
+        call = calls[case.batch]
+        _say(f"shared workspace, call {k}: B={case.batch}")
+        call.use_workspace(B.DSA_OP_FUSED_DECODE, ws)
+        out, lse, idx = _fused(call)
+        assert int(ws[256:state].count_nonzero()) == 0, k
+        for b in range(case.batch):
+            check_topk_row(idx[case.token(b, 0)], oracle.run_query(case, b, 0), case.topk)

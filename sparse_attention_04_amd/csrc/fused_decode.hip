@@ -113,7 +113,12 @@ __global__ __launch_bounds__(kIdxThreads, 1) void fused_decode_kernel(IndexerDec
 
 #define DSA_FUSED_SHAPES(X) \
   X(kBF16, 1, true)         \
-  X(kBF16, 1, false)
+  X(kBF16, 1, false)        \
+  X(kBF16, 4, true)         \
+  X(kFP8, 1, true)          \
+  X(kMX, 1, true)           \
+  X(kFP8, 4, true)          \
+  X(kMX, 4, true)
 
 const void* pick_fused(int dtype, int maxq, bool lo) {
 #define DSA_PICK(DT_, Q_, LO_) \

@@ -7,9 +7,9 @@ from sparse_attention_04_amd.build import check_no_spills
 R = "x.hip:1:1: remark: {} [-Rpass-analysis=kernel-resource-usage]"
 
 
-def _remarks(name, scratch=0, vspill=0):
+def _remarks(name, scratch=0, vspill=0, sspill=0):
     return "\n".join(R.format(t) for t in [f"Function Name: {name}", "VGPRs: 256",
-                                            f"ScratchSize [bytes/lane]: {scratch}", "SGPRs Spill: 0",
+                                            f"ScratchSize [bytes/lane]: {scratch}", f"SGPRs Spill: {sspill}",
                                             f"VGPRs Spill: {vspill}"])
 
 
@@ -20,6 +20,12 @@ def test_clean_kernel_passes():
 @pytest.mark.parametrize("kw", [dict(scratch=16), dict(vspill=3)])
 def test_spills_are_reported(kw):
     assert check_no_spills(_remarks("_ZN3dsa15sfa_bf16_kernelI", **kw), ("sfa_bf16_kernel",))
+
+
+def test_sgpr_spills_to_vgpr_lanes_pass():
+    # SGPR spills without scratch land in lanes of reserved VGPRs
+    assert check_no_spills(_remarks("_ZN3dsa15sfa_bf16_kernelI", sspill=40), ("sfa_bf16_kernel",)) == []
+    assert check_no_spills(_remarks("_ZN3dsa15sfa_bf16_kernelI", sspill=40, scratch=8), ("sfa_bf16_kernel",))
 
 
 def test_other_kernels_are_ignored_but_some_must_be_seen():

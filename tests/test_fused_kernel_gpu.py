@@ -62,9 +62,12 @@ def _compare_paths(case, sample=None):
     _say(f"{case.name}: fused kernel")
     out1, lse1, idx1 = _fused(call)
     assert np.array_equal(np.sort(idx0, 1), np.sort(idx1, 1))
-    # the same rows in other ranges: within a few bf16 ulps of each other
-    tol = 2.0 ** -7 * np.maximum(np.abs(out0), 1e-3) + 1e-4
-    assert np.all(np.abs(out0 - out1) <= tol), float(np.max(np.abs(out0 - out1)))
+    # the same rows in other ranges: the fp16 partials (2^-11 of max|V|) and
+    # the bf16 output rounding differ, so two bf16 ulps apart at most; each
+    # path is held to the oracle's bar below
+    mag = np.maximum(np.abs(out0), np.abs(out1))
+    tol = 2.0 ** -6 * mag + 2.0 ** -10
+    assert np.all(np.abs(out0 - out1) <= tol), float(np.max(np.abs(out0 - out1) - tol))
     assert np.allclose(lse0, lse1, atol=1e-4, rtol=1e-5)
     toks = range(case.total_q) if sample is None else sample
     where = {case.token(b, i): (b, i) for b in range(case.batch) for i in range(int(case.q_lens_host[b]))}
@@ -88,6 +91,20 @@ def test_fused_kernel_short_and_ragged_contexts():
     # barrier), one just above k, ragged last pages, 16-token pages
     case = case_to(make_case("c2_decode_bf16", 82, batch=4, seq_lens=[1, 2048, 2049, 5001], page_size=16),
                    "cuda")
+    _compare_paths(case)
+
+
+def test_fused_kernel_multi_token():
+    # 4, 2, 3 and 1 query tokens per sequence (causal among them), two of them
+    # close to k
+    case = case_to(make_case("c5_decode4", 86, batch=4, seq_lens=[2050, 5000, 2049, 6000],
+                             q_lens=[4, 2, 3, 1]), "cuda")
+    _compare_paths(case)
+
+
+@pytest.mark.parametrize("name", ["c4_decode_fp8", "c4_decode_mxfp8"])
+def test_fused_kernel_quantised_indexer(name):
+    case = case_to(make_case(name, 87, batch=3, seq_len_range=(3000, 7000)), "cuda")
     _compare_paths(case)
 
 

@@ -219,7 +219,16 @@ dsa_status dsa_sparse_attn(const dsa_batch* batch, const dsa_sfa_args* args,
                            void* ws, size_t ws_bytes, void* stream);
 
 /* Decode step (small T_b): indexer + Top-K, then SFA on the selected rows.
- * idx_out may be NULL (the indices then live in the workspace).              */
+ * idx_out may be NULL (the indices then live in the workspace).
+ * The two operators run fused in one kernel where the shapes allow it (bf16
+ * SFA over bf16 rows with 128 heads and 576/512 dims; the indexer in bf16,
+ * FP8 or MXFP8; at most as many (token, slot range) tasks as the device has
+ * compute units): each sequence's attention starts as soon as its own index
+ * rows are complete, the deep fusion of LI and SFA of "Day0 Inference
+ * Optimization on Ascend CANN", section 2.  Results are those of the two
+ * separate operators up to the order of positions within an index row (and
+ * the rounding that order brings).  DSA_FUSED_KERNEL=0 in the environment
+ * selects the two-kernel path.                                              */
 dsa_status dsa_fused_decode(const dsa_batch* batch, const dsa_indexer_args* iargs,
                             const dsa_sfa_args* sargs, void* out, float* lse,
                             int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);

@@ -313,11 +313,18 @@ def main():
 
     a = algorithmic(case)
     tokens = case.total_q
-    # The dominant kernel: dsa_indexer_topk is one launch of the decode
-    # indexer kernel, so back-to-back calls timed with events on the stream it
-    # runs on give that kernel's average duration (plus the inter-launch gap);
-    # dsa_sparse_attn is two launches (attention and the split combine).
-    kern = {"indexer_decode_kernel": (ms_idx, a["indexer_bytes"]),
+    # The dominant kernel of the step.  dsa_fused_decode is the fused decode
+    # kernel (indexer and attention in one launch) followed by the split
+    # combine, so back-to-back calls timed with events on the stream they run
+    # on give the pair's average duration (with the gaps); its algorithmic
+    # bytes are the step's.  The separate stages (dsa_indexer_topk: one
+    # launch of the decode indexer kernel; dsa_sparse_attn: attention and
+    # combine) are timed the same way and reported beside it.
+    fused = os.environ.get("DSA_FUSED_KERNEL", "1") != "0"
+    step_kernels = ("fused_decode_kernel+sfa_combine_kernel" if fused else
+                    "indexer_decode_kernel+sfa_bf16_kernel+sfa_combine_kernel")
+    kern = {step_kernels: (ms_step, a["fused_bytes"]),
+            "indexer_decode_kernel": (ms_idx, a["indexer_bytes"]),
             "sfa_bf16_kernel+sfa_combine_kernel": (ms_sfa, a["sfa_bytes"])}
     dom = max(kern, key=lambda k: kern[k][0])
     dms, dbytes = kern[dom]
@@ -327,7 +334,7 @@ def main():
     if os.path.exists(prof):
         try:
             tr = json.load(open(prof))
-            ent = tr.get(args.workload, {}).get(dom.split("+")[0])
+            ent = tr.get(args.workload, {}).get(dom)
             if ent and ent.get("kernel_source_sha") == _kernel_sha():
                 traffic = ent["bytes_per_launch"]
         except Exception:
@@ -354,6 +361,7 @@ def main():
             "page_size": case.page_size, "value_sets_rotated": R,
         },
         "stages_ms": {"fused_step": ms_step, "indexer_topk": ms_idx, "sparse_attn": ms_sfa},
+        "step_kernels": step_kernels,
         "algorithmic": {"fused_step_bytes": a["fused_bytes"], "indexer_bytes": a["indexer_bytes"],
                         "sfa_bytes": a["sfa_bytes"], "indexer_flops_per_head": a["indexer_flops"],
                         "sfa_flops": a["sfa_flops"]},

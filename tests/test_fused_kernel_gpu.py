@@ -108,6 +108,18 @@ def test_fused_kernel_quantised_indexer(name):
     _compare_paths(case)
 
 
+@pytest.mark.parametrize("q_lens", [[2, 0, 3], [1, 0, 1]])
+def test_fused_kernel_sequence_without_query_tokens(q_lens):
+    # a sequence with cached keys but no new token: its indexer workgroups
+    # publish nothing, no attention task waits for it, and its state words
+    # end zero like the others'
+    case = case_to(make_case("c5_decode4", 88, batch=3, seq_lens=[3000, 2500, 4000], q_lens=q_lens), "cuda")
+    call = _compare_paths(case)
+    ws, _ = call.workspace(B.DSA_OP_FUSED_DECODE)
+    state = B.dsa_workspace_size(B.DSA_OP_INDEXER_TOPK, call.batch, call.iargs, call.sargs)
+    assert int(ws[256:state].count_nonzero()) == 0
+
+
 def test_fused_kernel_full_size_32k():
     _say("c2_decode_bf16_32k: generating on device")
     case = make_case("c2_decode_bf16_32k", 83, device="cuda")

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void indexer_decode_kernel(IndexerD
 // what the device holds at once), and kernels on one stream run one after
 // another, so a plain launch is resident as a whole unless other work shares
 // the device; then the bounded waits give up, the affected rows are poisoned
-// and the error bit is set (see the end of the kernel).  A cooperative launch
+// and the error bit is set (the end of indexer_decode_body).  A cooperative launch
 // would have the runtime guarantee residency, but it measured about 11 us of
 // idle device time before and after each launch on this part (74 us kernel,
 // 22 us of gaps per call).

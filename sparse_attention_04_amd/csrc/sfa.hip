@@ -11,9 +11,9 @@
 //
 // bf16 kernel (H = 128, Dqk = 576, Dv = 512): a workgroup owns one query token,
 // all of its heads (half of them over an FP8 cache) and a contiguous range of
-// index slots.  Per tile of 32
-// slots it gathers the 32 latent rows through the block table into LDS (a
-// 4-deep ring), then every wave (32 heads) computes
+// index slots.  Per tile of 32 slots it gathers the 32 latent rows through the
+// block table into LDS (a 4-deep ring), then every wave (16 heads: 8 waves
+// over bf16 rows, 4 over FP8 rows) computes
 //   S^T[row, head] = KV[row, :] . q[head, :]     (16x16x32 bf16 MFMAs, rows on M)
 // so that after the softmax weights are formed the probabilities already sit in the
 // B-operand layout of the second product

@@ -40,6 +40,11 @@
  *     4-byte aligned.  A misaligned pointer is DSA_ERR_INVALID_ARG.
  *   Ordering: work is enqueued asynchronously on `stream` (a hipStream_t, NULL
  *     = the default stream); nothing is waited for.
+ *   Empty calls: with total_q = 0 (every sequence without a new query token)
+ *     a call validates its arguments as usual and returns DSA_OK having
+ *     computed nothing; the arrays with one entry per query token (q, head
+ *     weights, q scales, outputs, index rows, the prolog's x) may then be
+ *     NULL.
  *   Errors: arguments are validated on the host before anything is enqueued;
  *     a failed check returns its status and enqueues nothing.  A failed launch
  *     returns DSA_ERR_HIP.  dsa_last_error() returns a thread-local message for

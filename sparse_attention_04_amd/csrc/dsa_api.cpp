@@ -92,7 +92,9 @@ dsa_status check_cache(const dsa_paged_cache* c, const char* name, int dim, int 
 
 dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
   if (!a) return fail(DSA_ERR_INVALID_ARG, "indexer args are NULL");
-  if (!a->q || !a->head_weights) return fail(DSA_ERR_INVALID_ARG, "indexer q / head_weights are NULL");
+  // arrays with one entry per query token may be NULL when there is none
+  const bool any_q = b->total_q > 0;
+  if (any_q && (!a->q || !a->head_weights)) return fail(DSA_ERR_INVALID_ARG, "indexer q / head_weights are NULL");
   if (!aligned(a->q, 16) || !aligned(a->head_weights, 4) || (a->q_dtype == DSA_FP8_E4M3 && !aligned(a->q_scale, 4)))
     return fail(DSA_ERR_INVALID_ARG, "indexer q must be 16-byte aligned, head_weights and fp8 q_scale 4-byte aligned");
   if (a->topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", a->topk);
@@ -102,14 +104,14 @@ dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
   if (!ok_shape)
     return fail(DSA_ERR_UNSUPPORTED, "indexer shape (dtype %d, heads %d, dim %d) is not compiled in; supported: f32 4x32, bf16/fp8/mxfp8 64x128",
                 a->q_dtype, a->n_heads, a->head_dim);
-  if ((a->q_dtype == DSA_FP8_E4M3 || a->q_dtype == DSA_MXFP8_E4M3) && !a->q_scale)
+  if (any_q && (a->q_dtype == DSA_FP8_E4M3 || a->q_dtype == DSA_MXFP8_E4M3) && !a->q_scale)
     return fail(DSA_ERR_INVALID_ARG, "indexer q_scale is NULL for a quantised dtype");
   return check_cache(a->k_cache, "k_cache", a->head_dim, a->q_dtype, b);
 }
 
 dsa_status check_sfa(const dsa_batch* b, const dsa_sfa_args* a) {
   if (!a) return fail(DSA_ERR_INVALID_ARG, "sfa args are NULL");
-  if (!a->q) return fail(DSA_ERR_INVALID_ARG, "sfa q is NULL");
+  if (!a->q && b->total_q > 0) return fail(DSA_ERR_INVALID_ARG, "sfa q is NULL");
   if (!aligned(a->q, 16)) return fail(DSA_ERR_INVALID_ARG, "sfa q must be 16-byte aligned");
   if (a->q_dtype != DSA_F32 && a->q_dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "sfa dtype %d not supported (f32, bf16)", a->q_dtype);
   const bool ok_shape = (a->q_dtype == DSA_F32 && a->n_heads == 8 && a->qk_dim == 80 && a->v_dim == 64) ||
@@ -528,7 +530,7 @@ dsa_status dsa_indexer_topk(const dsa_batch* b, const dsa_indexer_args* a, int32
   dsa_status s = check_batch(b);
   if (s == DSA_OK) s = check_indexer(b, a);
   if (s != DSA_OK) return s;
-  if (!idx_out) return fail(DSA_ERR_INVALID_ARG, "idx_out is NULL");
+  if (!idx_out && b->total_q > 0) return fail(DSA_ERR_INVALID_ARG, "idx_out is NULL");
   if (!aligned(idx_out, 4) || !aligned(ws, 16)) return fail(DSA_ERR_INVALID_ARG, "idx_out must be 4-byte, ws 16-byte aligned");
   const size_t need = dsa_workspace_size(DSA_OP_INDEXER_TOPK, b, a, nullptr);
   if (ws_bytes < need || (!ws && need)) return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -545,7 +547,7 @@ dsa_status dsa_sparse_attn(const dsa_batch* b, const dsa_sfa_args* a, const int3
   dsa_status s = check_batch(b);
   if (s == DSA_OK) s = check_sfa(b, a);
   if (s != DSA_OK) return s;
-  if (!idx || !out) return fail(DSA_ERR_INVALID_ARG, "idx / out is NULL");
+  if ((!idx || !out) && b->total_q > 0) return fail(DSA_ERR_INVALID_ARG, "idx / out is NULL");
   if (!aligned(idx, 4) || !aligned(out, 16) || !aligned(lse, 4) || !aligned(ws, 16))
     return fail(DSA_ERR_INVALID_ARG, "out and ws must be 16-byte, idx and lse 4-byte aligned");
   if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", topk);
@@ -576,7 +578,7 @@ dsa_status fused_decode_impl(const dsa_batch* b, const dsa_indexer_args* ia, con
   if (s == DSA_OK) s = check_indexer(b, ia);
   if (s == DSA_OK) s = check_sfa(b, sa);
   if (s != DSA_OK) return s;
-  if (!out) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
+  if (!out && b->total_q > 0) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
   if (!aligned(out, 16) || !aligned(lse, 4) || !aligned(idx_out, 4) || !aligned(ws, 16))
     return fail(DSA_ERR_INVALID_ARG, "out and ws must be 16-byte, lse and idx_out 4-byte aligned");
   if (ia->k_cache->page_size != sa->kv_cache->page_size)
@@ -624,7 +626,8 @@ dsa_status dsa_indexer_prolog(const dsa_batch* b, const dsa_prolog_args* a, void
   dsa_status s = check_batch(b);
   if (s != DSA_OK) return s;
   if (!a) return fail(DSA_ERR_INVALID_ARG, "prolog args are NULL");
-  if (!a->x || !a->w_q || !a->w_k || !a->w_w || !a->ln_gamma || !a->ln_beta)
+  const bool any_q = b->total_q > 0;   // x and the outputs have one row per query token
+  if ((any_q && !a->x) || !a->w_q || !a->w_k || !a->w_w || !a->ln_gamma || !a->ln_beta)
     return fail(DSA_ERR_INVALID_ARG, "prolog x, weights and LayerNorm parameters must be non-NULL");
   if (a->out_dtype != DSA_BF16 && a->out_dtype != DSA_FP8_E4M3 && a->out_dtype != DSA_MXFP8_E4M3)
     return fail(DSA_ERR_UNSUPPORTED, "prolog out_dtype %d: bf16, fp8 or mxfp8", a->out_dtype);
@@ -636,7 +639,7 @@ dsa_status dsa_indexer_prolog(const dsa_batch* b, const dsa_prolog_args* a, void
                 prolog_d_model_unit());
   if (!(a->ln_eps >= 0.f) || !(a->ln_eps < 1e30f)) return fail(DSA_ERR_INVALID_ARG, "ln_eps must be finite and >= 0");
   const bool quant = a->out_dtype != DSA_BF16;
-  if (!q_out || !w_out || (quant && !q_scale_out))
+  if (any_q && (!q_out || !w_out || (quant && !q_scale_out)))
     return fail(DSA_ERR_INVALID_ARG, "q_out, w_out (and q_scale_out for a quantised dtype) must be non-NULL");
   if (!aligned(a->x, 16) || !aligned(a->w_q, 16) || !aligned(a->w_k, 16) || !aligned(a->w_w, 16) ||
       !aligned(q_out, 16) || !aligned(w_out, 16) || !aligned(q_bf16_out, 16) || !aligned(k_bf16_out, 4) ||
@@ -687,7 +690,7 @@ dsa_status dsa_fused_prefill(const dsa_batch* b, const dsa_indexer_args* ia, con
   if (s == DSA_OK) s = check_indexer(b, ia);
   if (s == DSA_OK) s = check_sfa(b, sa);
   if (s != DSA_OK) return s;
-  if (!out) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
+  if (!out && b->total_q > 0) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
   if (!aligned(out, 16) || !aligned(lse, 4) || !aligned(idx_out, 4) || !aligned(ws, 16))
     return fail(DSA_ERR_INVALID_ARG, "out and ws must be 16-byte, lse and idx_out 4-byte aligned");
   if (q_block != 64) return fail(DSA_ERR_UNSUPPORTED, "q_block must be 64 (got %d)", q_block);

@@ -160,3 +160,38 @@ def test_misaligned_pointers_are_rejected(what):
                                   ctypes.c_void_p(out), None, None, ctypes.c_void_p(ws), need, None)
     assert st == B.DSA_ERR_INVALID_ARG, B.lib().dsa_last_error()
     assert b"align" in B.lib().dsa_last_error()
+
+
+def test_empty_calls_return_ok_without_per_token_arrays():
+    """total_q = 0: every entry point validates and returns DSA_OK without
+    computing, and the per-token arrays may be NULL (nothing is enqueued, so
+    the fake batch and workspace pointers are never used)."""
+    batch, ia, sa, keep = _structs()
+    batch.total_q = 0
+    batch.max_q_len = 0
+    ia.q = ia.q_scale = ia.head_weights = None
+    sa.q = None
+    lib = B.lib()
+    bp, ip, sp = ctypes.pointer(batch), ctypes.pointer(ia), ctypes.pointer(sa)
+    ws = ctypes.c_void_p(0x4000)
+    n = B.dsa_workspace_size(B.DSA_OP_FUSED_DECODE, batch, ia, sa)
+    assert lib.dsa_fused_decode(bp, ip, sp, None, None, None, ws, n, None) == B.DSA_OK, lib.dsa_last_error()
+    n = B.dsa_workspace_size(B.DSA_OP_INDEXER_TOPK, batch, ia, sa)
+    assert lib.dsa_indexer_topk(bp, ip, None, ws, n, None) == B.DSA_OK, lib.dsa_last_error()
+    n = B.dsa_workspace_size(B.DSA_OP_SPARSE_ATTN, batch, ia, sa)
+    assert lib.dsa_sparse_attn(bp, sp, None, 2048, None, None, ws, n, None) == B.DSA_OK, lib.dsa_last_error()
+    n = B.dsa_workspace_size(B.DSA_OP_FUSED_PREFILL, batch, ia, sa)
+    assert lib.dsa_fused_prefill(bp, ip, sp, 64, None, None, None, ws, n, None) == B.DSA_OK, lib.dsa_last_error()
+    fake = 0x1000
+    pa = B.dsa_prolog_args(None, 7168, fake, fake, fake, fake, fake, 1e-6, 64, 128, B.DSA_FP8_E4M3)
+    kc = B.dsa_paged_cache(fake, fake, B.DSA_FP8_E4M3, 16, 64, 128)
+    n = lib.dsa_prolog_workspace_size(bp, ctypes.pointer(pa))
+    assert lib.dsa_indexer_prolog(bp, ctypes.pointer(pa), None, None, None, ctypes.pointer(kc), None, None, ws, n,
+                                  None) == B.DSA_OK, lib.dsa_last_error()
+    # with a token the same NULL arrays are refused
+    batch.total_q = 1
+    batch.max_q_len = 1
+    assert lib.dsa_fused_decode(bp, ip, sp, None, None, None, ws, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_topk(bp, ip, None, ws, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_prolog(bp, ctypes.pointer(pa), None, None, None, ctypes.pointer(kc), None, None, ws,
+                                  1 << 30, None) == B.DSA_ERR_INVALID_ARG

@@ -138,3 +138,37 @@ def test_forced_timeout_poisons_rows_and_is_reported():
         idx = call.indexer_topk().clone()
     torch.cuda.synchronize()
     _check_all(case, idx)
+
+
+def test_empty_call_between_real_calls():
+    """Every sequence with cached keys but no new token (total_q = 0): the
+    decode entry points return without computing (the per-token tensors are
+    empty, their pointers NULL), and the workspaces they were given still
+    serve the next real call, whose rows and outputs match the oracle."""
+    empty = case_to(make_case("c5_decode4", 55, batch=3, seq_lens=[3000, 2500, 4000], q_lens=[0, 0, 0]), "cuda")
+    real = case_to(make_case("c2_decode_bf16", 56, batch=3, seq_len_range=(2500, 5000)), "cuda")
+    assert empty.total_q == 0
+    ce, cr = B.Call(empty), B.Call(real)
+    for op in (B.DSA_OP_FUSED_DECODE, B.DSA_OP_INDEXER_TOPK, B.DSA_OP_SPARSE_ATTN):
+        ws = torch.zeros(max(ce.workspace(op)[1], cr.workspace(op)[1]), dtype=torch.uint8, device="cuda")
+        ce.use_workspace(op, ws)
+        cr.use_workspace(op, ws)
+    _say("empty call: fused decode, indexer, sparse attention")
+    ce.fused_decode()
+    ce.indexer_topk()
+    ce.sparse_attn(ce.idx)
+    torch.cuda.synchronize()
+    ws, _ = cr.workspace(B.DSA_OP_FUSED_DECODE)
+    assert int(ws.count_nonzero()) == 0
+    _say(f"real call after it: {real.name} B={real.batch} T={real.total_q}")
+    out, lse, idx = (t.clone() for t in cr.fused_decode())
+    idx2 = cr.indexer_topk().clone()
+    torch.cuda.synchronize()
+    _check_all(real, idx)
+    _check_all(real, idx2)
+    out_h, idx_h = out.float().cpu().numpy(), idx.cpu().numpy()
+    for b in range(real.batch):
+        g = real.token(b, 0)
+        sel = idx_h[g][idx_h[g] >= 0]
+        ref_o, _ = oracle.sfa_query(real, b, 0, sel)
+        check_sfa(out_h[g], ref_o, real.sfa_dtype)

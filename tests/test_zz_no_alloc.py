@@ -87,3 +87,27 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     st = B.lib().dsa_fused_decode_noalloc(*(B.ctypes.pointer(x) for x in (call.batch, call.iargs, call.sargs)),
                                           call.out.data_ptr(), call.lse.data_ptr(), None, None)
     assert st == B.DSA_ERR_UNSUPPORTED and b"static scratch" in B.lib().dsa_last_error()
+
+
+def test_noalloc_empty_call_then_real_call():
+    """No new token in any sequence (total_q = 0): the call returns without
+    computing; the next call on the same static scratch is exact."""
+    assert torch.cuda.is_available()
+    B.lib()
+    empty = case_to(make_case("c5_decode4", 65, batch=2, seq_lens=[3000, 4000], q_lens=[0, 0]), "cuda")
+    real = case_to(make_case("c2_decode_bf16", 66, batch=3, seq_len_range=(2500, 6000)), "cuda")
+    ce, cr = B.Call(empty), B.Call(real)
+    _say("no-alloc: empty call")
+    ce.fused_decode_noalloc(ce.out, ce.lse, ce.idx)
+    _say(f"no-alloc: {real.name} B={real.batch} T={real.total_q} after it")
+    out, lse, idx = torch.empty_like(cr.out), torch.empty_like(cr.lse), torch.empty_like(cr.idx)
+    cr.fused_decode_noalloc(out, lse, idx)
+    torch.cuda.synchronize()
+    idx_h, out_h = idx.cpu().numpy(), out.float().cpu().numpy()
+    for b in range(real.batch):
+        g = real.token(b, 0)
+        ref = oracle.run_query(real, b, 0)
+        check_topk_row(idx_h[g], ref, real.topk)
+        sel = idx_h[g][idx_h[g] >= 0]
+        ref_o, _ = oracle.sfa_query(real, b, 0, sel)
+        check_sfa(out_h[g], ref_o, real.sfa_dtype)

@@ -314,6 +314,23 @@ const char* dsa_status_string(int32_t status);
 /* Thread-local description of the last failure in this thread ("" if none). */
 const char* dsa_last_error(void);
 
+/*
+ * dsa_take_device_errors -- whether a bounded cross-workgroup wait of the
+ * decode indexer gave up in any call since the last report, without running
+ * every call under DSA_DEBUG.  Such a call has already overwritten the
+ * affected index rows with -1 (see "Errors" above); this reports it on the
+ * host.
+ *   ws:     the workspace those calls used, whose first 4 bytes hold the
+ *           sticky error bits (16-byte aligned, device memory), or NULL for
+ *           this device's static scratch of dsa_fused_decode_noalloc (DSA_OK
+ *           if no such call ran on this device yet).
+ *   stream: synchronised first (a hipStream_t; NULL = the default stream).
+ * Returns DSA_ERR_HIP if any bit is set, clearing them (each failure is
+ * reported once), else DSA_OK.  It blocks: meant as a periodic check between
+ * steps, not for code under graph capture.
+ */
+dsa_status dsa_take_device_errors(void* ws, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

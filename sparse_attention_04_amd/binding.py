@@ -25,7 +25,8 @@ DTYPE_CODE = {"f32": DSA_F32, "bf16": DSA_BF16, "fp8": DSA_FP8_E4M3, "mxfp8": DS
 
 EXPORTED = ("dsa_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_fused_decode",
             "dsa_fused_prefill", "dsa_status_string", "dsa_last_error", "dsa_fused_decode_noalloc",
-            "dsa_noalloc_scratch_bytes", "dsa_indexer_prolog", "dsa_prolog_workspace_size")
+            "dsa_noalloc_scratch_bytes", "dsa_indexer_prolog", "dsa_prolog_workspace_size",
+            "dsa_take_device_errors")
 
 
 class DsaError(RuntimeError):
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_status_string.argtypes = [ctypes.c_int32]
         L.dsa_last_error.restype = ctypes.c_char_p
         L.dsa_last_error.argtypes = []
+        L.dsa_take_device_errors.restype = ctypes.c_int
+        L.dsa_take_device_errors.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         _LIB = L
     return _LIB
 
@@ -162,6 +165,13 @@ def dsa_fused_decode_noalloc(batch, iargs, sargs, out, lse, idx_out, stream=None
 
 def dsa_noalloc_scratch_bytes() -> int:
     return int(lib().dsa_noalloc_scratch_bytes())
+
+
+def dsa_take_device_errors(ws=None, stream=None):
+    """Raise DsaError(DSA_ERR_HIP) if a bounded wait of the decode indexer gave
+    up in a call on workspace `ws` (None: the static scratch of the
+    allocation-free entry point) since the last check; clears the bits."""
+    _check(lib().dsa_take_device_errors(_ptr(ws), _stream(stream)))
 
 
 def dsa_indexer_prolog(batch, pargs, q_out, q_scale_out, w_out, k_cache, q_bf16_out, k_bf16_out, ws, ws_bytes,

@@ -24,6 +24,14 @@ size_t fused_decode_state_bytes(const dsa_batch* b);
 dsa_status debug_check_batch(const dsa_batch* b, int num_pages, int page_size, const int32_t* idx, int topk,
                              hipStream_t st);
 
+// The current device's static scratch of dsa_fused_decode_noalloc, or NULL in
+// *out if no such call has set it up on this device yet.
+dsa_status noalloc_scratch_if_set_up(void** out);
+
+// Wait for `st`, then read and clear the sticky error bits in the first word
+// of an indexer workspace: DSA_ERR_HIP with a message if any was set.
+dsa_status take_error_bits(uint32_t* ws, hipStream_t st);
+
 // Record `msg` as the thread's last error and return `st`; clear it.
 dsa_status set_error(dsa_status st, const char* msg);
 void clear_error();

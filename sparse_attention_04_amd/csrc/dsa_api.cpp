@@ -249,21 +249,6 @@ IndexerDecodeParams indexer_decode_params(const dsa_batch* b, const dsa_indexer_
   return p;
 }
 
-// DSA_DEBUG: wait for the call and report the error bits its bounded waits set.
-dsa_status debug_error_bits(uint32_t* ws, hipStream_t st) {
-  hipError_t e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return hip_fail(e, "indexer (debug sync)");
-  uint32_t flags = 0;
-  e = hipMemcpy(&flags, ws, 4, hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return hip_fail(e, "indexer (debug flags)");
-  if (flags) {
-    const uint32_t zero = 0;
-    e = hipMemcpy(ws, &zero, 4, hipMemcpyHostToDevice);   // report each failure once
-    if (e != hipSuccess) return hip_fail(e, "indexer (debug flags reset)");
-    return fail(DSA_ERR_HIP, "indexer reported error bits 0x%x (bounded wait expired or LDS bound)", flags);
-  }
-  return DSA_OK;
-}
 
 dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out,
                               uint32_t* ws, hipStream_t st) {
@@ -320,7 +305,7 @@ dsa_status run_indexer_decode(const dsa_batch* b, const dsa_indexer_args* a, int
     e = launch_indexer_decode(dt, a->n_heads, a->head_dim, maxq, p, st);
     if (e != hipSuccess) return hip_fail(e, "indexer launch");
   }
-  return debug_mode() ? debug_error_bits(ws, st) : DSA_OK;
+  return debug_mode() ? take_error_bits(ws, st) : DSA_OK;
 }
 
 dsa_status run_indexer_prefill(const dsa_batch* b, const dsa_indexer_args* a, int32_t* idx_out, hipStream_t st) {
@@ -464,7 +449,7 @@ dsa_status run_fused_kernel(const dsa_batch* b, const dsa_indexer_args* ia, cons
   e = launch_sfa_combine(kBF16, sa->n_heads, sa->v_dim, sp, st);
   if (e != hipSuccess) return hip_fail(e, "sfa combine launch");
   launched = true;
-  return debug_mode() ? debug_error_bits(ws, st) : DSA_OK;
+  return debug_mode() ? take_error_bits(ws, st) : DSA_OK;
 }
 
 // Workspace layout.  The zero state (the decode indexer's cross-workgroup
@@ -501,6 +486,17 @@ const char* dsa_status_string(int32_t s) {
 }
 
 const char* dsa_last_error(void) { return g_err.c_str(); }
+
+dsa_status dsa_take_device_errors(void* ws, void* stream) {
+  g_err.clear();
+  void* p = ws;
+  if (!p) {
+    dsa_status s = dsa::noalloc_scratch_if_set_up(&p);
+    if (s != DSA_OK || !p) return s;
+  }
+  if (!aligned(p, 16)) return fail(DSA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  return dsa::take_error_bits((uint32_t*)p, (hipStream_t)stream);
+}
 
 size_t dsa_workspace_size(int32_t op, const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa) {
   if (!b || b->batch < 1 || b->total_q < 0) return 0;
@@ -604,6 +600,23 @@ dsa_status fused_decode_impl(const dsa_batch* b, const dsa_indexer_args* ia, con
 }
 
 size_t fused_decode_state_bytes(const dsa_batch* b) { return indexer_bytes(b); }
+
+// Wait for `st` and report (once) the error bits the bounded waits set: with
+// DSA_DEBUG after every indexer launch, and in dsa_take_device_errors.
+dsa_status take_error_bits(uint32_t* ws, hipStream_t st) {
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "indexer (error-bit sync)");
+  uint32_t flags = 0;
+  e = hipMemcpy(&flags, ws, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "indexer (error-bit read)");
+  if (flags) {
+    const uint32_t zero = 0;
+    e = hipMemcpy(ws, &zero, 4, hipMemcpyHostToDevice);   // report each failure once
+    if (e != hipSuccess) return hip_fail(e, "indexer (error-bit reset)");
+    return fail(DSA_ERR_HIP, "indexer reported error bits 0x%x (bounded wait expired or LDS bound)", flags);
+  }
+  return DSA_OK;
+}
 
 dsa_status set_error(dsa_status st, const char* msg) { return fail(st, "%s", msg); }
 void clear_error() { g_err.clear(); }

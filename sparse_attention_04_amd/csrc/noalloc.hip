@@ -71,6 +71,18 @@ dsa_status scratch_for_current_device(void** out, hipStream_t st) {
 }
 
 }  // namespace
+
+dsa_status noalloc_scratch_if_set_up(void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(DSA_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return DSA_OK;
+  std::lock_guard<std::mutex> lock(g_mu);
+  *out = g_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace dsa
 
 extern "C" {

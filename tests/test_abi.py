@@ -195,3 +195,9 @@ def test_empty_calls_return_ok_without_per_token_arrays():
     assert lib.dsa_indexer_topk(bp, ip, None, ws, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
     assert lib.dsa_indexer_prolog(bp, ctypes.pointer(pa), None, None, None, ctypes.pointer(kc), None, None, ws,
                                   1 << 30, None) == B.DSA_ERR_INVALID_ARG
+
+
+def test_take_device_errors_checks_its_pointer_first():
+    # a misaligned workspace is refused before anything touches the device
+    assert B.lib().dsa_take_device_errors(ctypes.c_void_p(0x1004), None) == B.DSA_ERR_INVALID_ARG
+    assert b"aligned" in B.lib().dsa_last_error()

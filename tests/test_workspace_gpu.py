@@ -127,6 +127,12 @@ def test_forced_timeout_poisons_rows_and_is_reported():
         torch.cuda.synchronize()
     assert np.all(fidx.cpu().numpy()[1:] == -1)
     assert np.all(np.isneginf(lse.cpu().numpy()[1:]))
+    _say("forced timeout: dsa_take_device_errors reports it once, without DSA_DEBUG")
+    ws, _ = call.workspace(B.DSA_OP_FUSED_DECODE)
+    with pytest.raises(B.DsaError) as ei:
+        B.dsa_take_device_errors(ws)
+    assert ei.value.status == B.DSA_ERR_HIP and "error bits" in str(ei.value)
+    B.dsa_take_device_errors(ws)    # cleared: the next check passes
     _say("forced timeout: DSA_DEBUG=1 reports it")
     with _with_env(DSA_TEST_FORCE_TIMEOUT="1", DSA_DEBUG="1"):
         with pytest.raises(B.DsaError) as ei:
@@ -138,6 +144,8 @@ def test_forced_timeout_poisons_rows_and_is_reported():
         idx = call.indexer_topk().clone()
     torch.cuda.synchronize()
     _check_all(case, idx)
+    out, lse, fidx = call.fused_decode()
+    B.dsa_take_device_errors(ws)    # a normal call sets no bit
 
 
 def test_empty_call_between_real_calls():

@@ -39,7 +39,8 @@
  *     scale pools, head weights, lse, index rows, lengths and block tables
  *     4-byte aligned.  A misaligned pointer is DSA_ERR_INVALID_ARG.
  *   Ordering: work is enqueued asynchronously on `stream` (a hipStream_t, NULL
- *     = the default stream); nothing is waited for.
+ *     = the default stream); nothing is waited for, except by calls under
+ *     DSA_DEBUG=1 and by dsa_take_device_errors, which say so below.
  *   Empty calls: with total_q = 0 (every sequence without a new query token)
  *     a call validates its arguments as usual and returns DSA_OK having
  *     computed nothing; the arrays with one entry per query token (q, head

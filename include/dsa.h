@@ -33,7 +33,10 @@
  *     provided it holds the largest state and the largest scratch among them
  *     at once: sizing it with dsa_workspace_size() for a call whose batch,
  *     query-token count and topk are each at least those of every call that
- *     shares it is enough.
+ *     shares it is enough.  Its first 256 bytes are a header that calls do
+ *     not leave zero: the sticky error bits (dsa_take_device_errors) and a
+ *     count of fused decode calls that dates their handoffs (zero-filling the
+ *     whole workspace again between calls is always allowed).
  *   Alignment: the workspace and the q, k_cache / kv_cache data and output
  *     arrays are 16-byte aligned (the kernels move them 16 bytes at a time);
  *     scale pools, head weights, lse, index rows, lengths and block tables

@@ -22,6 +22,10 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // Error bits written to the workspace header when a bounded wait gives up.
 constexpr uint32_t kErrBarrierTimeout = 1u;
 
+// The fused decode's ready-word epoch that follows call counter value c (never
+// 0, the value of a cleared ready word).
+__host__ __device__ __forceinline__ uint32_t epoch_after(uint32_t c) { return (c + 1u == 0u) ? 1u : c + 1u; }
+
 // Order-preserving map float -> uint32 (larger float -> larger key).  -0.0 is
 // canonicalised to +0.0 first so both zeros compare equal.  Key 0 is never
 // produced for a finite input (the smallest, -inf, maps to 0x007FFFFF), so 0

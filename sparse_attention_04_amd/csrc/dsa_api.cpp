@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -398,14 +397,6 @@ bool fused_kernel_enabled() {
   return !(s && s[0] == '0');
 }
 
-uint32_t next_epoch() {
-  static std::atomic<uint32_t> counter{0};
-  uint32_t e;
-  do {
-    e = counter.fetch_add(1u) + 1u;
-  } while (e == 0u);   // 0 is a cleared ready word
-  return e;
-}
 
 dsa_status run_fused_kernel(const dsa_batch* b, const dsa_indexer_args* ia, const dsa_sfa_args* sa, int32_t* idx,
                             void* out, float* lse, uint32_t* ws, unsigned char* sfa_ws, hipStream_t st,
@@ -443,10 +434,11 @@ dsa_status run_fused_kernel(const dsa_batch* b, const dsa_indexer_args* ia, cons
   if (e != hipSuccess) return hip_fail(e, "occupancy query (fused decode)");
   if (occ < 1) return DSA_OK;
   const IndexerDecodeParams ip = indexer_decode_params(b, ia, idx, ws, G, (int)cap_keys, (int)stage_pages);
-  const SfaParams sp = sfa_params(b, sa, idx, ia->topk, out, lse, sfa_ws, pl);
-  e = launch_fused_decode(dt, maxq, ip, sp, next_epoch(), lds, st);
+  SfaParams sp = sfa_params(b, sa, idx, ia->topk, out, lse, sfa_ws, pl);
+  sp.epoch_word = ws + kWsEpochWord;   // advanced by the combine (or the bump) after the kernel
+  e = launch_fused_decode(dt, maxq, ip, sp, lds, st);
   if (e != hipSuccess) return hip_fail(e, "fused decode launch");
-  e = launch_sfa_combine(kBF16, sa->n_heads, sa->v_dim, sp, st);
+  e = sp.splits > 1 ? launch_sfa_combine(kBF16, sa->n_heads, sa->v_dim, sp, st) : launch_fused_epoch_bump(sp.epoch_word, st);
   if (e != hipSuccess) return hip_fail(e, "sfa combine launch");
   launched = true;
   return debug_mode() ? take_error_bits(ws, st) : DSA_OK;

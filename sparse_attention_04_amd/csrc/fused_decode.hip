@@ -28,7 +28,13 @@
 // sequence never became ready (a wait gave up) skips its rows, contributes an
 // empty range (lse = -inf) and sets the error bit, so the grid always drains
 // and no row of a previous call is ever read.  The ready word holds an epoch
-// that differs for every call, and the sequence's last task clears it.
+// that differs from call to call, and the sequence's last task clears it; a
+// word a late writer leaves behind therefore never matches a later call's
+// epoch.  The epoch comes from a counter in the workspace header that every
+// workgroup reads at its start and the kernel after this one (the combine,
+// or epoch_bump_kernel when there is one range per token) advances, so all
+// workgroups of a launch agree on it and every replay of a captured graph
+// gets a new one, as separate calls do.
 #include "common.h"
 #include "kernels.h"
 #include "indexer_decode_body.h"
@@ -54,13 +60,14 @@ __device__ void sfa_empty_range(const SfaParams& p, int g, int split) {
 }
 
 template <int DT, int MAXQ, bool LO>
-__global__ __launch_bounds__(kIdxThreads, 1) void fused_decode_kernel(IndexerDecodeParams ip, SfaParams sp,
-                                                                     uint32_t epoch) {
+__global__ __launch_bounds__(kIdxThreads, 1) void fused_decode_kernel(IndexerDecodeParams ip, SfaParams sp) {
   static_assert(kIdxThreads == 64 * 8, "both phases run 8 waves");
   extern __shared__ __align__(16) uint32_t smem[];
   const int G = gridDim.x;   // a multiple of 8
   const int w = blockIdx.x;
   const int vw = (w & 7) * (G >> 3) + (w >> 3);
+  // issued first, used only when the rows are published or awaited
+  const uint32_t epoch = epoch_after(load_relaxed_agent(ip.ws + kWsEpochWord));
   indexer_decode_body<DT, 64, 128, MAXQ, true>(ip, vw, smem, epoch);
   // the indexer's LDS is free once every wave is past it
   __syncthreads();
@@ -120,6 +127,10 @@ __global__ __launch_bounds__(kIdxThreads, 1) void fused_decode_kernel(IndexerDec
   X(kFP8, 4, true)          \
   X(kMX, 4, true)
 
+__global__ void epoch_bump_kernel(uint32_t* w) {
+  if (threadIdx.x == 0) *w = epoch_after(*w);
+}
+
 const void* pick_fused(int dtype, int maxq, bool lo) {
 #define DSA_PICK(DT_, Q_, LO_) \
   if (dtype == DT_ && maxq == Q_ && lo == LO_) return (const void*)fused_decode_kernel<DT_, Q_, LO_>;
@@ -148,19 +159,24 @@ hipError_t fused_decode_occupancy(int dtype, int maxq, bool precise_weights, siz
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k, kIdxThreads, lds);
 }
 
+hipError_t launch_fused_epoch_bump(uint32_t* epoch_word, hipStream_t st) {
+  hipLaunchKernelGGL(epoch_bump_kernel, dim3(1), dim3(64), 0, st, epoch_word);
+  return hipGetLastError();
+}
+
 hipError_t launch_fused_decode(int dtype, int maxq, const IndexerDecodeParams& ip, const SfaParams& sp,
-                               uint32_t epoch, size_t lds, hipStream_t st) {
+                               size_t lds, hipStream_t st) {
   const void* k = pick_fused(dtype, maxq, sp.precise_weights != 0);
   // one task per workgroup at most: 8 * ceil(total_q / 8) * splits <= grid
   const int64_t tasks = 8 * (int64_t)((sp.bv.total_q + 7) / 8) * sp.splits;
   if (!k || ip.grid % 8 != 0 || ip.seq_base != 0 || sp.hsplit != 1 || sp.kv8 ||
-      sp.rows_per_split > kSfaMaxRows || tasks > ip.grid)
+      sp.rows_per_split > kSfaMaxRows || tasks > ip.grid || !sp.epoch_word)
     return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   IndexerDecodeParams ipc = ip;
   SfaParams spc = sp;
-  void* args[] = {(void*)&ipc, (void*)&spc, (void*)&epoch};
+  void* args[] = {(void*)&ipc, (void*)&spc};
   e = hipLaunchKernel(k, dim3(ip.grid), dim3(kIdxThreads), args, lds, st);
   if (e != hipSuccess) return e;
   return hipGetLastError();

@@ -43,6 +43,7 @@ struct WsLayout {
   uint32_t* base;
   int32_t nseq, nq, grid_pad;
   __host__ __device__ uint32_t* err() const { return base; }
+  __host__ __device__ uint32_t* call_epoch() const { return base + kWsEpochWord; }
   __host__ __device__ uint32_t* seq_ctr(int b) const { return base + 64 + 32 * b; }
   __host__ __device__ uint32_t* seq_exit(int b) const { return seq_ctr(b) + 1; }
   __host__ __device__ uint32_t* seq_failed(int b) const { return seq_ctr(b) + 2; }

@@ -36,6 +36,10 @@ struct IndexerDecodeParams {
   uint32_t barrier_slack;  // added to every barrier target (0; a test sets it to force timeouts)
 };
 
+// Word of the indexer workspace header that counts fused decode calls (the
+// source of their ready-word epochs); word 0 holds the sticky error bits.
+constexpr int kWsEpochWord = 8;
+
 size_t indexer_ws_bytes(int nseq, int nq, int grid);
 size_t indexer_decode_lds_bytes(int dtype, int maxq, int chunk_cap, int stage_pages);
 hipError_t indexer_decode_occupancy(int dtype, int H, int D, int maxq, size_t lds, int* blocks_per_cu);
@@ -113,6 +117,7 @@ struct SfaParams {
   float* part_o;           // splits > 1: [total_q][splits][H][Dv], fp16 (bf16 kernel) or f32 (f32 kernel)
   float* part_ml;          // splits > 1: [total_q][splits][H] log2-sum-exp of each range
   unsigned long long* dbg; // optional: per-phase clock sums of workgroup 0, wave 0 (profiling)
+  uint32_t* epoch_word;    // fused decode only: the call counter the combine advances, else null
 };
 
 hipError_t launch_sfa(int dtype, int H, int Dqk, int Dv, const SfaParams& p, hipStream_t st);
@@ -125,7 +130,9 @@ size_t fused_decode_sfa_lds_bytes(int rows_per_split);
 int fused_decode_max_rows();
 hipError_t fused_decode_occupancy(int dtype, int maxq, bool precise_weights, size_t lds, int* blocks_per_cu);
 hipError_t launch_fused_decode(int dtype, int maxq, const IndexerDecodeParams& ip, const SfaParams& sp,
-                               uint32_t epoch, size_t lds, hipStream_t st);
+                               size_t lds, hipStream_t st);
+// Advances the call counter when no combine follows the fused kernel (one range per token).
+hipError_t launch_fused_epoch_bump(uint32_t* epoch_word, hipStream_t st);
 hipError_t launch_sfa_combine(int dtype, int H, int Dv, const SfaParams& p, hipStream_t st);
 
 }  // namespace dsa

@@ -62,6 +62,8 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p, int H) {
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int c0 = (threadIdx.x & 63) * CPT;
   const int S = p.splits;
+  // the fused decode's call counter moves on once its kernel is complete
+  if (p.epoch_word && g == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.epoch_word = epoch_after(*p.epoch_word);
   if (h >= H) return;
   // Splits go in groups of 4 whose log-sum-exps and partials are all loaded
   // before any is used (one memory round trip per group); the running

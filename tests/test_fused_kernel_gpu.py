@@ -144,3 +144,47 @@ def test_fused_kernel_leaves_ready_words_zero():
         assert int(ws[256:state].count_nonzero()) == 0, k
         for b in range(case.batch):
             check_topk_row(idx[case.token(b, 0)], oracle.run_query(case, b, 0), case.topk)
+
+
+def test_fused_kernel_graph_replays_take_fresh_epochs():
+    """A captured fused decode replayed several times: each replay derives its
+    ready-word epoch from the workspace's call counter, which the launch after
+    the fused kernel advances, so a ready word that a late writer of the
+    previous call could leave behind (planted here before every replay: the
+    previous call's epoch in every sequence's word) is never taken for the
+    next call's.  The index buffer is set to -1 before each replay, so rows
+    read before they were written would show.  Every replay must match the
+    eager call."""
+    case = case_to(make_case("c2_decode_bf16", 89, batch=3, seq_len_range=(3000, 6000)), "cuda")
+    call = B.Call(case)
+    _say(f"graph: {case.name} B={case.batch}: eager call")
+    out0, lse0, idx0 = _fused(call)
+    ws, _ = call.workspace(B.DSA_OP_FUSED_DECODE)
+    words = ws.view(torch.int32)
+    _say("graph: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call.fused_decode()
+    torch.cuda.synchronize()
+    for r in range(4):
+        c0 = int(words[8].item()) & 0xFFFFFFFF
+        for b in range(case.batch):
+            words[64 + 32 * b + 3] = c0 - (1 << 32) if c0 >= (1 << 31) else c0
+        call.idx.fill_(-1)
+        torch.cuda.synchronize()
+        _say(f"graph: replay {r} (counter {c0})")
+        g.replay()
+        torch.cuda.synchronize()
+        c1 = int(words[8].item()) & 0xFFFFFFFF
+        assert c1 == (c0 + 1 if c0 + 1 < (1 << 32) else 1), (c0, c1)
+        assert int(words[64:64 + 32 * case.batch].count_nonzero()) == 0, "state words left set"
+        out1 = call.out.float().cpu().numpy()
+        lse1 = call.lse.cpu().numpy()
+        idx1 = call.idx.cpu().numpy()
+        assert np.array_equal(np.sort(idx0, 1), np.sort(idx1, 1)), r
+        mag = np.maximum(np.abs(out0), np.abs(out1))
+        assert np.all(np.abs(out0 - out1) <= 2.0 ** -6 * mag + 2.0 ** -10), r
+        assert np.allclose(lse0, lse1, atol=1e-4, rtol=1e-5), r
+        # eager work between replays
+        call.indexer_topk()
+        torch.cuda.synchronize()

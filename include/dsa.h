@@ -271,7 +271,10 @@ dsa_status dsa_fused_prefill(const dsa_batch* batch, const dsa_indexer_args* iar
  * scratch, so calls of any shapes may follow each other; a call whose state
  * or scratch (together dsa_workspace_size(DSA_OP_FUSED_DECODE, ...)) exceeds
  * its part returns DSA_ERR_UNSUPPORTED and enqueues nothing.  The first
- * call on a device also enqueues one clear of the array.  All calls on one
+ * call on a device also enqueues one clear of the array (make that call
+ * before capturing a graph, or every replay repeats the clear).  Replays of
+ * a captured call are safe: the handoff inside each is dated by a counter
+ * on the device, not by a value frozen into the graph.  All calls on one
  * GPU share its array: calls that may overlap on the same GPU (other streams,
  * other host threads) race and must be ordered by the caller.               */
 dsa_status dsa_fused_decode_noalloc(const dsa_batch* batch, const dsa_indexer_args* iargs,

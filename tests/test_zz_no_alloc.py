@@ -113,3 +113,36 @@ def test_noalloc_empty_call_then_real_call():
         check_sfa(out_h[g], ref_o, real.sfa_dtype)
     # no bounded wait gave up in these calls: the static scratch's error bits are clear
     B.dsa_take_device_errors(None)
+
+
+def test_noalloc_graph_replays_match_the_eager_call():
+    """A captured allocation-free call (captured after an eager one, which
+    makes the one-time clear) replayed three times, with eager work between
+    the replays: each replay's rows and outputs match the eager call's."""
+    assert torch.cuda.is_available()
+    B.lib()
+    case = case_to(make_case("c2_decode_bf16", 67, batch=3, seq_len_range=(3000, 6000)), "cuda")
+    call = B.Call(case)
+    out, lse, idx = torch.empty_like(call.out), torch.empty_like(call.lse), torch.empty_like(call.idx)
+    _say("no-alloc graph: eager call")
+    call.fused_decode_noalloc(out, lse, idx)
+    torch.cuda.synchronize()
+    out0, lse0, idx0 = out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call.fused_decode_noalloc(out, lse, idx)
+    torch.cuda.synchronize()
+    for r in range(3):
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        _say(f"no-alloc graph: replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        out1, lse1, idx1 = out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+        assert np.array_equal(np.sort(idx0, 1), np.sort(idx1, 1)), r
+        mag = np.maximum(np.abs(out0), np.abs(out1))
+        assert np.all(np.abs(out0 - out1) <= 2.0 ** -6 * mag + 2.0 ** -10), r
+        assert np.allclose(lse0, lse1, atol=1e-4, rtol=1e-5), r
+        call.fused_decode()     # eager work between replays (the workspace path)
+        torch.cuda.synchronize()
+    B.dsa_take_device_errors(None)

@@ -210,6 +210,15 @@ bool force_timeout_mode() {
   return s && s[0] == '1';
 }
 
+// DSA_TEST_WITHHOLD_READY=1 (tests only): the fused decode kernel's indexer
+// never publishes a sequence's rows and its attention tasks give up waiting
+// after a few sleeps, so the tasks' failure path (an empty range and the
+// error bit) can be checked while every kernel still ends.
+bool withhold_ready_mode() {
+  const char* s = getenv("DSA_TEST_WITHHOLD_READY");
+  return s && s[0] == '1';
+}
+
 // DSA_PROFILE=1: kernels record per-phase clock sums of their first workgroup
 // in the last kProfileBytes of the workspace.
 constexpr size_t kProfileBytes = 256;
@@ -240,6 +249,13 @@ IndexerDecodeParams indexer_decode_params(const dsa_batch* b, const dsa_indexer_
   p.stage_pages = stage;
   p.spin_limit = kSpinLimit;
   p.barrier_slack = 0;
+  p.ready_spin_limit = kSpinLimit;
+  p.publish_ready = 1;
+  if (withhold_ready_mode()) {
+    // test hook: no rows are handed over and the tasks stop waiting quickly
+    p.ready_spin_limit = 64;
+    p.publish_ready = 0;
+  }
   if (force_timeout_mode()) {
     // test hook: no barrier can complete, and every wait gives up quickly
     p.spin_limit = 64;

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void fused_decode_kernel(IndexerDec
     int ok = 1;
     while (load_relaxed_agent(W.seq_ready(b)) != epoch) {
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > ip.spin_limit) {
+      if (++spins > ip.ready_spin_limit) {
         atomic_add_agent(W.err(), kErrBarrierTimeout);
         ok = 0;
         break;

@@ -456,7 +456,7 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
         const uint32_t tk = atomic_add_agent(W.seq_exit(p.seq_base + b), 1u);
         if (tk == (uint32_t)(nb - 1)) {
           store_relaxed_agent(W.seq_exit(p.seq_base + b), 0u);
-          if (T > 0) store_relaxed_agent(W.seq_ready(p.seq_base + b), epoch);
+          if (T > 0 && p.publish_ready) store_relaxed_agent(W.seq_ready(p.seq_base + b), epoch);
         }
       }
     }
@@ -976,7 +976,7 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
         // poisoning above before this
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid == 0 && T > 0) store_relaxed_agent(W.seq_ready(p.seq_base + b), epoch);
+        if (tid == 0 && T > 0 && p.publish_ready) store_relaxed_agent(W.seq_ready(p.seq_base + b), epoch);
       }
     }
   }

@@ -34,6 +34,8 @@ struct IndexerDecodeParams {
   int32_t stage_pages;     // LDS slots for the workgroup's block-table slice
   uint32_t spin_limit;     // sleeps before a cross-workgroup wait gives up
   uint32_t barrier_slack;  // added to every barrier target (0; a test sets it to force timeouts)
+  uint32_t ready_spin_limit;  // fused kernel: sleeps before a task's wait for its rows gives up
+  uint32_t publish_ready;  // fused kernel: 1; 0 only in a test that withholds the handoff
 };
 
 // Word of the indexer workspace header that counts fused decode calls (the

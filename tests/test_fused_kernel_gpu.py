@@ -188,3 +188,34 @@ def test_fused_kernel_graph_replays_take_fresh_epochs():
         # eager work between replays
         call.indexer_topk()
         torch.cuda.synchronize()
+
+
+def test_fused_kernel_withheld_handoff_gives_empty_ranges():
+    """The tasks' failure path, forced from the host (DSA_TEST_WITHHOLD_READY:
+    no sequence's rows are ever published and each task gives up after a few
+    sleeps): every task writes an empty range, so the output is zero with
+    lse = -inf, the index rows are still complete, the error bit is set, the
+    state words come back zero and the next call is exact."""
+    case = case_to(make_case("c2_decode_bf16", 90, batch=3, seq_len_range=(3000, 6000)), "cuda")
+    call = B.Call(case)
+    _say(f"withheld handoff: {case.name} B={case.batch}: normal call")
+    out0, lse0, idx0 = _fused(call)
+    ws, _ = call.workspace(B.DSA_OP_FUSED_DECODE)
+    state = B.dsa_workspace_size(B.DSA_OP_INDEXER_TOPK, call.batch, call.iargs, call.sargs)
+    B.dsa_take_device_errors(ws)
+    _say("withheld handoff: every task gives up")
+    with _env(DSA_TEST_WITHHOLD_READY="1"):
+        out1, lse1, idx1 = _fused(call)
+    assert np.array_equal(np.sort(idx0, 1), np.sort(idx1, 1))
+    assert np.all(out1 == 0.0)
+    assert np.all(np.isneginf(lse1))
+    with pytest.raises(B.DsaError) as ei:
+        B.dsa_take_device_errors(ws)
+    assert ei.value.status == B.DSA_ERR_HIP
+    assert int(ws[256:state].count_nonzero()) == 0
+    _say("withheld handoff: a normal call afterwards")
+    out2, lse2, idx2 = _fused(call)
+    assert np.array_equal(np.sort(idx0, 1), np.sort(idx2, 1))
+    mag = np.maximum(np.abs(out0), np.abs(out2))
+    assert np.all(np.abs(out0 - out2) <= 2.0 ** -6 * mag + 2.0 ** -10)
+    B.dsa_take_device_errors(ws)

@@ -108,6 +108,13 @@ def test_fused_kernel_quantised_indexer(name):
     _compare_paths(case)
 
 
+@pytest.mark.parametrize("name", ["c4_decode_fp8", "c4_decode_mxfp8"])
+def test_fused_kernel_quantised_indexer_multi_token(name):
+    # the quantised indexers with 4, 2, 3 and 1 query tokens per sequence
+    case = case_to(make_case(name, 91, batch=4, seq_lens=[2050, 5000, 2049, 6000], q_lens=[4, 2, 3, 1]), "cuda")
+    _compare_paths(case)
+
+
 @pytest.mark.parametrize("q_lens", [[2, 0, 3], [1, 0, 1]])
 def test_fused_kernel_sequence_without_query_tokens(q_lens):
     # a sequence with cached keys but no new token: its indexer workgroups

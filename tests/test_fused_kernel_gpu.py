@@ -108,6 +108,16 @@ def test_fused_kernel_quantised_indexer(name):
     _compare_paths(case)
 
 
+@pytest.mark.parametrize("topk", [1, 64, 4096])
+def test_fused_kernel_other_topk(topk):
+    # a single selected row (one range of one tile per token) and a small k,
+    # both through the fused kernel, and k twice the usual (64 ranges per
+    # token, more tasks than workgroups: the two-kernel path); contexts both
+    # below and above k
+    case = case_to(make_case("c2_decode_bf16", 92, batch=4, seq_lens=[700, 3000, 5000, 9000], topk=topk), "cuda")
+    _compare_paths(case)
+
+
 @pytest.mark.parametrize("name", ["c4_decode_fp8", "c4_decode_mxfp8"])
 def test_fused_kernel_quantised_indexer_multi_token(name):
     # the quantised indexers with 4, 2, 3 and 1 query tokens per sequence

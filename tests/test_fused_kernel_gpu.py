@@ -108,6 +108,15 @@ def test_fused_kernel_quantised_indexer(name):
     _compare_paths(case)
 
 
+@pytest.mark.parametrize("page_size", [1, 2, 1024, 4096])
+def test_fused_kernel_extreme_page_sizes(page_size):
+    # the smallest and largest page sizes the boundary takes: one key per
+    # block-table entry, and pages larger than a whole context
+    case = case_to(make_case("c2_decode_bf16", 93, batch=3, seq_lens=[700, 3000, 5000], page_size=page_size),
+                   "cuda")
+    _compare_paths(case)
+
+
 @pytest.mark.parametrize("topk", [1, 64, 4096])
 def test_fused_kernel_other_topk(topk):
     # a single selected row (one range of one tile per token) and a small k,

@@ -403,6 +403,15 @@ def test_prefill_small_pages():
     _run_prefill(case, _sample_prefill_queries(case, per_seq=30))
 
 
+@pytest.mark.parametrize("page_size", [1, 1024])
+def test_prefill_extreme_page_sizes(page_size):
+    # one-token pages (every key and latent row through its own block-table
+    # entry) and 1024-token pages (a tile never crosses a page)
+    case = case_to(make_case("c3_prefill_bf16", 28, seq_len_range=(2600, 2600), q_len=300, page_size=page_size,
+                             topk=512), "cuda")
+    _run_prefill(case, _sample_prefill_queries(case, per_seq=20))
+
+
 def test_prefill_mixed_batch_zigzag_units():
     # sequences with different numbers of query blocks (odd, even, one) share a launch
     case = case_to(make_case("c3_prefill_bf16", 24, batch=3, seq_lens=[3000, 2100, 4100], q_lens=[130, 64, 257],

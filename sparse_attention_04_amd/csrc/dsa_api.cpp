@@ -219,6 +219,18 @@ bool withhold_ready_mode() {
   return s && s[0] == '1';
 }
 
+// The boundary-bin handoff of the decode indexer (the sequence's last
+// workgroup chooses among the keys of the first pass's boundary bin) is taken
+// when that bin holds at most kHandoffCap keys.  DSA_INDEXER_HANDOFF_CAP=n
+// lowers the limit (0 turns the handoff off, so every query runs the later
+// radix passes); tests use it to run both paths on the same inputs.
+int handoff_cap() {
+  const char* s = getenv("DSA_INDEXER_HANDOFF_CAP");
+  if (!s || !s[0]) return kHandoffCap;
+  const long v = strtol(s, nullptr, 10);
+  return (int)std::max<long>(0, std::min<long>(v, kHandoffCap));
+}
+
 // DSA_PROFILE=1: kernels record per-phase clock sums of their first workgroup
 // in the last kProfileBytes of the workspace.
 constexpr size_t kProfileBytes = 256;
@@ -251,6 +263,7 @@ IndexerDecodeParams indexer_decode_params(const dsa_batch* b, const dsa_indexer_
   p.barrier_slack = 0;
   p.ready_spin_limit = kSpinLimit;
   p.publish_ready = 1;
+  p.cand_cap = handoff_cap();
   if (withhold_ready_mode()) {
     // test hook: no rows are handed over and the tasks stop waiting quickly
     p.ready_spin_limit = 64;

@@ -83,26 +83,30 @@ __global__ __launch_bounds__(kIdxThreads, 1) void fused_decode_kernel(IndexerDec
   const int g = (w & 7) * chunk + r / S;
   if (r / S >= chunk || g >= sp.bv.total_q) return;
   __shared__ int s_ok, s_b;
-  if (threadIdx.x == 0) {
-    WsLayout W{ip.ws, ip.ws_nseq, ip.ws_nq, ip.ws_grid_pad};
-    const int b = find_seq(sp.bv, g);
-    uint32_t spins = 0;
-    int ok = 1;
-    while (load_relaxed_agent(W.seq_ready(b)) != epoch) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > ip.ready_spin_limit) {
-        atomic_add_agent(W.err(), kErrBarrierTimeout);
-        ok = 0;
-        break;
+  // The task's q loads are issued before this wait (inside the attention
+  // body), so they overlap it; no index slot is read before it ends.
+  auto wait_ready = [&]() -> bool {
+    if (threadIdx.x == 0) {
+      WsLayout W{ip.ws, ip.ws_nseq, ip.ws_nq, ip.ws_grid_pad};
+      const int b = find_seq(sp.bv, g);
+      uint32_t spins = 0;
+      int ok = 1;
+      while (load_relaxed_agent(W.seq_ready(b)) != epoch) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > ip.ready_spin_limit) {
+          atomic_add_agent(W.err(), kErrBarrierTimeout);
+          ok = 0;
+          break;
+        }
       }
+      s_ok = ok;
+      s_b = b;
     }
-    s_ok = ok;
-    s_b = b;
-  }
-  __syncthreads();
-  if (s_ok)
-    sfa_bf16_body<kFusedDqk, kFusedDv, LO, 1, false, 8, true>(sp, g, 0, split, false, (unsigned char*)smem);
-  else
+    __syncthreads();
+    return s_ok != 0;
+  };
+  if (!sfa_bf16_body<kFusedDqk, kFusedDv, LO, 1, false, 8, true>(sp, g, 0, split, false, (unsigned char*)smem,
+                                                                 wait_ready))
     sfa_empty_range(sp, g, split);
   // the last task of the sequence clears its ready word and its counter
   __syncthreads();

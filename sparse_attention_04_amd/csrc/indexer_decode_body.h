@@ -37,8 +37,11 @@ __host__ __device__ constexpr size_t xchg_offset_words(int maxq, int chunk_cap, 
 //                                  decode kernel the ready word (the call's epoch
 //                                  once every index row of the sequence is
 //                                  written) and the attention's exit counter
-//   then per query {hist0[2048], outcnt (+31 pad)}
-//   then per query {hist1[2048], hist2[2048], tie[grid_pad]}
+//   then per query {hist0[2048], outcnt, candcnt (+30 pad)}
+//   then per query {hist1[2048], hist2[2048], tie[grid_pad]}, which a query
+//                                  whose boundary bin is handed to the last
+//                                  workgroup (section 3c) uses instead as its
+//                                  list of (key, position) candidate pairs
 struct WsLayout {
   uint32_t* base;
   int32_t nseq, nq, grid_pad;
@@ -55,6 +58,9 @@ struct WsLayout {
     return base + 64 + 32 * nseq + (size_t)nq * 2080 + (size_t)g * (4096 + grid_pad) + (pass - 1) * 2048;
   }
   __host__ __device__ uint32_t* outcnt(int g) const { return qa(g) + 2048; }
+  __host__ __device__ uint32_t* candcnt(int g) const { return qa(g) + 2049; }
+  __host__ __device__ uint64_t* cand(int g) const { return (uint64_t*)hist(g, 1); }
+  __host__ __device__ int cand_pairs() const { return (4096 + grid_pad) / 2; }
   __host__ __device__ uint32_t* tie(int g) const {
     return base + 64 + 32 * nseq + (size_t)nq * 2080 + (size_t)g * (4096 + grid_pad) + 4096;
   }
@@ -252,7 +258,158 @@ __device__ __forceinline__ int block_rank(bool pred, int* scratch, int& total) {
 
 // ------------------------------------------------------------------ kernel ---
 
-enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3 };
+enum : int { kActive = 0, kTakeBin = 1, kTiePass = 2, kAll = 3, kHandoff = 4 };
+
+// Exact choice, inside the sequence's last workgroup, of the s_need[q] best
+// of the s_nc[q] candidate pairs (key in the low word, position in the high
+// word) of every handed-off query q; all of a query's candidates share their
+// leading 11 key bits.  Order: larger key first, and among equal keys the
+// smaller position.  Each pair becomes a 52-bit composite, key bits 20..0
+// above (2^31 - 1 - position), so the candidates are distinct and ordered as
+// the selection orders them.  A radix select over the composites takes
+// digits from the top (11, 11, 11, 11, 8 bits) and stops, query by query, once
+// the boundary digit's candidates are all needed.  The composites stay in
+// registers (thread t holds candidates t + 512 r); each query has two LDS
+// histograms used in turn, so a pass costs two barriers, and the first pass's
+// counts are taken as the candidates arrive.  The chosen positions go to the
+// query's row from slot K - s_need[q] on, in no particular order.  One call
+// serves queries q0 .. q0 + MAXQ - 1; the kernels call it one query at a time,
+// since the four-query kernels have no registers to spare for more (they
+// already keep part of their scalars in vector-register lanes).
+// LDS: 2 * MAXQ * 2048 words from `lds`.
+constexpr int kHandRegs = (kHandoffCap + kIdxThreads - 1) / kIdxThreads;
+
+template <int MAXQ, typename Put>
+__device__ void handoff_select(const WsLayout& W, int tok0, int T, const int* s_hand, const int* s_nc,
+                               const int* s_need, int32_t* idx_out, int K, uint32_t* lds, Put put_row) {
+  static_assert(kBinsPerThread == 4 && kRadixBins == 4 * kIdxThreads, "four bins per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __syncthreads();   // the previous call's LDS reads are done
+  __shared__ int s_wsum[MAXQ][kIdxWaves], s_hb[MAXQ][3], s_slot[MAXQ];
+  uint32_t* hist = lds;   // [2][MAXQ][2048]
+  for (int i = tid; i < 2 * MAXQ * kRadixBins / 4; i += kIdxThreads) ((u32x4*)hist)[i] = u32x4{0u, 0u, 0u, 0u};
+  if (tid < MAXQ) s_slot[tid] = 0;
+  bool act[MAXQ];
+  int n[MAXQ], need[MAXQ];
+  uint64_t pre[MAXQ], pm[MAXQ];
+  uint64_t c[MAXQ][kHandRegs];
+#pragma unroll
+  for (int q = 0; q < MAXQ; q++) {
+    act[q] = q < T && s_hand[q];
+    n[q] = act[q] ? s_nc[q] : 0;
+    need[q] = act[q] ? s_need[q] : 0;
+    pre[q] = 0;
+    pm[q] = 0;
+    const uint64_t* cl = W.cand(tok0 + q);
+#pragma unroll
+    for (int r = 0; r < kHandRegs; r++) {
+      const int i = tid + kIdxThreads * r;
+      c[q][r] = (i < n[q]) ? __hip_atomic_load(const_cast<uint64_t*>(cl) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0ull;
+    }
+  }
+  __syncthreads();   // histograms clear
+#pragma unroll
+  for (int q = 0; q < MAXQ; q++) {
+#pragma unroll
+    for (int r = 0; r < kHandRegs; r++) {
+      const int i = tid + kIdxThreads * r;
+      const uint32_t key = (uint32_t)c[q][r], pos = (uint32_t)(c[q][r] >> 32);
+      c[q][r] = ((uint64_t)(key & 0x1FFFFFu) << 31) | (uint64_t)(0x7FFFFFFFu - pos);
+      if (i < n[q]) atomicAdd(&hist[q * kRadixBins + (uint32_t)(c[q][r] >> 41)], 1u);
+    }
+  }
+  for (int ps = 0; ps < 5; ps++) {
+    bool any = false;
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) any |= act[q];
+    if (!any) break;   // uniform: every thread holds the same act[]
+    const int shift = (ps < 4) ? 41 - 11 * ps : 0;
+    const uint32_t dmask = (ps < 4) ? 0x7FFu : 0xFFu;
+    uint32_t* H = hist + (ps & 1) * MAXQ * kRadixBins;
+    uint32_t* Hn = hist + ((ps + 1) & 1) * MAXQ * kRadixBins;
+    if (ps > 0) {
+#pragma unroll
+      for (int q = 0; q < MAXQ; q++) {
+        if (!act[q]) continue;
+#pragma unroll
+        for (int r = 0; r < kHandRegs; r++) {
+          const int i = tid + kIdxThreads * r;
+          if (i < n[q] && (c[q][r] & pm[q]) == pre[q])
+            atomicAdd(&H[q * kRadixBins + ((uint32_t)(c[q][r] >> shift) & dmask)], 1u);
+        }
+      }
+    }
+    // the other set, read by the previous pass's scan (finished before the
+    // barrier that ended it), is cleared for the next pass
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++)
+      if (act[q]) ((u32x4*)(Hn + q * kRadixBins))[tid] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    // boundary bin of every active query: suffix sums over 4 bins per thread
+    u32x4 v[MAXQ];
+    int cs[MAXQ], x[MAXQ];
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) {
+      if (!act[q]) continue;
+      v[q] = ((const u32x4*)(H + q * kRadixBins))[tid];
+      cs[q] = (int)(v[q][0] + v[q][1] + v[q][2] + v[q][3]);
+      x[q] = cs[q];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_down(x[q], o);
+        if (lane + o < 64) x[q] += t;
+      }
+      if (lane == 0) s_wsum[q][wave] = x[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) {
+      if (!act[q]) continue;
+      int later = 0;
+#pragma unroll
+      for (int w = 0; w < kIdxWaves; w++) later += (w > wave) ? s_wsum[q][w] : 0;
+      const int incl = x[q] + later, above = incl - cs[q];
+      if (above < need[q] && need[q] <= incl) {
+        int run = above;
+#pragma unroll
+        for (int e = 3; e >= 0; e--) {
+          if (run + (int)v[q][e] >= need[q]) {
+            s_hb[q][0] = 4 * tid + e;
+            s_hb[q][1] = run;
+            s_hb[q][2] = (int)v[q][e];
+            break;
+          }
+          run += (int)v[q][e];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) {
+      if (!act[q]) continue;
+      need[q] -= s_hb[q][1];
+      pre[q] |= (uint64_t)s_hb[q][0] << shift;
+      pm[q] |= (uint64_t)dmask << shift;
+      if (s_hb[q][2] == need[q]) act[q] = false;   // the boundary digit is taken whole
+    }
+  }
+  // every composite at or above the final prefix is chosen
+#pragma unroll
+  for (int q = 0; q < MAXQ; q++) {
+    if (!(q < T && s_hand[q])) continue;
+    int32_t* row = idx_out + (size_t)(tok0 + q) * K;
+    const int m = s_need[q];
+#pragma unroll
+    for (int r = 0; r < kHandRegs; r++) {
+      const int i = tid + kIdxThreads * r;
+      if (i < n[q] && (c[q][r] & pm[q]) >= pre[q]) {
+        const int k = atomicAdd(&s_slot[q], 1);
+        if (k < m) put_row(row, K - m + k, (int)(0x7FFFFFFFu - (uint32_t)(c[q][r] & 0x7FFFFFFFu)));
+      }
+    }
+  }
+}
 
 // Phase timestamps of workgroup 0 (100 MHz real-time counter) in header words
 // 16.. of the workspace, for profiling the phases of one launch; compiled in
@@ -325,7 +482,7 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
   __shared__ int s_scan[kIdxThreads];
   __shared__ int s_rank[kIdxWaves + 1];
   __shared__ uint32_t s_prefix[MAXQ], s_pmask[MAXQ];
-  __shared__ int s_need[MAXQ], s_state[MAXQ], s_take[MAXQ];
+  __shared__ int s_need[MAXQ], s_state[MAXQ], s_take[MAXQ], s_candn[MAXQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const BatchView& bv = p.bv;
@@ -432,6 +589,7 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
     else if (L - T + tid + 1 <= K) st = kAll;      // every visible position is kept
     s_state[tid] = st;
     s_take[tid] = 0;
+    s_candn[tid] = 0;
   }
   __syncthreads();
 
@@ -641,6 +799,7 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
   // in flight at once.
   __shared__ int s_scanq[MAXQ][kIdxWaves];
   __shared__ int s_binq[MAXQ], s_aboveq[MAXQ], s_bincntq[MAXQ];
+  const int hand_cap = min(p.cand_cap, W.cand_pairs());
   int round = 0;
   for (int pass = 0; pass < kMaxPasses; pass++) {
     bool act = false;
@@ -749,8 +908,16 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
       s_need[q] = nneed;
       s_prefix[q] |= ((uint32_t)s_binq[q]) << shift;
       s_pmask[q] |= dmask << shift;
-      if (s_bincntq[q] == nneed) s_state[q] = kTakeBin;
-      else if (pass == kMaxPasses - 1) s_state[q] = kTiePass;
+      if (s_bincntq[q] == nneed) {
+        s_state[q] = kTakeBin;
+      } else if (pass == 0 && s_bincntq[q] <= hand_cap) {
+        // few enough keys share the boundary bin: the sequence's last
+        // workgroup chooses among them (3c) instead of two more passes
+        s_state[q] = kHandoff;
+        s_candn[q] = s_bincntq[q];
+      } else if (pass == kMaxPasses - 1) {
+        s_state[q] = kTiePass;
+      }
     }
     __syncthreads();
     DSA_STAMP(5 + 3 * pass);
@@ -801,55 +968,75 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
   // with one atomic per query (all a sequence's workgroups add to the same
   // counter, so fewer, larger reservations wait less on each other); then
   // each wave writes its keys from its offset within the workgroup's range.
+  // Handed-off queries: the keys above the boundary bin go to the row the
+  // same way, and the keys in it to the query's candidate list.
+  bool any_hand = false;
+  for (int q = 0; q < MAXQ; q++) any_hand |= (s_state[q] == kHandoff);
   {
-    __shared__ int s_wcnt[MAXQ][kIdxWaves];
-    __shared__ int s_wgbase[MAXQ];
-    bool tb[MAXQ];
-    int cnt[MAXQ];
+    __shared__ int s_wcnt[MAXQ][kIdxWaves], s_wccnt[MAXQ][kIdxWaves];
+    __shared__ int s_wgbase[MAXQ], s_cbase[MAXQ];
+    bool tb[MAXQ], hd[MAXQ];
+    int cnt[MAXQ], ccnt[MAXQ];
 #pragma unroll
     for (int q = 0; q < MAXQ; q++) {
-      tb[q] = q < T && s_state[q] == kTakeBin;
+      hd[q] = q < T && s_state[q] == kHandoff;
+      tb[q] = hd[q] || (q < T && s_state[q] == kTakeBin);
       cnt[q] = 0;
+      ccnt[q] = 0;
       if (!tb[q]) continue;
       const uint32_t pre = s_prefix[q], pm = s_pmask[q];
       const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
       // lane: 4 consecutive keys per round, one 16-B LDS read
-      int c = 0;
+      int c = 0, cd = 0;
       for (int i0 = 4 * kWave * wave; i0 < nloc; i0 += 4 * kIdxThreads) {
         const int i = i0 + 4 * lane;
         const u32x4 v = (i < nloc) ? *(const u32x4*)(scq + i) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const uint32_t x = (i + e < nloc) ? v[e] : 0u;
-          c += (x != 0u && (x & pm) >= pre) ? 1 : 0;
+          const uint32_t xm = x & pm;
+          c += (x != 0u && (hd[q] ? xm > pre : xm >= pre)) ? 1 : 0;
+          cd += (hd[q] && x != 0u && xm == pre) ? 1 : 0;
         }
       }
       cnt[q] = wave_sum(c);
+      ccnt[q] = hd[q] ? wave_sum(cd) : 0;
     }
     if (lane == 0) {
 #pragma unroll
-      for (int q = 0; q < MAXQ; q++) s_wcnt[q][wave] = cnt[q];
+      for (int q = 0; q < MAXQ; q++) {
+        s_wcnt[q][wave] = cnt[q];
+        s_wccnt[q][wave] = ccnt[q];
+      }
     }
     __syncthreads();
     // One thread reserves the workgroup's slots of every query and reads the
-    // sequence's failure flag; without a tie pass these are its last accesses
-    // to shared workspace state, so it then takes the exit ticket (ordered
-    // after the reservations).  The ticket's value is only needed after the
-    // row writes, so it stays in a register and its latency overlaps them.
+    // sequence's failure flag; without a tie pass or a handoff these are its
+    // last accesses to shared workspace state, so it then takes the exit
+    // ticket (ordered after the reservations).  The ticket's value is only
+    // needed after the row writes, so it stays in a register and its latency
+    // overlaps them.
     if (tid == 0) {
-      uint32_t got[MAXQ];
+      uint32_t got[MAXQ], gotc[MAXQ];
 #pragma unroll
       for (int q = 0; q < MAXQ; q++) {
-        int tot = 0;
+        int tot = 0, totc = 0;
 #pragma unroll
-        for (int w = 0; w < kIdxWaves; w++) tot += s_wcnt[q][w];
+        for (int w = 0; w < kIdxWaves; w++) {
+          tot += s_wcnt[q][w];
+          totc += s_wccnt[q][w];
+        }
         got[q] = tot ? atomic_add_agent(W.outcnt(tok0 + q), (uint32_t)tot) : 0u;
+        gotc[q] = totc ? atomic_add_agent(W.candcnt(tok0 + q), (uint32_t)totc) : 0u;
       }
       const uint32_t fl = load_relaxed_agent(failed);
 #pragma unroll
-      for (int q = 0; q < MAXQ; q++) s_wgbase[q] = (int)got[q];
+      for (int q = 0; q < MAXQ; q++) {
+        s_wgbase[q] = (int)got[q];
+        s_cbase[q] = (int)gotc[q];
+      }
       s_failed = fl != 0u;
-      if (!FUSED && !any_tie) {
+      if (!FUSED && !any_tie && !any_hand) {
         __builtin_amdgcn_s_waitcnt(0);
         ticket = atomic_add_agent(W.seq_exit(p.seq_base + b), 1u);
       }
@@ -863,20 +1050,34 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
       const uint32_t pre = s_prefix[q], pm = s_pmask[q];
       const uint32_t* scq = sc + (size_t)q * p.chunk_cap;
       int32_t* row = p.idx_out + (size_t)(tok0 + q) * K;
-      int base = s_wgbase[q];
+      uint64_t* cl = W.cand(tok0 + q);
+      int base = s_wgbase[q], cbase = s_cbase[q];
 #pragma unroll
-      for (int w = 0; w < kIdxWaves; w++) base += (w < wave) ? s_wcnt[q][w] : 0;
+      for (int w = 0; w < kIdxWaves; w++) {
+        base += (w < wave) ? s_wcnt[q][w] : 0;
+        cbase += (w < wave) ? s_wccnt[q][w] : 0;
+      }
       for (int i0 = 4 * kWave * wave; i0 < nloc; i0 += 4 * kIdxThreads) {
         const int i = i0 + 4 * lane;
         const u32x4 v = (i < nloc) ? *(const u32x4*)(scq + i) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const uint32_t x = (i + e < nloc) ? v[e] : 0u;
-          const bool sel = x != 0u && (x & pm) >= pre;
+          const uint32_t xm = x & pm;
+          const bool sel = x != 0u && (hd[q] ? xm > pre : xm >= pre);
           const uint64_t m = __ballot(sel);
           const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
           if (sel && base + r < K) put_row(row, base + r, s0 + i + e);
           base += __popcll(m);
+          if (hd[q]) {
+            const bool cd = x != 0u && xm == pre;
+            const uint64_t mc = __ballot(cd);
+            const int rc = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0));
+            if (cd && cbase + rc < hand_cap)
+              __hip_atomic_store(cl + cbase + rc, (uint64_t)x | ((uint64_t)(uint32_t)(s0 + i + e) << 32),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            cbase += __popcll(mc);
+          }
         }
       }
     }
@@ -944,8 +1145,10 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
   {
     __shared__ int s_last;
     // (FUSED: the ticket also follows this workgroup's row writes, so the
-    // last one out knows every row of the sequence complete)
-    if (FUSED || any_tie) {
+    // last one out knows every row of the sequence complete; a handoff: it
+    // follows the candidate writes, so the last one out finds every list
+    // complete)
+    if (FUSED || any_tie || any_hand) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) ticket = atomic_add_agent(W.seq_exit(p.seq_base + b), 1u);
@@ -956,6 +1159,34 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
     __syncthreads();
     if (s_last) {
       const bool poison = load_relaxed_agent(failed) != 0u;
+      // ---- 3c. handed-off boundary bins: the last workgroup out chooses the
+      // remaining s_need keys among the bin's candidates (every workgroup's
+      // list entries were written before its ticket).  The list holds exactly
+      // the bin's count unless a wait gave up, which poisons the rows anyway.
+      // (every query's count is read: after a failed wait the workgroups may
+      // not all have agreed on the handoff, and the list is cleared below)
+      __shared__ int s_nc[MAXQ];
+      if (tid < MAXQ)
+        s_nc[tid] = (tid < T && L - T + tid + 1 > K)
+                        ? (int)min(load_relaxed_agent(W.candcnt(tok0 + tid)), (uint32_t)hand_cap) : 0;
+      __syncthreads();
+      __shared__ int s_hand[MAXQ];
+      if (tid < MAXQ) s_hand[tid] = tid < T && s_state[tid] == kHandoff && !poison && s_nc[tid] == s_candn[tid];
+      __syncthreads();
+      bool any_sel = false;
+      for (int q = 0; q < T && q < MAXQ; q++) {
+        any_sel |= s_hand[q] != 0;
+        if (s_state[q] != kHandoff || poison || s_hand[q]) continue;
+        // the list does not hold the bin's count: cannot happen when no
+        // wait gave up; the row is poisoned and the error reported
+        int32_t* row = p.idx_out + (size_t)(tok0 + q) * K;
+        if (tid == 0) atomic_add_agent(W.err(), 8u);
+        for (int s = tid; s < K; s += kIdxThreads) put_row(row, s, -1);
+      }
+      if (any_sel) {
+        for (int q0 = 0; q0 < T && q0 < MAXQ; q0++)
+          handoff_select<1>(W, tok0 + q0, T - q0, s_hand + q0, s_nc + q0, s_need + q0, p.idx_out, K, smem, put_row);
+      }
       for (int q = 0; q < T && q < MAXQ; q++) {
         if (L - T + q + 1 <= K) continue;        // kept every position: no scores, no workspace
         const int g = tok0 + q;
@@ -963,12 +1194,13 @@ __device__ __forceinline__ void indexer_decode_body(const IndexerDecodeParams& p
           int32_t* row = p.idx_out + (size_t)g * K;
           for (int s = tid; s < K; s += kIdxThreads) put_row(row, s, -1);
         }
-        u32x4* h0 = (u32x4*)W.qa(g);              // hist0, outcnt and its pad
+        u32x4* h0 = (u32x4*)W.qa(g);              // hist0, outcnt, candcnt and the pad
         for (int i = tid; i < 2080 / 4; i += kIdxThreads) h0[i] = u32x4{0u, 0u, 0u, 0u};
-        u32x4* h12 = (u32x4*)W.hist(g, 1);        // hist1, hist2
+        u32x4* h12 = (u32x4*)W.hist(g, 1);        // hist1, hist2 (or the candidate list)
         for (int i = tid; i < 4096 / 4; i += kIdxThreads) h12[i] = u32x4{0u, 0u, 0u, 0u};
-        uint32_t* tw = W.tie(g);
-        for (int i = tid; i < nb; i += kIdxThreads) tw[i] = 0u;
+        uint32_t* tw = W.tie(g);                  // tie counts (or the list's tail)
+        const int tail = max(nb, 2 * s_nc[q] - 4096);
+        for (int i = tid; i < tail; i += kIdxThreads) tw[i] = 0u;
       }
       if (tid < 3) W.seq_ctr(p.seq_base + b)[tid] = 0u;   // barrier, exit, failure
       if constexpr (FUSED) {

@@ -36,7 +36,14 @@ struct IndexerDecodeParams {
   uint32_t barrier_slack;  // added to every barrier target (0; a test sets it to force timeouts)
   uint32_t ready_spin_limit;  // fused kernel: sleeps before a task's wait for its rows gives up
   uint32_t publish_ready;  // fused kernel: 1; 0 only in a test that withholds the handoff
+  int32_t cand_cap;        // boundary-bin candidates a sequence's last workgroup may select
+                           // itself (pairs; 0 = always run the later radix passes)
 };
+
+// Candidate pairs the boundary-bin handoff may use per query: they live in the
+// query's pass-1/2 histograms and tie counts, which a handed-off query never
+// uses ((4096 + grid_pad) / 2 words with the host's grid pad of 2048).
+constexpr int kHandoffCap = 3072;
 
 // Word of the indexer workspace header that counts fused decode calls (the
 // source of their ready-word epochs); word 0 holds the sticky error bits.

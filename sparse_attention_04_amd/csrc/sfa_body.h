@@ -156,14 +156,22 @@ struct SfaKv8Geom {
   static constexpr size_t lds_bytes(int rows) { return rows_off() + (size_t)rows * 4; }
 };
 
+// Gate of a body whose index rows are always complete: nothing to wait for.
+struct SfaNoGate {
+  __device__ bool operator()() const { return true; }
+};
+
 // The work of one workgroup: token g, head group hy (workgroups sharing the
 // token's heads), slot range `split`.  COHERENT: the index rows were written
 // by other workgroups of the same launch (the fused decode kernel) and are
-// read with agent-scope loads.  prof_wg marks the workgroup whose first wave
-// records phase clocks (DSA_SFA_PHASES builds).
-template <int DQK, int DV, bool LO, int HG, bool KV8, int NWV = 4, bool COHERENT = false>
-__device__ __forceinline__ void sfa_bf16_body(const SfaParams& p, int g, int hy, int split, bool prof_wg,
-                                              unsigned char* sfa_smem) {
+// read with agent-scope loads; gate() (called by every thread, after the q
+// loads are issued and before any index slot is read) waits until they are
+// complete, and when it returns false the body returns false at once, having
+// read no slot.  prof_wg marks the workgroup whose first wave records phase
+// clocks (DSA_SFA_PHASES builds).
+template <int DQK, int DV, bool LO, int HG, bool KV8, int NWV = 4, bool COHERENT = false, typename Gate = SfaNoGate>
+__device__ __forceinline__ bool sfa_bf16_body(const SfaParams& p, int g, int hy, int split, bool prof_wg,
+                                              unsigned char* sfa_smem, Gate gate = Gate{}) {
   using G = SfaBf16Geom<DQK, DV, NWV>;
   using G8 = SfaKv8Geom<DQK, DV>;
   constexpr int ROWB = G::ROWB, PITCH = G::PITCH, TR = G::TR, TILE = G::TILE;
@@ -200,19 +208,20 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaParams& p, int g, int hy,
   const int nslots = max(0, min(p.topk - slot0, p.rows_per_split));
   const int32_t* idx = p.idx + (size_t)g * p.topk + slot0;
   // Loads that depend on the token only are issued first: this thread's first
-  // index slot, and the cu_q entries the token's sequence is found from.
+  // index slot, and the cu_q entries the token's sequence is found from (with
+  // COHERENT rows the slot is read only after the gate, below).
   auto idx_at = [&](int r) -> int {
     if constexpr (COHERENT) return (int)load_relaxed_agent((const uint32_t*)idx + r);
     return idx[r];
   };
-  const int pos0 = (tid < nslots) ? idx_at(tid) : -1;
+  int pos0 = (!COHERENT && tid < nslots) ? idx_at(tid) : -1;
   const int cq = (1 + lane < bv.batch) ? bv.cu_q[1 + lane] : 0x7FFFFFFF;
 
   // q^T as the B operand of S^T = KV q^T (16x16x32): for head group ht, lane l
   // holds head head0 + 16*ht and dims 32*k + 8*(l/16) .. +7 of K-step k.  The
   // workgroup's 16 * NW * HG heads start at 16 * NW * HG * hy; wave w
   // holds HG groups of 16.  Loaded first, so that their latency overlaps the
-  // row lookups.
+  // row lookups (and, with COHERENT rows, the wait for them).
   const int head0 = 16 * NW * HG * hy + 16 * HG * wave + l16;
   bf16x8 qb[HG][KS];
 #pragma unroll
@@ -220,6 +229,10 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaParams& p, int g, int hy,
     const bf16x8* qs = (const bf16x8*)((const uint16_t*)p.q + ((size_t)g * H + head0 + 16 * ht) * DQK);
 #pragma unroll
     for (int k = 0; k < KS; k++) qb[ht][k] = qs[4 * k + grp];
+  }
+  if constexpr (COHERENT) {
+    if (!gate()) return false;
+    pos0 = (tid < nslots) ? idx_at(tid) : -1;
   }
   // the token's sequence: the number of b in [1, batch) with cu_q[b] <= g
   // (cu_q is non-decreasing), from the entries loaded above when the batch
@@ -634,6 +647,7 @@ __device__ __forceinline__ void sfa_bf16_body(const SfaParams& p, int g, int hy,
     for (int i = 0; i < 8; i++) p.dbg[i] = ph[i];
 #endif
 #undef DSA_PHASE
+  return true;
 }
 
 }  // namespace

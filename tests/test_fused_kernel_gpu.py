@@ -54,6 +54,12 @@ def _fused(call):
     return out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
 
 
+def _max_abs_v(case):
+    """Largest |V| element of the latent rows (the NaN page tails aside)."""
+    v = case.kv_pool[..., :case.d_v].float().cpu().numpy()   # bf16 -> f32 is exact
+    return float(np.nanmax(np.abs(v)))
+
+
 def _compare_paths(case, sample=None):
     call = B.Call(case)
     _say(f"{case.name} B={case.batch} T={case.total_q}: two-kernel path")
@@ -62,11 +68,12 @@ def _compare_paths(case, sample=None):
     _say(f"{case.name}: fused kernel")
     out1, lse1, idx1 = _fused(call)
     assert np.array_equal(np.sort(idx0, 1), np.sort(idx1, 1))
-    # the same rows in other ranges: the fp16 partials (2^-11 of max|V|) and
-    # the bf16 output rounding differ, so two bf16 ulps apart at most; each
-    # path is held to the oracle's bar below
+    # the same rows in other ranges: each path's fp16 partials are within
+    # 2^-11 of max|V| (a partial is a convex combination of V rows) and its
+    # bf16 output within 2^-8 relative, so the two differ by at most
+    # 2^-10 max|V| + 2^-7 |out|; each path is held to the oracle's bar below
     mag = np.maximum(np.abs(out0), np.abs(out1))
-    tol = 2.0 ** -6 * mag + 2.0 ** -10
+    tol = 2.0 ** -7 * mag + 2.0 ** -10 * _max_abs_v(case) + 2.0 ** -16
     assert np.all(np.abs(out0 - out1) <= tol), float(np.max(np.abs(out0 - out1) - tol))
     assert np.allclose(lse0, lse1, atol=1e-4, rtol=1e-5)
     toks = range(case.total_q) if sample is None else sample

@@ -187,7 +187,7 @@ typedef struct {
  *          keys are stored (the indexer's dtype)                            */
 typedef struct {
   const void* x;
-  int32_t d_model;             /* a positive multiple of 256                     */
+  int32_t d_model;             /* a positive multiple of 128                     */
   const void* w_q;
   const void* w_k;
   const void* w_w;

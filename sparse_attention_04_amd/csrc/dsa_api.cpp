@@ -648,9 +648,9 @@ extern "C" {
 
 size_t dsa_prolog_workspace_size(const dsa_batch* b, const dsa_prolog_args* a) {
   if (!b || !a || b->total_q < 0 || a->n_heads < 1 || a->head_dim < 1 || a->d_model < 1) return 0;
-  const int parts = prolog_n_parts(b->total_q, std::max(a->d_model, prolog_d_model_unit()));
-  return align_up((size_t)b->total_q * a->n_heads * a->head_dim * 2, 256) +
-         align_up((size_t)parts * b->total_q * (a->head_dim + a->n_heads) * 4, 256) + 256;
+  const size_t words = prolog_part_words(b->total_q, std::max(a->d_model, prolog_d_model_unit()), a->n_heads,
+                                         a->head_dim);
+  return align_up((size_t)b->total_q * a->n_heads * a->head_dim * 2, 256) + align_up(words * 4, 256) + 256;
 }
 
 dsa_status dsa_indexer_prolog(const dsa_batch* b, const dsa_prolog_args* a, void* q_out, void* q_scale_out,
@@ -707,7 +707,7 @@ dsa_status dsa_indexer_prolog(const dsa_batch* b, const dsa_prolog_args* a, void
   p.q_out = q_out;
   p.q_scale_out = q_scale_out;
   p.w_out = w_out;
-  p.kw_part = (float*)(w + align_up((size_t)b->total_q * a->n_heads * a->head_dim * 2, 256));
+  p.part = (float*)(w + align_up((size_t)b->total_q * a->n_heads * a->head_dim * 2, 256));
   p.k_bf16_out = k_bf16_out;
   p.k_data = const_cast<void*>(kc->data);
   p.k_scale = const_cast<void*>(kc->scale);

@@ -89,9 +89,9 @@ struct PrologParams {
   void* q_out;             // fp8 / mx: [total_q][H][D] e4m3 bytes
   void* q_scale_out;       // fp8: f32 [total_q][H]; mx: u8 [total_q][H][D/32]
   float* w_out;            // [total_q][H]
-  float* kw_part;          // [n_parts][total_q][D + H] partial sums of the k and w columns (workspace)
-  int32_t n_parts;         // set by the launcher
-  int32_t split_extra;     // set by the launcher: k / w tiles split by chunk over the q workgroups
+  float* part;             // workspace: float32 partial sums, [n_parts][total_q][H*D + D + H] with
+                           // several d_model ranges, else [1][total_q][D + H] (k and w columns)
+  int32_t n_parts;         // set by the launcher: d_model ranges of the GEMM
   void* k_bf16_out;        // optional [total_q][D] bf16 normalised keys
   void* k_data;            // paged K cache [num_pages][P][D] (written at the new tokens' rows)
   void* k_scale;           // its scales (fp8: f32 [num_pages][P]; mx: u8 [num_pages][P][D/32])
@@ -99,6 +99,7 @@ struct PrologParams {
 
 int prolog_d_model_unit();
 int prolog_n_parts(int total_q, int d_model);
+size_t prolog_part_words(int total_q, int d_model, int H, int D);
 hipError_t launch_prolog(int out_dtype, const PrologParams& p, hipStream_t st);
 
 // ------------------------------------------------------------------- SFA ---

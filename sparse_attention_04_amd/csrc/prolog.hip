@@ -9,19 +9,24 @@
 //
 // The pages run the independent preparation operators on separate streams so
 // that they overlap.  Here the three projections are one launch: its
-// workgroups take 32-column tiles of [W_q | W_k | W_w] (8192 + 128 + 64
-// columns for the 64 x 128 indexer), so every projection streams its weights
+// workgroups take 128-row tiles of W_q, W_k and W_w (8192 + 128 + 64 rows
+// for the 64 x 128 indexer) and, for the few tokens of a decode step, one of
+// up to four ranges of d_model each, so every projection streams its weights
 // at the same time with no stream synchronisation.  A second launch, one
-// workgroup per token, quantises q per (token, head) or per 32-group,
-// normalises and quantises k and writes it into the cache.
+// workgroup per token and 16 heads, adds the ranges' partial sums, quantises
+// q per (token, head) or per 32-group, normalises and quantises k and writes
+// it into the cache.
 //
-//   prolog_gemm_kernel: out[t][c] = sum_k x[t][k] W[c][k] over d_model, the
-//     weights staged through LDS (see the kernel); q columns are rounded to
-//     bf16, k and w stay float32.  For decode (tens of tokens) the launch is
-//     bound by the weight stream (d_model x 8384 bf16).
-//   prolog_finish_kernel: quantise q; add up the k and w partials; LayerNorm k
-//     in float32, round to bf16, quantise, append at t = L_b - T_b + i through
-//     the block table.
+//   prolog_gemm_kernel: out[t][c] = sum_k x[t][k] W[c][k] over a range of
+//     d_model, the weights staged through LDS (see the kernel), as float32
+//     partial sums (or, for launches with one range, q rounded to bf16).  For
+//     decode (tens of tokens) the launch is bound by the weight stream
+//     (d_model x 8384 bf16).
+//   prolog_finish_kernel: add up the partials; round q to bf16 and quantise
+//     it; LayerNorm k in float32, round to bf16, quantise, append at
+//     t = L_b - T_b + i through the block table.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -31,16 +36,18 @@ namespace {
 
 constexpr int kPgThreads = 256;    // 4 waves
 constexpr int kPgM = 64;            // tokens per workgroup (each wave: 16)
-constexpr int kPgN = 32;            // weight rows (output columns) per tile
-constexpr int kPgKC = 256;          // d_model elements per staged chunk
-constexpr int kPgRowB = kPgKC * 2;  // bytes of one row's chunk (512)
+constexpr int kPgN = 144;           // weight rows (output columns) per tile
+constexpr int kPgKC = 128;          // d_model elements per staged chunk
+constexpr int kPgRowB = kPgKC * 2;  // bytes of one row's chunk (256)
 constexpr int kPgRows = kPgN + kPgM;                    // weight rows, then token rows
-constexpr int kPgChunkB = kPgRows * kPgRowB;            // 48 KiB per chunk
-constexpr int kPgLoads = kPgChunkB / 1024;              // 1-KiB loads per chunk (48)
-constexpr int kPgLPW = kPgLoads / 4;                    // per wave (12)
+constexpr int kPgChunkB = kPgRows * kPgRowB;            // 52 KiB per chunk
+constexpr int kPgLoads = kPgChunkB / 1024;              // 1-KiB loads per chunk (52)
+constexpr int kPgLPW = kPgLoads / 4;                    // per wave (13)
 constexpr int kPgNBuf = 3;                              // chunks in the LDS ring
+constexpr int kPgNT = kPgN / 16;                        // 16-column N-tiles per wave (9)
 constexpr int kPgDmodelUnit = kPgKC;
-static_assert(kPgLoads % 4 == 0 && kPgRowB * 2 == 1024, "two rows per 1-KiB load");
+constexpr int kPgMaxSplit = 4;                          // d_model ranges of a decode-sized launch
+static_assert(kPgLoads % 4 == 0 && kPgRowB * 4 == 1024, "four rows per 1-KiB load");
 
 __device__ __forceinline__ int find_seq_pg(const BatchView& bv, int tok) {
   int lo = 0, hi = bv.batch - 1;
@@ -59,138 +66,113 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 #define DSA_PG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-// Tile t of the concatenated weight rows [W_q | W_k | W_w] (all multiples of
-// 32 rows): its matrix (0 q, 1 k, 2 w) and first row in that matrix.
-__device__ __forceinline__ void tile_of(const PrologParams& p, int tile, int& mat, int& row0) {
-  const int nq = p.H * p.D / kPgN, nk = p.D / kPgN;
-  if (tile < nq) { mat = 0; row0 = tile * kPgN; }
-  else if (tile < nq + nk) { mat = 1; row0 = (tile - nq) * kPgN; }
-  else { mat = 2; row0 = (tile - nq - nk) * kPgN; }
+// Row r of the concatenated weights [W_q | W_k | W_w] (H*D + D + H rows; r
+// is also the output column): its source row.
+__device__ __forceinline__ const uint16_t* weight_row(const PrologParams& p, int r) {
+  const int hd = p.H * p.D;
+  if (r < hd) return (const uint16_t*)p.w_q + (size_t)r * p.d_model;
+  if (r < hd + p.D) return (const uint16_t*)p.w_k + (size_t)(r - hd) * p.d_model;
+  return (const uint16_t*)p.w_w + (size_t)(r - hd - p.D) * p.d_model;
 }
 
-// out[t][c] = sum_k x[t][k] W[c][k].  A workgroup computes 64 tokens x 32
-// weight rows; wave w owns tokens 16w .. 16w + 15 with 16x16x32 bf16 MFMAs
-// (two 16-column N-tiles), so no partial sums cross waves.  d_model streams in
-// chunks of 256 elements through a 3-deep LDS ring: 48 one-KiB direct
-// global->LDS loads per chunk (two rows each, fully coalesced), rows of 512
-// bytes whose 16-byte pieces are XOR-swizzled by row (piece c of row r sits in
-// slot c ^ (r % 32)), so the operand reads of 16 rows hit 16 distinct bank
-// groups.
+// out[t][c] = sum_k x[t][k] W[c][k].  A workgroup computes 64 tokens x 144
+// rows of the concatenated weights over one range of d_model; wave w owns
+// tokens 16w .. 16w + 15 with 16x16x32 bf16 MFMAs (nine 16-column N-tiles),
+// so no partial sums cross waves.  Its d_model range streams in chunks of 128
+// elements through a 3-deep LDS ring: 52 one-KiB direct global->LDS loads per
+// chunk (four rows each, fully coalesced), rows of 256 bytes whose 16-byte
+// pieces are XOR-swizzled by row (piece c of row r sits in slot c ^ (r % 16)),
+// so the operand reads of 16 rows hit 16 distinct bank groups.  With 8384 rows
+// (the 64 x 128 indexer) and four ranges the grid is 59 x 4 = 236 workgroups:
+// one round on 256 compute units.
 //
-// Jobs: the workgroup's main tile over every chunk, then (decode launches, a
-// single token block) its share of slices: the K and head-weight tiles split
-// by chunk over the workgroups, so the grid is exactly the q tiles and one
-// round of workgroups covers it.  Their partial sums go to part[chunk] and the
-// finish kernel adds them in chunk order.  Launches with several token blocks
-// (many workgroups anyway) give every tile, K and head-weight ones included,
-// a workgroup of its own (part[0]).
+// A decode-sized launch (one block of at most 64 tokens, grid z = p.n_parts
+// ranges of d_model) writes float32 partial sums of every output column to
+// part[range][token][column of q | k | w]; the finish kernel adds them in
+// range order and rounds q to bf16.  Larger launches (one range) round q to
+// bf16 here and write the k and w columns to part[0].  Splitting d_model
+// gives the weight stream enough workgroups with 144 rows each: a compute
+// unit then has 72 KiB of weights in flight, and re-reads a quarter as many
+// token rows as with one range.
 __global__ __launch_bounds__(kPgThreads, 1) void prolog_gemm_kernel(PrologParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char pg_smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.y * kPgM;
   const int dm = p.d_model;
-  const int nch = dm / kPgKC;
-  const int nq_tiles = p.H * p.D / kPgN, nx_tiles = (p.D + p.H) / kPgN;
-  const bool split = p.split_extra != 0;
-  const int nmain = nch;
-  int nextra = 0;
-  if (split)
-    for (int e = blockIdx.x; e < nx_tiles * nch; e += nq_tiles) nextra++;
-  const int njobs = nmain + nextra;
-  int main_mat, main_row0;
-  tile_of(p, blockIdx.x, main_mat, main_row0);
-
-  // job -> (weight matrix, first row, chunk)
-  auto job = [&](int j, int& mat, int& row0, int& c) {
-    if (j < nmain) {
-      mat = main_mat; row0 = main_row0; c = j;
-    } else {
-      const int e = blockIdx.x + (j - nmain) * nq_tiles;
-      tile_of(p, nq_tiles + e / nch, mat, row0);
-      c = e % nch;
-    }
-  };
+  const int nch_all = dm / kPgKC;
+  const int split = blockIdx.z, nsplit = gridDim.z;
+  const int c_begin = (int)((int64_t)nch_all * split / nsplit), c_end = (int)((int64_t)nch_all * (split + 1) / nsplit);
+  const int nch = c_end - c_begin;
+  const int ncol = p.H * p.D + p.D + p.H;
+  const int row0 = blockIdx.x * kPgN;
   const uint32_t ring = lds_addr(pg_smem);
+  // load ins of a chunk fills rows 4 ins .. 4 ins + 3 (weight rows first,
+  // then token rows; rows past the weights or past total_q repeat the last)
+  const uint16_t* src_row[kPgLPW];
+#pragma unroll
+  for (int k = 0; k < kPgLPW; k++) {
+    const int R = 4 * (wave + 4 * k) + (lane >> 4);
+    src_row[k] = (R < kPgN) ? weight_row(p, min(row0 + R, ncol - 1))
+                            : (const uint16_t*)p.x + (size_t)min(m0 + R - kPgN, p.total_q - 1) * dm;
+  }
   auto issue = [&](int j) {
-    int mat, row0, c;
-    job(j, mat, row0, c);
-    const uint16_t* W = (const uint16_t*)(mat == 0 ? p.w_q : mat == 1 ? p.w_k : p.w_w);
+    const int c = c_begin + j;
     const uint32_t buf = ring + (uint32_t)(j % kPgNBuf) * kPgChunkB;
 #pragma unroll
     for (int k = 0; k < kPgLPW; k++) {
       const int ins = wave + 4 * k;
-      const int R = 2 * ins + (lane >> 5);
-      const int piece = (lane & 31) ^ (R & 31);
-      const uint16_t* src = (R < kPgN)
-          ? W + (size_t)(row0 + R) * dm
-          : (const uint16_t*)p.x + (size_t)min(m0 + R - kPgN, p.total_q - 1) * dm;
-      dma16(src + c * kPgKC + piece * 8, __builtin_amdgcn_readfirstlane(buf + ins * 1024u));
+      const int R = 4 * ins + (lane >> 4);
+      const int piece = (lane & 15) ^ (R & 15);
+      dma16(src_row[k] + c * kPgKC + piece * 8, __builtin_amdgcn_readfirstlane(buf + ins * 1024u));
     }
   };
   issue(0);
-  if (njobs > 1) issue(1);
+  if (nch > 1) issue(1);
 
   const int g16 = lane >> 4, l16 = lane & 15;
-  f32x4 acc[2], acce[2];
+  f32x4 acc[kPgNT];
 #pragma unroll
-  for (int n = 0; n < 2; n++) {
-    acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acce[n] = acc[n];
-  }
-  for (int j = 0; j < njobs; j++) {
-    if (j + 1 < njobs) DSA_PG_WAIT_VMCNT(kPgLPW); else DSA_PG_WAIT_VMCNT(0);
-    // every wave's loads of job j have landed, and every wave is done with the
-    // buffer of job j - 1, which job j + 2 refills
+  for (int n = 0; n < kPgNT; n++) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < nch; j++) {
+    if (j + 1 < nch) DSA_PG_WAIT_VMCNT(kPgLPW); else DSA_PG_WAIT_VMCNT(0);
+    // every wave's loads of chunk j have landed, and every wave is done with
+    // the buffer of chunk j - 1, which chunk j + 2 refills
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (j + 2 < njobs) issue(j + 2);
+    if (j + 2 < nch) issue(j + 2);
     const unsigned char* buf = pg_smem + (size_t)(j % kPgNBuf) * kPgChunkB;
-    const bool is_main = j < nmain;
-    if (!is_main) {
-#pragma unroll
-      for (int n = 0; n < 2; n++) acce[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // A: token row kPgN + 16 wave + l16; B: weight rows l16 and 16 + l16;
+    // A: token row kPgN + 16 wave + l16; B: weight rows 16 n + l16;
     // K-step ks takes pieces 4 ks + g16 (8 elements each)
     const int ra = kPgN + 16 * wave + l16;
 #pragma unroll
     for (int ks = 0; ks < kPgKC / 32; ks++) {
       const int pc = 4 * ks + g16;
-      const bf16x8 a = *(const bf16x8*)(buf + ra * kPgRowB + ((pc ^ (ra & 31)) * 16));
-      const bf16x8 b0 = *(const bf16x8*)(buf + l16 * kPgRowB + ((pc ^ l16) * 16));
-      const bf16x8 b1 = *(const bf16x8*)(buf + (16 + l16) * kPgRowB + ((pc ^ (16 + l16)) * 16));
-      if (is_main) {
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[1], 0, 0, 0);
-      } else {
-        acce[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acce[0], 0, 0, 0);
-        acce[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acce[1], 0, 0, 0);
+      const bf16x8 a = *(const bf16x8*)(buf + ra * kPgRowB + ((pc ^ (ra & 15)) * 16));
+#pragma unroll
+      for (int n = 0; n < kPgNT; n++) {
+        const int rb = 16 * n + l16;
+        const bf16x8 bv = *(const bf16x8*)(buf + rb * kPgRowB + ((pc ^ (rb & 15)) * 16));
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[n], 0, 0, 0);
       }
     }
-    // C layout of a 16x16 tile: lane l holds column l % 16 and rows
-    // 4 (l / 16) + i.  Tokens past total_q are not written.
-    const bool last_main = (j == nmain - 1);
-    if (!last_main && is_main) continue;
-    int mat, row0, c;
-    job(j, mat, row0, c);
-    f32x4 v[2];
-#pragma unroll
-    for (int n = 0; n < 2; n++) v[n] = is_main ? acc[n] : acce[n];
-#pragma unroll
-    for (int n = 0; n < 2; n++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int tok = m0 + 16 * wave + 4 * g16 + i;
-        if (tok >= p.total_q) continue;
-        const int col = row0 + 16 * n + l16;
-        if (mat == 0) {
-          ((uint16_t*)p.q_bf16)[(size_t)tok * p.H * p.D + col] = f32_to_bf16(v[n][i]);
-        } else {
-          const int kc = (mat == 1) ? col : p.D + col;     // column of [k | w]
-          const int part = is_main ? 0 : c;
-          p.kw_part[((size_t)part * p.total_q + tok) * (p.D + p.H) + kc] = v[n][i];
-        }
-      }
   }
+  // C layout of a 16x16 tile: lane l holds column l % 16 and rows
+  // 4 (l / 16) + i.  Tokens past total_q and rows past the weights are not
+  // written.
+#pragma unroll
+  for (int n = 0; n < kPgNT; n++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int tok = m0 + 16 * wave + 4 * g16 + i;
+      const int r = row0 + 16 * n + l16;
+      if (tok >= p.total_q || r >= ncol) continue;
+      if (nsplit > 1) {
+        p.part[((size_t)split * p.total_q + tok) * ncol + r] = acc[n][i];
+      } else if (r < p.H * p.D) {
+        ((uint16_t*)p.q_bf16)[(size_t)tok * p.H * p.D + r] = f32_to_bf16(acc[n][i]);
+      } else {
+        p.part[(size_t)tok * (p.D + p.H) + (r - p.H * p.D)] = acc[n][i];
+      }
+    }
 }
 
 // float -> e4m3fn byte, round to nearest even, saturated to +-448 first.
@@ -213,14 +195,40 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
   const int tok = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = p.H, D = p.D;          // D == 128: two elements per lane
+  const int S = p.n_parts;                   // d_model ranges of the GEMM
+  const int ncol = H * D + D + H;
   // ---- q: workgroup y quantises heads 16y .. 16y + 15, four per wave (all
-  // four loaded before any is used)
-  if (OUT != kBF16) {
+  // four loaded before any is used).  With several ranges, q is the sum of
+  // their float32 partials in range order, rounded to bf16 here.
+  if (OUT != kBF16 || S > 1) {
     const uint16_t* q = (const uint16_t*)p.q_bf16 + (size_t)tok * H * D;
     const int hb = 16 * blockIdx.y + 4 * wave;
     uint32_t two[4];
+    if (S > 1) {
+      float2 sum[4];
 #pragma unroll
-    for (int u = 0; u < 4; u++) two[u] = (hb + u < H) ? *(const uint32_t*)(q + (size_t)(hb + u) * D + 2 * lane) : 0u;
+      for (int u = 0; u < 4; u++) sum[u] = float2{0.f, 0.f};
+      for (int sp = 0; sp < S; sp++) {
+        const float* ps = p.part + ((size_t)sp * p.total_q + tok) * ncol;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          if (hb + u >= H) continue;
+          const float2 v = *(const float2*)(ps + (size_t)(hb + u) * D + 2 * lane);
+          sum[u].x += v.x;
+          sum[u].y += v.y;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        two[u] = (uint32_t)f32_to_bf16(sum[u].x) | ((uint32_t)f32_to_bf16(sum[u].y) << 16);
+        if (hb + u < H && (OUT == kBF16 || p.q_bf16 != p.q_out))
+          *(uint32_t*)((uint16_t*)p.q_bf16 + (size_t)tok * H * D + (size_t)(hb + u) * D + 2 * lane) = two[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; u++) two[u] = (hb + u < H) ? *(const uint32_t*)(q + (size_t)(hb + u) * D + 2 * lane) : 0u;
+    }
+    if (OUT != kBF16) {
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       const int h = hb + u;
@@ -243,6 +251,7 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
       }
       *(uint16_t*)((uint8_t*)p.q_out + ((size_t)tok * H + h) * D + 2 * lane) = (uint16_t)bytes;
     }
+    }
   }
   if (blockIdx.y != 0) return;
   // ---- k and w: the sums of their partials.  Thread t adds parts
@@ -250,15 +259,17 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
   // column t % 64 (loads unrolled); the sub-sums then meet in LDS in a fixed
   // order.
   __shared__ float s_k[2][128], s_w[4][64];
-  const int KW = D + H;
-  const float* pk = p.kw_part + (size_t)tok * KW;
+  // part[range][token][column]: all columns of [q | k | w] with several
+  // ranges, the k and w columns only with one
+  const int KW = (S > 1) ? ncol : D + H;
+  const float* pk = p.part + (size_t)tok * KW + ((S > 1) ? H * D : 0);
   const size_t pstride = (size_t)p.total_q * KW;
   {
     const int kc = tid & 127, kh = tid >> 7;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     int c = kh, u = 0;
 #pragma unroll 4
-    for (; c < p.n_parts; c += 2, u = (u + 1) & 3) acc[u] += pk[c * pstride + kc];
+    for (; c < S; c += 2, u = (u + 1) & 3) acc[u] += pk[c * pstride + kc];
     s_k[kh][kc] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     if (H <= 64) {
       const int wc = tid & 63, wh = tid >> 6;
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
       int cw = wh, uw = 0;
       const bool has = wc < H;
 #pragma unroll 4
-      for (; cw < p.n_parts; cw += 4, uw = (uw + 1) & 3) aw[uw] += has ? pk[cw * pstride + D + wc] : 0.f;
+      for (; cw < S; cw += 4, uw = (uw + 1) & 3) aw[uw] += has ? pk[cw * pstride + D + wc] : 0.f;
       s_w[wh][wc] = (aw[0] + aw[1]) + (aw[2] + aw[3]);
     }
   }
@@ -276,7 +287,7 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
   } else if (wave == 1) {
     for (int h = lane; h < H; h += 64) {
       float acc = 0.f;
-      for (int c = 0; c < p.n_parts; c++) acc += pk[c * pstride + D + h];
+      for (int c = 0; c < S; c++) acc += pk[c * pstride + D + h];
       p.w_out[(size_t)tok * H + h] = acc;
     }
   }
@@ -324,24 +335,32 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
 
 int prolog_d_model_unit() { return kPgDmodelUnit; }
 
-// Partial-sum slots of the K / head-weight columns a launch needs.
+// Ranges of d_model a launch splits the GEMM into (the partial-sum slots it
+// needs): a decode-sized launch (one block of tokens) takes up to four ranges
+// of at least two chunks each; larger launches one.
 int prolog_n_parts(int total_q, int d_model) {
-  return (total_q <= kPgM) ? d_model / kPgKC : 1;
+  if (total_q > kPgM) return 1;
+  return std::max(1, std::min(kPgMaxSplit, d_model / kPgKC / 2));
+}
+
+// float32 words of the partial-sum workspace.
+size_t prolog_part_words(int total_q, int d_model, int H, int D) {
+  const int S = prolog_n_parts(total_q, d_model);
+  return (size_t)S * total_q * ((S > 1) ? (size_t)H * D + D + H : (size_t)D + H);
 }
 
 hipError_t launch_prolog(int out_dtype, const PrologParams& p0, hipStream_t st) {
   if (p0.total_q == 0) return hipSuccess;
-  if (p0.D != 128 || (p0.H % kPgN) != 0 || p0.d_model <= 0 || (p0.d_model % kPgDmodelUnit) != 0)
+  if (p0.D != 128 || (p0.H % 32) != 0 || p0.d_model <= 0 || (p0.d_model % kPgDmodelUnit) != 0)
     return hipErrorInvalidValue;
   PrologParams p = p0;
   const int mblocks = (p.total_q + kPgM - 1) / kPgM;
-  p.split_extra = (mblocks == 1) ? 1 : 0;
   p.n_parts = prolog_n_parts(p.total_q, p.d_model);
-  const int ntiles = p.H * p.D / kPgN + (p.split_extra ? 0 : (p.D + p.H) / kPgN);
+  const int ntiles = (p.H * p.D + p.D + p.H + kPgN - 1) / kPgN;
   const size_t lds = (size_t)kPgNBuf * kPgChunkB;
   hipError_t e = hipFuncSetAttribute((const void*)prolog_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prolog_gemm_kernel, dim3(ntiles, mblocks), dim3(kPgThreads), lds, st, p);
+  hipLaunchKernelGGL(prolog_gemm_kernel, dim3(ntiles, mblocks, p.n_parts), dim3(kPgThreads), lds, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g2(p.total_q, (p.H + 15) / 16);

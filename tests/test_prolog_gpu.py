@@ -157,3 +157,14 @@ def test_prolog_full_size_fp8():
     case = make_case("c4_decode_fp8", 74, device="cuda")
     call = _run_prolog(case, 7168, 74)
     _check_decode(case, call, limit=8)
+
+
+@pytest.mark.parametrize("name,heads,d_model", [("c4_decode_fp8", 32, 640), ("c4_decode_mxfp8", 128, 384),
+                                                ("c5_decode4", 96, 1024)])
+def test_prolog_other_head_counts_and_widths(name, heads, d_model):
+    """Head counts other than 64 and hidden widths that split d_model unevenly
+    (640: ranges of 2 and 3 chunks of 128) or not at all (384): the GEMM's
+    tiles of 144 concatenated weight rows end partway through W_w, and with
+    96 heads the workgroups take more than one round."""
+    case = case_to(make_case(name, 76, batch=2, seq_lens=[3000, 4100], h_i=heads), "cuda")
+    _run_prolog(case, d_model, 76)

@@ -47,6 +47,7 @@ constexpr int kPgNBuf = 3;                              // chunks in the LDS rin
 constexpr int kPgNT = kPgN / 16;                        // 16-column N-tiles per wave (9)
 constexpr int kPgDmodelUnit = kPgKC;
 constexpr int kPgMaxSplit = 4;                          // d_model ranges of a decode-sized launch
+static_assert(kPgMaxSplit == 4, "the finish kernel reads two k parts and one w part per thread");
 static_assert(kPgLoads % 4 == 0 && kPgRowB * 4 == 1024, "four rows per 1-KiB load");
 
 __device__ __forceinline__ int find_seq_pg(const BatchView& bv, int tok) {
@@ -195,6 +196,25 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
   const int tok = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = p.H, D = p.D;          // D == 128: two elements per lane
+  // The key's cache row (wave 0 of workgroup 0 of the token), found first so
+  // that its chain of loads overlaps the sums below: the token's sequence from
+  // one wave-wide load of cu_q (a binary search for batches above 65), then
+  // its length and offsets, then the block-table entry.
+  const BatchView& bv = p.bv;
+  int64_t krow = 0;
+  if (blockIdx.y == 0 && wave == 0) {
+    int b;
+    if (bv.batch <= 65) {
+      const int cq = (1 + lane < bv.batch) ? bv.cu_q[1 + lane] : 0x7FFFFFFF;
+      b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(cq <= tok)));
+    } else {
+      b = find_seq_pg(bv, tok);
+    }
+    const int c0 = bv.cu_q[b], c1 = bv.cu_q[b + 1], L = bv.seq_lens[b];
+    const int t = L - (c1 - c0) + (tok - c0);
+    krow = ((int64_t)bv.block_table[(size_t)b * bv.max_pages + (t >> bv.page_shift)] << bv.page_shift) +
+           (t & (bv.page_size - 1));
+  }
   const int S = p.n_parts;                   // d_model ranges of the GEMM
   const int ncol = H * D + D + H;
   // ---- q: workgroup y quantises heads 16y .. 16y + 15, four per wave (all
@@ -205,17 +225,24 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
     const int hb = 16 * blockIdx.y + 4 * wave;
     uint32_t two[4];
     if (S > 1) {
-      float2 sum[4];
+      // every range's partials of the four heads are loaded before any is
+      // added (S <= kPgMaxSplit)
+      float2 v[kPgMaxSplit][4];
 #pragma unroll
-      for (int u = 0; u < 4; u++) sum[u] = float2{0.f, 0.f};
-      for (int sp = 0; sp < S; sp++) {
+      for (int sp = 0; sp < kPgMaxSplit; sp++) {
         const float* ps = p.part + ((size_t)sp * p.total_q + tok) * ncol;
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-          if (hb + u >= H) continue;
-          const float2 v = *(const float2*)(ps + (size_t)(hb + u) * D + 2 * lane);
-          sum[u].x += v.x;
-          sum[u].y += v.y;
+        for (int u = 0; u < 4; u++)
+          v[sp][u] = (sp < S && hb + u < H) ? *(const float2*)(ps + (size_t)(hb + u) * D + 2 * lane) : float2{0.f, 0.f};
+      }
+      float2 sum[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        sum[u] = v[0][u];
+#pragma unroll
+        for (int sp = 1; sp < kPgMaxSplit; sp++) {
+          sum[u].x += v[sp][u].x;
+          sum[u].y += v[sp][u].y;
         }
       }
 #pragma unroll
@@ -255,9 +282,8 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
   }
   if (blockIdx.y != 0) return;
   // ---- k and w: the sums of their partials.  Thread t adds parts
-  // c = t / 128 (mod 2) of k column t % 128, and parts c = t / 64 (mod 4) of w
-  // column t % 64 (loads unrolled); the sub-sums then meet in LDS in a fixed
-  // order.
+  // c = t / 128 and c + 2 of k column t % 128, and takes part c = t / 64 of w
+  // column t % 64; the sub-sums then meet in LDS in a fixed order.
   __shared__ float s_k[2][128], s_w[4][64];
   // part[range][token][column]: all columns of [q | k | w] with several
   // ranges, the k and w columns only with one
@@ -265,20 +291,15 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
   const float* pk = p.part + (size_t)tok * KW + ((S > 1) ? H * D : 0);
   const size_t pstride = (size_t)p.total_q * KW;
   {
+    // (S <= kPgMaxSplit = 4: at most two parts per k thread and one per w
+    // thread, loaded together)
     const int kc = tid & 127, kh = tid >> 7;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int c = kh, u = 0;
-#pragma unroll 4
-    for (; c < S; c += 2, u = (u + 1) & 3) acc[u] += pk[c * pstride + kc];
-    s_k[kh][kc] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const float k0 = (kh < S) ? pk[kh * pstride + kc] : 0.f;
+    const float k1 = (kh + 2 < S) ? pk[(kh + 2) * pstride + kc] : 0.f;
+    s_k[kh][kc] = k0 + k1;
     if (H <= 64) {
       const int wc = tid & 63, wh = tid >> 6;
-      float aw[4] = {0.f, 0.f, 0.f, 0.f};
-      int cw = wh, uw = 0;
-      const bool has = wc < H;
-#pragma unroll 4
-      for (; cw < S; cw += 4, uw = (uw + 1) & 3) aw[uw] += has ? pk[cw * pstride + D + wc] : 0.f;
-      s_w[wh][wc] = (aw[0] + aw[1]) + (aw[2] + aw[3]);
+      s_w[wh][wc] = (wh < S && wc < H) ? pk[wh * pstride + D + wc] : 0.f;
     }
   }
   __syncthreads();
@@ -302,13 +323,8 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
   const uint16_t k0 = f32_to_bf16(d0 * inv * p.ln_gamma[2 * lane] + p.ln_beta[2 * lane]);
   const uint16_t k1 = f32_to_bf16(d1 * inv * p.ln_gamma[2 * lane + 1] + p.ln_beta[2 * lane + 1]);
   if (p.k_bf16_out) *(uint32_t*)((uint16_t*)p.k_bf16_out + (size_t)tok * D + 2 * lane) = (uint32_t)k0 | ((uint32_t)k1 << 16);
-  // cache row of this token: t = L_b - T_b + i
-  const BatchView& bv = p.bv;
-  const int b = find_seq_pg(bv, tok);
-  const int i = tok - bv.cu_q[b];
-  const int t = bv.seq_lens[b] - (bv.cu_q[b + 1] - bv.cu_q[b]) + i;
-  const int64_t row = ((int64_t)bv.block_table[(size_t)b * bv.max_pages + (t >> bv.page_shift)] << bv.page_shift) +
-                      (t & (bv.page_size - 1));
+  // cache row of this token: t = L_b - T_b + i (found above)
+  const int64_t row = krow;
   if (OUT == kBF16) {
     *(uint32_t*)((uint16_t*)p.k_data + row * D + 2 * lane) = (uint32_t)k0 | ((uint32_t)k1 << 16);
     return;

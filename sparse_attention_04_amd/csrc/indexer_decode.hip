@@ -21,6 +21,11 @@
 //   3. if equal keys straddle the boundary, one more exchange of per-workgroup
 //      tie counts hands the remaining slots to the smallest positions;
 //   4. each workgroup appends its selected positions to the query's output row.
+//   When the first pass's boundary bin holds at most kHandoffCap keys, steps
+//   2-3 stop after that pass: every workgroup writes the keys above the bin
+//   to the row and the keys in it to a list, and the sequence's last
+//   workgroup chooses the rest of them on its own (exactly, equal keys to the
+//   smaller positions), with no further barrier.
 //
 // All workgroups of a launch are co-resident (the grid is sized from the
 // occupancy of the kernel), every wait is bounded (group_barrier), and the grid

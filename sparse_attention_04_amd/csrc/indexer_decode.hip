@@ -71,9 +71,9 @@ int indexer_decode_max_q() { return kMaxDecodeQ; }
 
 size_t indexer_decode_lds_bytes(int dtype, int maxq, int chunk_cap, int stage_pages) {
   const size_t xchg = (dtype == kBF16 && maxq == 4) ? 2 * kXchgSlotWords : 0;
-  // the last workgroup's choice among the handed-off boundary bins reuses the
-  // same LDS for two 2048-bin histograms per query
-  const size_t handoff = 2 * (size_t)maxq * kRadixBins * 4;
+  // the last workgroup's choice among the handed-off boundary bins (one
+  // query at a time) reuses the same LDS for two 2048-bin histograms
+  const size_t handoff = 2 * (size_t)kRadixBins * 4;
   return std::max((xchg_offset_words(maxq, chunk_cap, stage_pages) + xchg) * 4, handoff);
 }
 

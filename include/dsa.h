@@ -209,7 +209,12 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* batch,
 
 /* Fused Lightning Indexer: scores, head weighting, causal mask and Top-K in
  * one pass over the paged K cache; the full score row is never written to
- * device memory.  idx_out: device int32 [total_q][topk] (see Top-K above).   */
+ * device memory.  idx_out: device int32 [total_q][topk] (see Top-K above).
+ * Decode-sized batches select with an exact radix select across the
+ * workgroups that share a sequence; when few keys share the first pass's
+ * boundary bin, the sequence's last workgroup finishes the choice alone.
+ * DSA_INDEXER_HANDOFF_CAP=n in the environment caps that bin (0: never; the
+ * result is the same index set either way, a test and diagnostic switch). */
 dsa_status dsa_indexer_topk(const dsa_batch* batch, const dsa_indexer_args* args,
                             int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 

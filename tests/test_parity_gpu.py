@@ -494,9 +494,10 @@ def test_quantised_prefill_full_size_sampled(name):
     assert np.all(np.where(valid, idx_h <= t[:, None], True))
 
 
-def test_c2_fp8kv_full_size_sampled():
+def test_c2_fp8kv_full_size_every_query():
     """The decode workload at full size (32 sequences, contexts U[4096, 32768])
-    with the SFA KV cache in FP8, in the configuration the benchmark times."""
+    with the SFA KV cache in FP8, in the configuration the benchmark times,
+    every query checked against the oracle."""
     _say("c2 fp8 KV full size: generating on device")
     case = make_case("c2_decode_fp8kv", 6, device="cuda")
     call = B.Call(case)

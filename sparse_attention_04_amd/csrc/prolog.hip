@@ -217,6 +217,21 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
   }
   const int S = p.n_parts;                   // d_model ranges of the GEMM
   const int ncol = H * D + D + H;
+  // The k and w partials of workgroup 0 of the token, loaded now for use
+  // after q.  part[range][token][column]: all columns of [q | k | w] with
+  // several ranges, the k and w columns only with one.  Thread t takes parts
+  // c = t / 128 and c + 2 of k column t % 128, and part c = t / 64 of w column
+  // t % 64 (S <= kPgMaxSplit = 4).
+  const int KW = (S > 1) ? ncol : D + H;
+  const float* pk = p.part + (size_t)tok * KW + ((S > 1) ? H * D : 0);
+  const size_t pstride = (size_t)p.total_q * KW;
+  const int kc = tid & 127, kh = tid >> 7, wc = tid & 63, wh = tid >> 6;
+  float k0 = 0.f, k1 = 0.f, w0 = 0.f;
+  if (blockIdx.y == 0) {
+    k0 = (kh < S) ? pk[kh * pstride + kc] : 0.f;
+    k1 = (kh + 2 < S) ? pk[(kh + 2) * pstride + kc] : 0.f;
+    w0 = (H <= 64 && wh < S && wc < H) ? pk[wh * pstride + D + wc] : 0.f;
+  }
   // ---- q: workgroup y quantises heads 16y .. 16y + 15, four per wave (all
   // four loaded before any is used).  With several ranges, q is the sum of
   // their float32 partials in range order, rounded to bf16 here.
@@ -281,27 +296,11 @@ __global__ __launch_bounds__(kFinThreads) void prolog_finish_kernel(PrologParams
     }
   }
   if (blockIdx.y != 0) return;
-  // ---- k and w: the sums of their partials.  Thread t adds parts
-  // c = t / 128 and c + 2 of k column t % 128, and takes part c = t / 64 of w
-  // column t % 64; the sub-sums then meet in LDS in a fixed order.
+  // ---- k and w: the sums of their partials (loaded at the start); the
+  // sub-sums meet in LDS in a fixed order
   __shared__ float s_k[2][128], s_w[4][64];
-  // part[range][token][column]: all columns of [q | k | w] with several
-  // ranges, the k and w columns only with one
-  const int KW = (S > 1) ? ncol : D + H;
-  const float* pk = p.part + (size_t)tok * KW + ((S > 1) ? H * D : 0);
-  const size_t pstride = (size_t)p.total_q * KW;
-  {
-    // (S <= kPgMaxSplit = 4: at most two parts per k thread and one per w
-    // thread, loaded together)
-    const int kc = tid & 127, kh = tid >> 7;
-    const float k0 = (kh < S) ? pk[kh * pstride + kc] : 0.f;
-    const float k1 = (kh + 2 < S) ? pk[(kh + 2) * pstride + kc] : 0.f;
-    s_k[kh][kc] = k0 + k1;
-    if (H <= 64) {
-      const int wc = tid & 63, wh = tid >> 6;
-      s_w[wh][wc] = (wh < S && wc < H) ? pk[wh * pstride + D + wc] : 0.f;
-    }
-  }
+  s_k[kh][kc] = k0 + k1;
+  if (H <= 64) s_w[wh][wc] = w0;
   __syncthreads();
   if (H <= 64) {
     if (tid < H) p.w_out[(size_t)tok * H + tid] = (s_w[0][tid] + s_w[1][tid]) + (s_w[2][tid] + s_w[3][tid]);
